@@ -1,0 +1,444 @@
+/*
+ * bkv_oracle.c -- plain, slow, single-threaded CPU oracle of the BeaconKV
+ * eviction hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library and its Python binding) never calls it, and the two share no
+ * code, header, table or constant.
+ *
+ * Every computation is carried out in IEEE binary64 unless a step below says
+ * otherwise.  Storage types are binary32 ("f32") and bfloat16 ("bf16", held as
+ * its 16-bit pattern).
+ *
+ * Sources (the method is described on web pages, cited by title and section):
+ *   [WZ]  wzjinhao.cn news article 56682 on BeaconKV (Chinese), sections
+ *         "怎么挑出这几个信标" (how the beacons are picked: FPS, Continual FPS,
+ *         pre-RoPE space) and "信标查询怎么用" (how beacon queries are used:
+ *         positions, max aggregation).
+ *   [IK]  inkeast.github.io MessageDaily paper-reading post on BeaconKV,
+ *         section 三 (problem definition: I = TopK(score(K,V), B_KV)) and
+ *         section 4.4 (beacon-guided eviction).
+ *   [AM]  aimodeling.com "BeaconKV: Beacon Queries Fix KV Eviction for Long
+ *         Reasoning", section "Beacon queries anticipate what will be
+ *         revisited" (recent sliding window always kept; defaults 16/16/32).
+ *
+ * Readings taken where the pages are silent are listed next to each step.
+ *
+ * Parity status: every function below is pinned by the CPU test suite
+ * (brute force, closed forms, invariants and library routines); none is
+ * "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* ------------------------------------------------------------------------ */
+/* Storage conversions                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Exact widening of one stored element to binary64. */
+double orc_load(const void *base, int dtype, long idx) {
+  if (dtype == ORC_F32) {
+    return (double)((const float *)base)[idx];
+  }
+  uint16_t h = ((const uint16_t *)base)[idx];
+  uint32_t w = (uint32_t)h << 16; /* bf16 is the top half of a binary32 */
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+/* Round a binary64 value once, to nearest with ties to even, to bfloat16
+ * (8 significant bits, binary32 exponent range, gradual underflow).  Written
+ * from the format's definition: scale by the bf16 spacing at |v|, round to an
+ * integer in the default (nearest-even) mode, scale back. */
+uint16_t orc_bf16_from_double(double v) {
+  if (isnan(v)) return (uint16_t)0x7FC0;
+  if (isinf(v)) return v > 0 ? (uint16_t)0x7F80 : (uint16_t)0xFF80;
+  if (v == 0.0) return signbit(v) ? (uint16_t)0x8000 : (uint16_t)0x0000;
+  int e;
+  (void)frexp(v, &e);            /* |v| = f * 2^e, f in [0.5, 1) */
+  int q = e - 8;                 /* spacing of 8-bit significands at |v| */
+  if (q < -133) q = -133;        /* bf16 subnormal spacing is 2^-133 */
+  double r = nearbyint(ldexp(v, -q)); /* exact scaling, then RNE */
+  double out = ldexp(r, q);
+  if (fabs(out) >= 0x1p128) return v > 0 ? (uint16_t)0x7F80 : (uint16_t)0xFF80;
+  float f = (float)out;          /* exactly representable, no rounding */
+  uint32_t w;
+  memcpy(&w, &f, sizeof w);
+  return (uint16_t)(w >> 16);
+}
+
+/* Store v into a storage element with a single rounding from binary64. */
+void orc_store(void *base, int dtype, long idx, double v) {
+  if (dtype == ORC_F32) {
+    ((float *)base)[idx] = (float)v; /* C conversion rounds to nearest-even */
+  } else {
+    ((uint16_t *)base)[idx] = orc_bf16_from_double(v);
+  }
+}
+
+static size_t elem_size(int dtype) { return dtype == ORC_F32 ? 4 : 2; }
+
+/* ------------------------------------------------------------------------ */
+/* Farthest point sampling on cosine similarity                               */
+/* ------------------------------------------------------------------------ */
+
+static double dot(const double *a, const double *b, int d) {
+  double s = 0.0;
+  for (int t = 0; t < d; ++t) s += a[t] * b[t];
+  return s;
+}
+
+/*
+ * orc_fps: greedy farthest point sampling of up to k of the c vectors X[c][d].
+ * [WZ, 怎么挑出这几个信标]: start at the query whose mean similarity to all
+ * queries is lowest; then, round after round, add the remaining query that is
+ * least similar to (farthest from) the already-selected set, until the preset
+ * number is reached.  Similarity is cosine similarity.
+ *
+ * Readings: the distance of a point to the selected set is its distance to
+ * the nearest selected point, so "least similar to the set" means the lowest
+ * maximum cosine to the set.  The mean similarity includes the point itself.
+ * Ties go to the lowest index.  Norms are clamped at 1e-12 (a zero vector has
+ * cosine 0 with everything).  If c <= k every vector is returned.
+ *
+ * Returns the number of picks, min(k, c), written to picks[] in pick order.
+ */
+int orc_fps(const double *X, int c, int d, int k, int *picks) {
+  int kk = k < c ? k : c;
+  if (kk <= 0) return 0;
+  double *xh = (double *)malloc(sizeof(double) * (size_t)c * d);
+  double *m = (double *)malloc(sizeof(double) * c);
+  char *picked = (char *)calloc(c, 1);
+
+  /* normalise every vector */
+  for (int i = 0; i < c; ++i) {
+    double n = sqrt(dot(X + (size_t)i * d, X + (size_t)i * d, d));
+    if (n < 1e-12) n = 1e-12;
+    for (int t = 0; t < d; ++t) xh[(size_t)i * d + t] = X[(size_t)i * d + t] / n;
+  }
+
+  /* start: lowest mean cosine similarity to all c vectors */
+  int start = -1;
+  double best_mu = 0.0;
+  for (int i = 0; i < c; ++i) {
+    double sum = 0.0;
+    for (int j = 0; j < c; ++j) sum += dot(xh + (size_t)i * d, xh + (size_t)j * d, d);
+    double mu = sum / c;
+    if (start < 0 || mu < best_mu) {
+      start = i;
+      best_mu = mu;
+    }
+  }
+  picks[0] = start;
+  picked[start] = 1;
+  for (int i = 0; i < c; ++i) m[i] = dot(xh + (size_t)i * d, xh + (size_t)start * d, d);
+
+  /* greedy rounds: the unpicked vector with the lowest max-cosine to the set */
+  for (int t = 1; t < kk; ++t) {
+    int best = -1;
+    for (int i = 0; i < c; ++i) {
+      if (picked[i]) continue;
+      if (best < 0 || m[i] < m[best]) best = i;
+    }
+    picks[t] = best;
+    picked[best] = 1;
+    for (int i = 0; i < c; ++i) {
+      double s = dot(xh + (size_t)i * d, xh + (size_t)best * d, d);
+      if (s > m[i]) m[i] = s;
+    }
+  }
+  free(xh);
+  free(m);
+  free(picked);
+  return kk;
+}
+
+/*
+ * orc_fps_stored: FPS over the first c rows of a stored buffer (row stride d).
+ * The rows are widened exactly to binary64 first.
+ */
+int orc_fps_stored(const void *buf, int dtype, int c, int d, int k, int *picks) {
+  if (c <= 0) return 0;
+  double *X = (double *)malloc(sizeof(double) * (size_t)c * d);
+  for (long i = 0; i < (long)c * d; ++i) X[i] = orc_load(buf, dtype, i);
+  int n = orc_fps(X, c, d, k, picks);
+  free(X);
+  return n;
+}
+
+/*
+ * orc_fps_ingest: Continual FPS for one attention head.
+ * [WZ, 怎么挑出这几个信标]: each attention head keeps only a small buffer with
+ * an upper bound on its size; once the buffer is full an FPS pass compresses
+ * it back to a smaller size, and the cycle repeats, so the full query history
+ * is never stored.  [AM, "Beacon queries anticipate what will be revisited"]:
+ * sampling works on pre-RoPE queries.
+ *
+ * Readings: every decode query of the head enters the buffer in time order;
+ * "full" means the count reaches C right after an append; the shrunk buffer
+ * holds the M picked rows (original stored values, bit copies) in pick order,
+ * and later arrivals follow them.
+ *
+ * buf: [C][d] storage rows; *count in [0, C) on entry; q_new: [T][d] rows.
+ * Returns 0, or -1 if the entry count or the sizes are invalid (buf untouched).
+ */
+int orc_fps_ingest(void *buf, int dtype, int d, int C, int M, int *count,
+                   const void *q_new, int T) {
+  int c = *count;
+  if (c < 0 || c >= C || M < 1 || M >= C || d < 1 || T < 0) return -1;
+  size_t es = elem_size(dtype);
+  size_t row = es * (size_t)d;
+  char *b = (char *)buf;
+  const char *q = (const char *)q_new;
+  int *picks = (int *)malloc(sizeof(int) * M);
+  char *tmp = (char *)malloc(row * (size_t)M);
+  for (int t = 0; t < T; ++t) {
+    memcpy(b + row * c, q + row * t, row);
+    c += 1;
+    if (c == C) {
+      int n = orc_fps_stored(buf, dtype, C, d, M, picks);
+      for (int i = 0; i < n; ++i) memcpy(tmp + row * i, b + row * picks[i], row);
+      memcpy(b, tmp, row * (size_t)n);
+      c = n;
+    }
+  }
+  free(picks);
+  free(tmp);
+  *count = c;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rotary position embedding                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * orc_rope: rotate one pre-RoPE vector x[d] to position pos.
+ * The pages name RoPE without fixing a convention.  Reading (the convention
+ * of Qwen3-family models): rotate-half pairing of coordinates i and i + d/2,
+ * inverse frequency theta^(-2i/d) evaluated in binary64 and held as binary32,
+ * angle pos * freq in binary64 (exact), cos and sin evaluated in binary64 and
+ * held as binary32, rotation evaluated in binary64.  The caller rounds y once
+ * to the storage type.
+ */
+void orc_rope(const double *x, int d, long pos, double theta, double *y) {
+  int h = d / 2;
+  for (int i = 0; i < h; ++i) {
+    double freq = (double)(float)pow(theta, -(2.0 * i) / (double)d);
+    double a = (double)pos * freq;
+    double cs = (double)(float)cos(a);
+    double sn = (double)(float)sin(a);
+    y[i] = x[i] * cs - x[i + h] * sn;
+    y[i + h] = x[i + h] * cs + x[i] * sn;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Beacon-guided scoring of one (sequence slot, KV head)                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * orc_score_unit: importance scores of the L cached keys of one KV head.
+ *
+ * [IK, 三]: eviction keeps I = TopK(score(K,V), B_KV) and BeaconKV's score is
+ * the aggregated attention of the recent queries together with the beacon
+ * set.  [WZ, 信标查询怎么用]: beacons receive the position encoding of the
+ * current decode step, recent queries keep the positions where they were
+ * generated, and scores are aggregated by maximum, not mean.
+ * [WZ, 怎么挑出这几个信标] and the page glossary: beacons are the queries FPS
+ * selects from the head's query history.
+ *
+ * Readings: one query buffer per query head; the beacons of a query head are
+ * FPS(buffer[0..count), nb) at scoring time (min(nb, count) of them); each
+ * observation row attends to all L keys (no causal mask), logits are
+ * q.k / sqrt(d) on the stored (post-RoPE) keys, softmax is per row over the L
+ * keys, and the score of key j is the maximum over all rows of every query
+ * head in the KV head's GQA group of that row's softmax probability.  A
+ * recent row with a negative position is absent.  If no row is present the
+ * scores are 0.  Rotated rows are rounded once to the storage type.
+ *
+ * Layouts: K [L][d]; recent [G][R][d]; recent_pos [R]; qbuf [G][C][d];
+ * qcount [G].  Outputs: scores [L] (binary64); optional obs [G*(R+nb)][d]
+ * storage rows (row g*(R+nb)+r for recent r, g*(R+nb)+R+b for beacon b;
+ * absent rows zero), obs_valid [G*(R+nb)], lse [G*(R+nb)] (absent rows get
+ * +inf).  Returns 0, or -1 for an invalid qcount.
+ */
+int orc_score_unit(int dtype, int d, int G, const void *K, int L,
+                   const void *recent, const int *recent_pos, int R,
+                   const void *qbuf, const int *qcount, int C, int nb,
+                   long pos_now, double theta, double *scores, void *obs,
+                   int *obs_valid, double *lse) {
+  int rows = G * (R + nb);
+  size_t es = elem_size(dtype);
+  double *y = (double *)calloc((size_t)(rows > 0 ? rows : 1) * d, sizeof(double));
+  int *valid = (int *)calloc(rows > 0 ? rows : 1, sizeof(int));
+  double *x = (double *)malloc(sizeof(double) * d);
+  double *yr = (double *)malloc(sizeof(double) * d);
+  int *picks = (int *)malloc(sizeof(int) * (nb > 0 ? nb : 1));
+  int status = 0;
+
+  for (int g = 0; g < G; ++g) {
+    /* recent queries at their own positions */
+    for (int r = 0; r < R; ++r) {
+      int row = g * (R + nb) + r;
+      if (recent_pos[r] < 0) continue;
+      const char *src = (const char *)recent + es * (size_t)d * ((size_t)g * R + r);
+      for (int t = 0; t < d; ++t) x[t] = orc_load(src, dtype, t);
+      orc_rope(x, d, recent_pos[r], theta, yr);
+      for (int t = 0; t < d; ++t) {
+        /* single rounding to the storage type */
+        char cell[4];
+        orc_store(cell, dtype, 0, yr[t]);
+        y[(size_t)row * d + t] = orc_load(cell, dtype, 0);
+      }
+      valid[row] = 1;
+    }
+    /* beacons: FPS over the buffer, rotated to the current decode position */
+    int cnt = qcount[g];
+    if (cnt < 0 || cnt >= C) {
+      status = -1;
+      continue;
+    }
+    const char *hb = (const char *)qbuf + es * (size_t)d * (size_t)C * g;
+    int nsel = orc_fps_stored(hb, dtype, cnt, d, nb, picks);
+    for (int b = 0; b < nsel; ++b) {
+      int row = g * (R + nb) + R + b;
+      const char *src = hb + es * (size_t)d * picks[b];
+      for (int t = 0; t < d; ++t) x[t] = orc_load(src, dtype, t);
+      orc_rope(x, d, pos_now, theta, yr);
+      for (int t = 0; t < d; ++t) {
+        char cell[4];
+        orc_store(cell, dtype, 0, yr[t]);
+        y[(size_t)row * d + t] = orc_load(cell, dtype, 0);
+      }
+      valid[row] = 1;
+    }
+  }
+
+  /* logits, per-row log-sum-exp, max over rows of the softmax probability */
+  double *s = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * (L > 0 ? L : 1));
+  double *kj = (double *)malloc(sizeof(double) * d);
+  double inv_sqrt_d = 1.0 / sqrt((double)d);
+  for (int j = 0; j < L; ++j) {
+    for (int t = 0; t < d; ++t) kj[t] = orc_load(K, dtype, (long)j * d + t);
+    for (int r = 0; r < rows; ++r) {
+      if (!valid[r]) continue;
+      s[(size_t)r * L + j] = dot(y + (size_t)r * d, kj, d) * inv_sqrt_d;
+    }
+  }
+  double *lse_r = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
+  for (int r = 0; r < rows; ++r) {
+    if (!valid[r] || L == 0) {
+      lse_r[r] = INFINITY;
+      continue;
+    }
+    double mx = -INFINITY;
+    for (int j = 0; j < L; ++j)
+      if (s[(size_t)r * L + j] > mx) mx = s[(size_t)r * L + j];
+    double sum = 0.0;
+    for (int j = 0; j < L; ++j) sum += exp(s[(size_t)r * L + j] - mx);
+    lse_r[r] = mx + log(sum);
+  }
+  for (int j = 0; j < L; ++j) {
+    double best = 0.0;
+    for (int r = 0; r < rows; ++r) {
+      if (!valid[r]) continue;
+      double p = exp(s[(size_t)r * L + j] - lse_r[r]);
+      if (p > best) best = p;
+    }
+    scores[j] = best;
+  }
+
+  if (obs) {
+    for (int r = 0; r < rows; ++r)
+      for (int t = 0; t < d; ++t) orc_store(obs, dtype, (long)r * d + t, y[(size_t)r * d + t]);
+  }
+  if (obs_valid)
+    for (int r = 0; r < rows; ++r) obs_valid[r] = valid[r];
+  if (lse)
+    for (int r = 0; r < rows; ++r) lse[r] = lse_r[r];
+
+  free(y);
+  free(valid);
+  free(x);
+  free(yr);
+  free(picks);
+  free(s);
+  free(kj);
+  free(lse_r);
+  return status;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Selection and compaction                                                   */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  double score;
+  int index;
+} scored_t;
+
+static int by_score_desc_index_asc(const void *pa, const void *pb) {
+  const scored_t *a = (const scored_t *)pa, *b = (const scored_t *)pb;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  return (a->index > b->index) - (a->index < b->index);
+}
+
+/*
+ * orc_select: the kept set of one KV head.
+ * [IK, 三]: at eviction time keep I = TopK(score, B_KV).  [AM, "Beacon queries
+ * anticipate what will be revisited"]: the highest-scoring entries survive
+ * while a recent sliding window is always preserved.
+ *
+ * Readings: B_KV counts every kept entry, the window included; the window is
+ * the last W entries [L-W, L); the other B-W are the top scores of [0, L-W),
+ * ties broken towards the lower index; if L <= B nothing is evicted.
+ *
+ * kept[] receives min(L, B) indices in ascending order.  Returns that count,
+ * or -1 if W > B, W < 0 or B < 0.
+ */
+int orc_select(const double *scores, int L, int B, int W, int *kept) {
+  if (B < 0 || W < 0 || W > B || L < 0) return -1;
+  if (L <= B) {
+    for (int i = 0; i < L; ++i) kept[i] = i;
+    return L;
+  }
+  int n = L - W;
+  scored_t *v = (scored_t *)malloc(sizeof(scored_t) * (n > 0 ? n : 1));
+  for (int j = 0; j < n; ++j) {
+    v[j].score = scores[j];
+    v[j].index = j;
+  }
+  qsort(v, n, sizeof(scored_t), by_score_desc_index_asc);
+  char *keep = (char *)calloc(L, 1);
+  for (int i = 0; i < B - W; ++i) keep[v[i].index] = 1;
+  for (int j = L - W; j < L; ++j) keep[j] = 1;
+  int c = 0;
+  for (int j = 0; j < L; ++j)
+    if (keep[j]) kept[c++] = j;
+  free(v);
+  free(keep);
+  return c;
+}
+
+/*
+ * orc_compact: X'[i] = X[kept[i]] for i < n, as bit copies of the rows of the
+ * pre-eviction X; rows >= n are left as they were.  The pages only say the
+ * kept entries are retained; reading: an order-preserving gather into the
+ * front of the same buffer.
+ */
+void orc_compact(void *X, long row_bytes, const int *kept, int n) {
+  char *x = (char *)X;
+  char *old = (char *)malloc((size_t)row_bytes * (n > 0 ? n : 1));
+  for (int i = 0; i < n; ++i) memcpy(old + (size_t)row_bytes * i, x + (size_t)row_bytes * kept[i], row_bytes);
+  memcpy(x, old, (size_t)row_bytes * n);
+  free(old);
+}
