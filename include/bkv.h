@@ -1,0 +1,207 @@
+/*
+ * bkv.h -- C ABI of libbkv, the BeaconKV eviction hot path for AMD MI355X
+ * (gfx950).
+ *
+ * BeaconKV keeps, per attention head, a small set of "beacon" queries chosen
+ * by farthest point sampling from the head's query history, and scores the
+ * KV cache with the attention of the recent queries together with those
+ * beacons before evicting down to a budget.  Sources (web pages about the
+ * method, cited by title and section):
+ *   [WZ] wzjinhao.cn news article 56682 on BeaconKV, sections
+ *        "怎么挑出这几个信标" (FPS, Continual FPS, pre-RoPE similarity) and
+ *        "信标查询怎么用" (beacon positions, max aggregation);
+ *   [IK] inkeast.github.io MessageDaily paper-reading post on BeaconKV,
+ *        section 三 (I = TopK(score(K,V), B_KV)) and section 4.4;
+ *   [AM] aimodeling.com "BeaconKV: Beacon Queries Fix KV Eviction for Long
+ *        Reasoning", section "Beacon queries anticipate what will be
+ *        revisited" (recent window always kept; 16 beacons, 16 recent
+ *        queries, window 32 by default).
+ *
+ * Conventions for every entry point
+ *   - Every pointer except `shape` and `status_out` is a DEVICE pointer on the
+ *     current HIP device.  The caller owns and allocates every buffer,
+ *     including the workspace; the library never allocates, frees or
+ *     synchronises (bkv_read_device_status excepted) and keeps no state
+ *     between calls.
+ *   - Work is enqueued on `stream` (0 = the null stream), in call order.
+ *   - Tensors are dense and row-major in the index order written next to
+ *     them.  N = shape->n_seq, Hkv = shape->n_kv_heads, Hq =
+ *     shape->n_q_heads (a multiple of Hkv; G = Hq / Hkv), d =
+ *     shape->head_dim, Lmax = shape->max_len.  Storage element type of K, V
+ *     and every query tensor: shape->dtype.  Query head g belongs to KV head
+ *     g / G.
+ *   - The return value is a synchronous status from host-side argument
+ *     checks (BKV_E_*), or BKV_E_HIP if a launch failed; nothing is enqueued
+ *     when it is not BKV_OK.  Data-dependent violations found on the device
+ *     (a length above Lmax, a buffer count outside [0, C)) set bits of the
+ *     device status word in the workspace and the affected unit is left
+ *     untouched; read it with bkv_read_device_status.
+ *   - Calls that share a workspace must not run concurrently.
+ */
+#ifndef BKV_H
+#define BKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bkv_status {
+  BKV_OK = 0,
+  BKV_E_NULL = 1,      /* a required pointer is NULL */
+  BKV_E_SHAPE = 2,     /* a size or count is outside the supported range */
+  BKV_E_DTYPE = 3,     /* unsupported storage type */
+  BKV_E_BUDGET = 4,    /* budget < window, window < 0 or budget > max_len */
+  BKV_E_CAPACITY = 5,  /* shrink target not in [1, C), or capacity too large */
+  BKV_E_WORKSPACE = 6, /* workspace NULL, too small or not 256-byte aligned */
+  BKV_E_HIP = 7        /* a kernel launch failed */
+};
+
+enum bkv_dtype { BKV_F32 = 0, BKV_BF16 = 1 };
+
+/* Device status bits (bkv_read_device_status). */
+#define BKV_DEV_BAD_LEN 0x1   /* len[n] < 0 or len[n] > max_len */
+#define BKV_DEV_BAD_COUNT 0x2 /* qcount[n][g] < 0 or >= C on entry */
+
+/* Supported ranges (checked on the host):
+ *   head_dim in {64, 128}; C (buffer capacity) <= 256; G * (R + nb) <= 256;
+ *   R <= 64; nb <= C; max_len <= 1 << 24. */
+
+typedef struct bkv_shape {
+  int32_t n_seq;      /* N: sequence slots (e.g. layers x batch, flattened) */
+  int32_t n_kv_heads; /* Hkv */
+  int32_t n_q_heads;  /* Hq, a multiple of Hkv */
+  int32_t head_dim;   /* d */
+  int32_t max_len;    /* Lmax: rows allocated per (slot, KV head) in K and V */
+  int32_t dtype;      /* enum bkv_dtype */
+} bkv_shape;
+
+/*
+ * Workspace.  One byte buffer, 256-byte aligned, at least
+ * bkv_workspace_size(shape, R, nb) bytes, serves every call made with the
+ * same shape, R and nb.  It holds the device status word (int32 at offset 0),
+ * run statistics (uint64 rows_moved at offset 8: rows gathered by
+ * bkv_compact since the last reset), and the per-call intermediates whose
+ * offsets bkv_workspace_layout reports:
+ *   [0] obs     : rotated observation rows [N][Hkv][RP][d], storage type,
+ *                 RP = G*(R+nb) rounded up to 32; row g*(R+nb)+r holds recent
+ *                 query r of query head h*G+g, row g*(R+nb)+R+b its beacon b;
+ *                 absent rows are zero;
+ *   [1] valid   : int32 [N][Hkv][RP], 1 for present rows;
+ *   [2] lse     : float [N][Hkv][RP], natural-log row normaliser of the
+ *                 softmax (+inf for absent rows);
+ *   [3] select  : int32 [N][Hkv][2] = {first evicted index, kept count};
+ *   [4] rope    : float2 [N][R+1][d/2] (cos, sin) tables.
+ * Zero the first 256 bytes once before first use (bkv_reset_device_status).
+ */
+size_t bkv_workspace_size(const bkv_shape *shape, int32_t R, int32_t nb);
+int bkv_workspace_layout(const bkv_shape *shape, int32_t R, int32_t nb, size_t offsets[5]);
+
+/*
+ * bkv_fps_update -- Continual FPS ingest ([WZ] 怎么挑出这几个信标: a bounded
+ * buffer per attention head, compressed by FPS back to a smaller size
+ * whenever it fills; [AM]: sampling in pre-RoPE query space).
+ *
+ *   q_new  [N][Hq][T][d]  new pre-RoPE queries, oldest first (read only)
+ *   qbuf   [N][Hq][C][d]  per-query-head buffers (in/out); rows [0, count)
+ *                         are live: retained FPS picks first, then arrivals
+ *                         in time order
+ *   qcount [N][Hq]        live row count, in [0, C) on entry (in/out)
+ *   C, M                  capacity and shrink target, 1 <= M < C <= 256
+ *   T >= 0                queries per head in this call
+ *
+ * The T queries are appended one at a time; each time the count reaches C
+ * the buffer is replaced by its FPS picks (M of them, in pick order).  FPS on
+ * cosine similarity: start at the row with the lowest mean cosine to all
+ * rows, then repeatedly add the row whose maximum cosine to the picked set
+ * is lowest; ties go to the lower row.  Cosines are evaluated in binary64.
+ * Rows at or beyond the final count are unspecified.
+ */
+int bkv_fps_update(const bkv_shape *shape, const void *q_new, int32_t T, void *qbuf,
+                   int32_t *qcount, int32_t C, int32_t M, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/*
+ * bkv_score -- beacon-guided importance scores ([IK] 三 and 4.4; [WZ]
+ * 信标查询怎么用).
+ *
+ *   K          [N][Hkv][Lmax][d]  cached keys, stored after RoPE (read only)
+ *   len        [N]                cache length L of each slot, <= Lmax
+ *   recent     [N][Hq][R][d]      recent pre-RoPE queries, R >= 0
+ *   recent_pos [N][R]             their positions; a negative position marks
+ *                                 an absent query
+ *   qbuf, qcount, C               the buffers of bkv_fps_update (read only)
+ *   nb                            beacons per query head (0 <= nb <= C)
+ *   pos_now    [N]                position of the current decode step
+ *   rope_theta                    RoPE base
+ *   scores     [N][Hkv][Lmax]     output, float; entries j < L are written
+ *
+ * For every query head the beacons are FPS(qbuf[0..count), min(nb, count)).
+ * Beacons are rotated to pos_now, recent queries to their own positions
+ * (rotate-half RoPE, inverse frequency theta^(-2i/d) held in binary32, angle
+ * in binary64, cos/sin held in binary32, rotation in binary64, result rounded
+ * once to the storage type).  Every observation row r of the G query heads
+ * of a KV head attends to all L keys: p_r = softmax_j(q_r . k_j / sqrt(d)),
+ * and score_j = max_r p_r(j).  Without any present row the scores are 0.
+ */
+int bkv_score(const bkv_shape *shape, const void *K, const int32_t *len, const void *recent,
+              const int32_t *recent_pos, int32_t R, const void *qbuf, const int32_t *qcount,
+              int32_t C, int32_t nb, const int32_t *pos_now, double rope_theta, float *scores,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bkv_select -- kept set ([IK] 三: I = TopK(score, B_KV); [AM]: the recent
+ * window is always kept).
+ *
+ *   scores [N][Hkv][Lmax]  non-negative finite floats, j < len[n] read
+ *   len    [N]             current lengths (read only)
+ *   budget, window         B_KV (window included) and W, 0 <= W <= B_KV <= Lmax
+ *   kept   [N][Hkv][B_KV]  output: ascending kept indices
+ *
+ * If L <= B_KV every index is kept (kept[i] = i for i < L, -1 after).
+ * Otherwise kept = [L-W, L) plus the B_KV-W highest scores of [0, L-W),
+ * ties at the cut going to the lower index.  Selection is exact on the
+ * binary32 scores.  Also records, per (slot, KV head), the first evicted
+ * index and the kept count in the workspace for bkv_compact.
+ */
+int bkv_select(const bkv_shape *shape, const float *scores, const int32_t *len, int32_t budget,
+               int32_t window, int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bkv_compact -- in-place, order-preserving gather of the kept rows.
+ *
+ *   K, V [N][Hkv][Lmax][d]  in/out; row i <- row kept[i] for i < kept count
+ *                           (bit copies of the pre-call rows); rows at or
+ *                           beyond the kept count are left as they were
+ *   len  [N]                set to min(len, budget)
+ *   kept                    the output of bkv_select with the same workspace
+ *
+ * Must follow bkv_select on the same workspace, budget and stream.  Adds the
+ * number of moved rows (per tensor) to the workspace statistic rows_moved.
+ */
+int bkv_compact(const bkv_shape *shape, void *K, void *V, int32_t *len, int32_t budget,
+                const int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* bkv_select followed by bkv_compact. */
+int bkv_select_compact(const bkv_shape *shape, const float *scores, void *K, void *V,
+                       int32_t *len, int32_t budget, int32_t window, int32_t *kept, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/* Text for a bkv_status value (static string). */
+const char *bkv_status_string(int status);
+
+/* Copies the device status word to *status_out; synchronises `stream`. */
+int bkv_read_device_status(const void *ws, int32_t *status_out, hipStream_t stream);
+
+/* Zeroes the status word and statistics (first 256 bytes of ws) on `stream`. */
+int bkv_reset_device_status(void *ws, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BKV_H */

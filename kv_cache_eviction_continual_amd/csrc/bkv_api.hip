@@ -1,0 +1,249 @@
+// bkv_api.hip -- host side of the libbkv C ABI (argument checks, workspace
+// layout, kernel dispatch).  Declarations and contracts: include/bkv.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bkv.h"
+#include "bkv_device.hpp"
+
+namespace bkv {
+
+template <int DT, int D>
+hipError_t launch_fps_update(const void*, int, void*, int32_t*, int, int, int, int32_t*, hipStream_t);
+template <int DT, int D>
+hipError_t launch_obs_build(const void*, const int32_t*, int, int, const void*, const int32_t*, int, const int32_t*,
+                            double, float2*, void*, int32_t*, int, int, int, int, int32_t*, hipStream_t);
+template <int DT, int D>
+hipError_t launch_score(const void*, const int32_t*, int, int, int, const void*, const int32_t*, int, float*, float*,
+                        int32_t*, hipStream_t);
+hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
+                         hipStream_t);
+hipError_t launch_compact(void*, void*, const int32_t*, const int32_t*, int32_t*, int, int, int, int, int,
+                          unsigned long long*, hipStream_t);
+
+__global__ void zero_header_kernel(int32_t* w) {
+  if (threadIdx.x < (int)(kHeaderBytes / 4)) w[threadIdx.x] = 0;
+}
+
+namespace {
+
+constexpr int kMaxCapacity = 256;
+constexpr int kMaxRows = 256;
+constexpr int kMaxRecent = 64;
+constexpr int kMaxLen = 1 << 24;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_bytes(int dtype) { return dtype == BKV_F32 ? 4 : 2; }
+
+int check_shape(const bkv_shape* s) {
+  if (!s) return BKV_E_NULL;
+  if (s->dtype != BKV_F32 && s->dtype != BKV_BF16) return BKV_E_DTYPE;
+  if (s->n_seq < 0 || s->n_kv_heads < 1 || s->n_q_heads < s->n_kv_heads || s->n_q_heads % s->n_kv_heads != 0)
+    return BKV_E_SHAPE;
+  if (s->head_dim != 64 && s->head_dim != 128) return BKV_E_SHAPE;
+  if (s->max_len < 0 || s->max_len > kMaxLen) return BKV_E_SHAPE;
+  return BKV_OK;
+}
+
+struct WsLayout {
+  size_t obs, valid, lse, select, rope, total;
+  int RP;
+};
+
+// Header, then the select table (depends on the shape only, so bkv_select
+// and bkv_compact need no R or nb), then the scoring intermediates.
+size_t select_end(const bkv_shape* s) {
+  return align256(kHeaderBytes + (size_t)s->n_seq * s->n_kv_heads * 2 * sizeof(int32_t));
+}
+
+bool layout(const bkv_shape* s, int R, int nb, WsLayout* out) {
+  const int G = s->n_q_heads / s->n_kv_heads;
+  const long rows = (long)G * (R + nb);
+  if (R < 0 || nb < 0 || rows > kMaxRows) return false;
+  const int RP = (int)(((rows + 31) / 32) * 32);
+  const size_t units = (size_t)s->n_seq * s->n_kv_heads;
+  out->RP = RP;
+  out->select = kHeaderBytes;
+  size_t off = select_end(s);
+  out->obs = off;
+  off = align256(off + units * RP * s->head_dim * elem_bytes(s->dtype));
+  out->valid = off;
+  off = align256(off + units * RP * sizeof(int32_t));
+  out->lse = off;
+  off = align256(off + units * RP * sizeof(float));
+  out->rope = off;
+  off = align256(off + (size_t)s->n_seq * (R + 1) * (s->head_dim / 2) * sizeof(float2));
+  out->total = off;
+  return true;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return BKV_E_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return BKV_E_WORKSPACE;
+  if (ws_bytes < need) return BKV_E_WORKSPACE;
+  return BKV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_E_HIP; }
+
+}  // namespace
+}  // namespace bkv
+
+using namespace bkv;
+
+extern "C" {
+
+size_t bkv_workspace_size(const bkv_shape* shape, int32_t R, int32_t nb) {
+  if (check_shape(shape) != BKV_OK) return 0;
+  WsLayout w;
+  if (!layout(shape, R, nb, &w)) return 0;
+  return w.total;
+}
+
+int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t offsets[5]) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (!offsets) return BKV_E_NULL;
+  WsLayout w;
+  if (!layout(shape, R, nb, &w)) return BKV_E_SHAPE;
+  offsets[0] = w.obs;
+  offsets[1] = w.valid;
+  offsets[2] = w.lse;
+  offsets[3] = w.select;
+  offsets[4] = w.rope;
+  return BKV_OK;
+}
+
+int bkv_fps_update(const bkv_shape* shape, const void* q_new, int32_t T, void* qbuf, int32_t* qcount, int32_t C,
+                   int32_t M, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (C < 2 || C > kMaxCapacity || M < 1 || M >= C) return BKV_E_CAPACITY;
+  if (T < 0) return BKV_E_SHAPE;
+  if (!qbuf || !qcount || (T > 0 && !q_new)) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, kHeaderBytes)) != BKV_OK) return st;
+  const int heads = shape->n_seq * shape->n_q_heads;
+  if (heads == 0) return BKV_OK;
+  int32_t* w = (int32_t*)ws;
+  hipError_t e;
+  if (shape->dtype == BKV_BF16)
+    e = shape->head_dim == 128 ? launch_fps_update<BKV_BF16, 128>(q_new, T, qbuf, qcount, C, M, heads, w, stream)
+                               : launch_fps_update<BKV_BF16, 64>(q_new, T, qbuf, qcount, C, M, heads, w, stream);
+  else
+    e = shape->head_dim == 128 ? launch_fps_update<BKV_F32, 128>(q_new, T, qbuf, qcount, C, M, heads, w, stream)
+                               : launch_fps_update<BKV_F32, 64>(q_new, T, qbuf, qcount, C, M, heads, w, stream);
+  return hip_status(e);
+}
+
+int bkv_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
+              const int32_t* recent_pos, int32_t R, const void* qbuf, const int32_t* qcount, int32_t C, int32_t nb,
+              const int32_t* pos_now, double rope_theta, float* scores, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (C < 2 || C > kMaxCapacity || nb < 0 || nb > C) return BKV_E_CAPACITY;
+  if (R < 0 || R > kMaxRecent) return BKV_E_SHAPE;
+  if (!(rope_theta > 1.0)) return BKV_E_SHAPE;
+  WsLayout w;
+  if (!layout(shape, R, nb, &w)) return BKV_E_SHAPE;
+  if (w.RP == 0) return BKV_E_SHAPE;  // no observation rows at all
+  if (!K || !len || !scores || !pos_now || !qbuf || !qcount) return BKV_E_NULL;
+  if (R > 0 && (!recent || !recent_pos)) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, w.total)) != BKV_OK) return st;
+  const int N = shape->n_seq, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  unsigned char* base = (unsigned char*)ws;
+  int32_t* words = (int32_t*)ws;
+  float2* tab = (float2*)(base + w.rope);
+  void* obs = base + w.obs;
+  int32_t* valid = (int32_t*)(base + w.valid);
+  float* lse = (float*)(base + w.lse);
+  hipError_t e;
+#define BKV_SCORE_CASE(DT, D)                                                                                  \
+  e = launch_obs_build<DT, D>(qbuf, qcount, C, nb, recent, recent_pos, R, pos_now, rope_theta, tab, obs, valid, \
+                              N, Hq, Hkv, w.RP, words, stream);                                                 \
+  if (e == hipSuccess)                                                                                         \
+    e = launch_score<DT, D>(K, len, N, Hkv, shape->max_len, obs, valid, w.RP, scores, lse, words, stream);
+  if (shape->dtype == BKV_BF16) {
+    if (shape->head_dim == 128) {
+      BKV_SCORE_CASE(BKV_BF16, 128)
+    } else {
+      BKV_SCORE_CASE(BKV_BF16, 64)
+    }
+  } else {
+    if (shape->head_dim == 128) {
+      BKV_SCORE_CASE(BKV_F32, 128)
+    } else {
+      BKV_SCORE_CASE(BKV_F32, 64)
+    }
+  }
+#undef BKV_SCORE_CASE
+  return hip_status(e);
+}
+
+int bkv_select(const bkv_shape* shape, const float* scores, const int32_t* len, int32_t budget, int32_t window,
+               int32_t* kept, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (window < 0 || budget < window || budget < 1 || budget > shape->max_len) return BKV_E_BUDGET;
+  if (!scores || !len || !kept) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, select_end(shape))) != BKV_OK) return st;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  int32_t* words = (int32_t*)ws;
+  int32_t* sel = (int32_t*)((unsigned char*)ws + kHeaderBytes);
+  return hip_status(launch_select(scores, len, N, Hkv, shape->max_len, budget, window, kept, sel, words, stream));
+}
+
+int bkv_compact(const bkv_shape* shape, void* K, void* V, int32_t* len, int32_t budget, const int32_t* kept,
+                void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (budget < 1 || budget > shape->max_len) return BKV_E_BUDGET;
+  if (!K || !V || !len || !kept) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, select_end(shape))) != BKV_OK) return st;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  const int32_t* sel = (const int32_t*)((unsigned char*)ws + kHeaderBytes);
+  unsigned long long* moved = (unsigned long long*)((unsigned char*)ws + 8);
+  const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
+  return hip_status(launch_compact(K, V, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, stream));
+}
+
+int bkv_select_compact(const bkv_shape* shape, const float* scores, void* K, void* V, int32_t* len, int32_t budget,
+                       int32_t window, int32_t* kept, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = bkv_select(shape, scores, len, budget, window, kept, ws, ws_bytes, stream);
+  if (st != BKV_OK) return st;
+  return bkv_compact(shape, K, V, len, budget, kept, ws, ws_bytes, stream);
+}
+
+const char* bkv_status_string(int status) {
+  switch (status) {
+    case BKV_OK: return "ok";
+    case BKV_E_NULL: return "a required pointer is NULL";
+    case BKV_E_SHAPE: return "a size or count is outside the supported range";
+    case BKV_E_DTYPE: return "unsupported storage type";
+    case BKV_E_BUDGET: return "budget and window are inconsistent (need 0 <= window <= budget <= max_len)";
+    case BKV_E_CAPACITY: return "buffer capacity, shrink target or beacon count out of range";
+    case BKV_E_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
+    case BKV_E_HIP: return "a HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int bkv_read_device_status(const void* ws, int32_t* status_out, hipStream_t stream) {
+  if (!ws || !status_out) return BKV_E_NULL;
+  hipError_t e = hipMemcpyAsync(status_out, ws, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_status(e);
+}
+
+int bkv_reset_device_status(void* ws, hipStream_t stream) {
+  if (!ws) return BKV_E_NULL;
+  if (((uintptr_t)ws & 255) != 0) return BKV_E_WORKSPACE;
+  hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(64), 0, stream, (int32_t*)ws);
+  return hip_status(hipGetLastError());
+}
+
+}  // extern "C"
