@@ -1,0 +1,312 @@
+"""Benchmark of the BeaconKV eviction hot path on one MI355X.
+
+One step = one eviction period of the whole path over the full batch:
+  1. the cache grows back to L by the period's 128 decode steps (the length
+     array is reset; the 128 tail rows hold earlier, already-written keys),
+  2. bkv_fps_update ingests the period's 128 pre-RoPE queries per query head
+     (Continual FPS, shrinking buffers that fill),
+  3. bkv_score selects beacons, rotates observation rows and scores every
+     cached key,
+  4. bkv_select keeps the window plus the top B_KV - W,
+  5. bkv_compact gathers the kept K/V rows in place.
+
+Workload: all 36 layers of Qwen3-4B (32 query / 8 KV heads, d = 128) at batch
+16, bf16, evicting 2176 -> 2048 (window 32, 16 recent + 16 beacons, buffer
+128 -> 16), seeded synthetic data.  Inputs are resident in HBM before timing.
+
+Prints one JSON line (see the keys below).  --gpus N > 1 is refused: this
+build targets one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from kv_cache_eviction_continual_amd import bkv, configs, synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+CFG = 3
+N_POOL = 4          # distinct 128-step query blocks cycled over the steps
+N_EVENTS = 240      # evictions in a 32K-token generation (first at L = 2176)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("fps.hip", "score.hip", "select.hip", "bkv_api.hip", "bkv_device.hpp"):
+        with open(os.path.join(ROOT, "kv_cache_eviction_continual_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+class State:
+    """Device-resident state of the metric workload."""
+
+    def __init__(self, w, dev):
+        self.w = w
+        N, Hq, Hkv, d = w.n_slots, w.n_q_heads, w.n_kv_heads, w.head_dim
+        self.N = N
+        syn = synth.Synth(w, seed=0, device=dev)
+        self.syn = syn
+        log("generating K/V %s x 2 and %d query blocks" % ((N, Hkv, w.max_len, d), N_POOL))
+        self.K = syn.keys()
+        self.V = syn.values()
+        self.blocks = [syn.query_block(b) for b in range(N_POOL)]
+        R = w.n_recent
+        self.recent = [blk[:, :, -R:].contiguous() for blk in self.blocks]
+        self.shape = bkv.make_shape(N, Hkv, Hq, d, w.max_len, self.K.dtype)
+        self.ws = bkv.alloc_workspace(self.shape, R, w.n_beacons, device=dev)
+        self.qbuf = torch.zeros(N, Hq, w.capacity, d, dtype=self.K.dtype, device=dev)
+        self.qcount = torch.zeros(N, Hq, dtype=torch.int32, device=dev)
+        self.len_full = torch.full((N,), w.length, dtype=torch.int32, device=dev)
+        self.length = self.len_full.clone()
+        self.scores = torch.empty(N, Hkv, w.max_len, dtype=torch.float32, device=dev)
+        self.kept = torch.empty(N, Hkv, w.budget, dtype=torch.int32, device=dev)
+        now0 = w.length - 1
+        ev = np.arange(N_EVENTS)
+        pos_now = (now0 + w.interval * ev).astype(np.int32)
+        self.pos_now = torch.from_numpy(np.repeat(pos_now[:, None], N, axis=1)).to(dev).contiguous()
+        rp = pos_now[:, None] - np.arange(R - 1, -1, -1)[None, :]
+        self.recent_pos = torch.from_numpy(np.repeat(rp[:, None, :], N, axis=1).astype(np.int32)).to(dev).contiguous()
+        # warm the buffers with the first L queries of the stream (17 periods)
+        for b in range(w.warm_steps // w.interval):
+            blk = self.blocks[b % N_POOL]
+            bkv.bkv_fps_update(self.shape, blk, blk.shape[2], self.qbuf, self.qcount, w.capacity, w.shrink_to, self.ws)
+        torch.cuda.synchronize()
+
+    def step(self, i, ev=None):
+        w = self.w
+        p = i % N_POOL
+        e = i % N_EVENTS
+        if ev is not None:
+            ev[0].record()
+        self.length.copy_(self.len_full)
+        if ev is not None:
+            ev[1].record()
+        bkv.bkv_fps_update(self.shape, self.blocks[p], w.interval, self.qbuf, self.qcount, w.capacity, w.shrink_to,
+                           self.ws)
+        if ev is not None:
+            ev[2].record()
+        bkv.bkv_score(self.shape, self.K, self.length, self.recent[p], self.recent_pos[e], w.n_recent, self.qbuf,
+                      self.qcount, w.capacity, w.n_beacons, self.pos_now[e], w.rope_theta, self.scores, self.ws)
+        if ev is not None:
+            ev[3].record()
+        bkv.bkv_select(self.shape, self.scores, self.length, w.budget, w.window, self.kept, self.ws)
+        if ev is not None:
+            ev[4].record()
+        bkv.bkv_compact(self.shape, self.K, self.V, self.length, w.budget, self.kept, self.ws)
+        if ev is not None:
+            ev[5].record()
+
+
+def copy_probe(dev, nbytes=1 << 30, reps=10):
+    """Bandwidth of a plain device copy of known size (read + write bytes)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GBps": 2 * nbytes / ms / 1e6}
+
+
+def cpu_baseline(st: State, budget_s: float = 12.0, min_units: int = 4, max_units: int = 2048):
+    """The CPU oracle (single-threaded C, binary64) on a bounded sample of
+    (slot, KV head) units of the same workload: one period's ingest for the
+    unit's query heads, scoring, selection and compaction."""
+    import oracle
+
+    w = st.w
+    G = w.group
+    rng = np.random.default_rng(1234)
+    units_all = [(int(n), int(h)) for n, h in zip(rng.integers(0, st.N, max_units), rng.integers(0, w.n_kv_heads, max_units))]
+    blocks_np = {}
+    done = 0
+    t_total = 0.0
+    e = 0
+    p = 0
+    for (n, h) in units_all:
+        g0 = h * G
+        K_u = synth.to_numpy_storage(st.K_pristine[n, h])
+        V_u = synth.to_numpy_storage(st.V_pristine[n, h])
+        # untimed: replay the warm-up ingest of the unit's query heads
+        qbuf = np.zeros((1, G, w.capacity, w.head_dim), dtype=np.uint16)
+        qcount = np.zeros((1, G), dtype=np.int32)
+        for b in range(w.warm_steps // w.interval):
+            key = (b % N_POOL, n, h)
+            if key not in blocks_np:
+                blocks_np[key] = synth.to_numpy_storage(st.blocks[b % N_POOL][n:n + 1, g0:g0 + G])
+            oracle.fps_update(blocks_np[key], qbuf, qcount, w.shrink_to)
+        blk = blocks_np.setdefault((p, n, h), synth.to_numpy_storage(st.blocks[p][n:n + 1, g0:g0 + G]))
+        recent = synth.to_numpy_storage(st.recent[p][n, g0:g0 + G])
+        rpos = st.recent_pos[e, n].cpu().numpy()
+        pos_now = int(st.pos_now[e, n])
+        t0 = time.perf_counter()
+        oracle.fps_update(blk, qbuf, qcount, w.shrink_to)
+        s, _, _, _ = oracle.score_unit(K_u, w.length, recent, rpos, qbuf[0], qcount[0], w.n_beacons, pos_now,
+                                       w.rope_theta)
+        kept = oracle.select(s, w.length, w.budget, w.window)
+        oracle.compact(K_u, kept)
+        oracle.compact(V_u, kept)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if done >= min_units and t_total >= budget_s:
+            break
+    per_unit = t_total / done
+    units_per_pass = st.N * w.n_kv_heads
+    return {
+        "value": 1.0 / (per_unit * units_per_pass),
+        "unit": "passes/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d (slot, KV head) units of the workload, each: ingest of one 128-query block for its %d query "
+                  "heads, beacon FPS, scoring at L=%d, selection and compaction; %.1f s of oracle time "
+                  "(%.3f s per unit), extrapolated to %d units per pass" % (done, G, w.length, t_total, per_unit,
+                                                                           units_per_pass),
+    }
+
+
+def load_traffic(src_hash):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except Exception:
+        return None
+    if t.get("kernel_source_hash") != src_hash:
+        return None
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for the CPU baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = configs.get(CFG)
+    bkv.load()
+
+    st = State(w, dev)
+    if not args.no_cpu_baseline:
+        # pristine copies of the cache for the oracle sample, taken before any compaction
+        st.K_pristine = st.K.clone()
+        st.V_pristine = st.V.clone()
+    cp = copy_probe(dev)
+    log("copy probe: %.0f GB/s" % cp["GBps"])
+
+    for i in range(args.warmup):
+        st.step(i)
+    torch.cuda.synchronize()
+    bkv.bkv_reset_device_status(st.ws)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        st.step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = bkv.bkv_read_device_status(st.ws)
+    assert status == 0, "device status %d" % status
+    rows_moved = bkv.ws_rows_moved(st.ws)
+
+    stage_names = ["grow", "fps_update", "score", "select", "compact"]
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
+                for j, n in enumerate(stage_names)}
+    ms_per_step = elapsed * 1e3 / K
+    passes_per_s = K / elapsed
+
+    # algorithmic bytes
+    units = st.N * w.n_kv_heads
+    row_bytes = w.head_dim * 2
+    L = w.length
+    score_bytes = units * (L * row_bytes + w.obs_rows * row_bytes + L * 4)
+    compact_bytes = (rows_moved / K) * row_bytes * 2          # rows_moved counts K and V rows
+    entries = units * L
+    score_compact_gbps = (score_bytes + compact_bytes) / ((stage_ms["score"] + stage_ms["compact"]) * 1e6)
+
+    dominant = max(("score", "compact"), key=lambda n: stage_ms[n])
+    dom_bytes = compact_bytes if dominant == "compact" else score_bytes
+    achieved = dom_bytes / (stage_ms[dominant] * 1e6)
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(src_hash)
+    dom_traffic = None
+    if traffic and dominant in traffic.get("kernels", {}):
+        dom_traffic = traffic["kernels"][dominant].get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": "eviction passes/s + KV entries scored/s (HBM GB/s, % peak), Qwen3-4B b16 B=2K",
+        "value": passes_per_s,
+        "unit": "passes/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": w.batch, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "cache_len": L, "budget": w.budget,
+                   "window": w.window, "recent": w.n_recent, "beacons": w.n_beacons, "fps_capacity": w.capacity,
+                   "fps_shrink_to": w.shrink_to, "queries_per_step": w.interval},
+        "entries_scored_per_s": entries * passes_per_s,
+        "score_compact_GBps": score_compact_gbps,
+        "score_compact_frac_of_peak": score_compact_gbps / HBM_PEAK_GBPS,
+        "stage_ms": stage_ms,
+        "algorithmic_bytes_per_step": {"score": score_bytes, "compact": compact_bytes},
+        "copy_probe_GBps": cp["GBps"],
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": dom_traffic,
+        },
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(st, budget_s=args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
