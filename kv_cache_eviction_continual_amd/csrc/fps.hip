@@ -14,16 +14,25 @@
 //
 // FPS on cosine similarity: start at the row with the lowest mean cosine to
 // all rows; then repeatedly add the row with the lowest maximum cosine to the
-// picked set; ties go to the lower row.  All cosines are evaluated in
-// binary64 from the stored values (bf16 and fp32 widen exactly), so the
-// argmin decisions are those of exact arithmetic up to binary64 rounding.
+// picked set; ties go to the lower row.
 //
-// Work split: one workgroup of 256 threads per query head.  The live buffer
-// sits in LDS in its storage type (row stride padded by 16 bytes).  A
-// candidate row is handled by P = d/32 adjacent lanes, each owning 32
-// dimensions; a pick needs one 32-term binary64 dot product per owned
-// candidate, a P-lane butterfly, a wave argmin and a cross-wave argmin
-// through LDS (one barrier per pick).
+// The decisions are those of binary64 evaluation:
+//   * the start (mean cosines) is evaluated in binary64;
+//   * the greedy rounds run on the Gram matrix X X^T from the matrix cores
+//     (bf16 or fp32 products are exact, sums are fp32), which bounds the
+//     error of every fp32 cosine by eps = 4 (d + 8) 2^-24 (fp32 dot-product
+//     error bound gamma_d plus the normalisation roundings, doubled).  When
+//     the best candidate is not ahead of the runner-up by more than 2 eps,
+//     the maximum cosines of every candidate inside that window are
+//     recomputed from the rows in binary64 and decide the pick;
+//   * rows whose norms leave [1e-15, 1e18] (where fp32 Gram entries could
+//     underflow or overflow) send the whole call to a plain binary64 path.
+//
+// One workgroup of 64 * NW threads per query head handles up to 32 * NW
+// rows; thread i owns candidate row i.  The live buffer sits in LDS in its
+// storage type (rows padded by 16 bytes); wave w keeps Gram rows
+// [32 w, 32 w + 32) in its MFMA accumulators, and each pick publishes one
+// Gram row through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,91 +40,109 @@
 
 namespace bkv {
 
-constexpr int kFpsThreads = 256;
-constexpr int kFpsWaves = kFpsThreads / 64;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 fps_bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float fps_floatx16;
 
-template <int DT, int D>
-struct FpsLayout {
+template <int DT, int D, int NW>
+struct Fps {
   using E = Elem<DT>;
+  using ET = typename E::T;
+  static constexpr int NT = 64 * NW;
+  static constexpr int kMaxRows = 32 * NW;
   static constexpr int kRowBytes = D * E::kBytes;
-  static constexpr int kRowStride = kRowBytes + 16;  // LDS padding against bank conflicts
-  static constexpr int kP = D / 32;                  // lanes per candidate
-  static constexpr int kGroups = kFpsThreads / kP;   // candidates handled per sweep
-  static constexpr int kMaxOwn = (256 + kGroups - 1) / kGroups;  // C <= 256
+  static constexpr int kRowStride = kRowBytes + 16;
+  static constexpr int kU = kRowBytes / 16;   // 16-byte units per row
+  static constexpr int kP = D / 32;           // lanes per exact dot product (32 dims each)
+  static constexpr int kGroups = NT / kP;     // exact dot products per sweep
+  static constexpr float kEps = 4.0f * (D + 8) * 5.9604644775390625e-8f;
 };
 
-// LDS carve-up shared by both kernels (C = capacity, M = extra rows).
 struct FpsSmem {
-  unsigned char* rows;  // [C + M] rows of kRowStride bytes
-  double* inv_n;        // [256]
+  unsigned char* rows;  // row r at rows + r * kRowStride
+  double* inv64;        // [kMaxRows] 1 / max(|x|, 1e-12), binary64
+  float* inv32;         // [kMaxRows] the same, binary32
+  float* rowbuf;        // [kMaxRows] published Gram row
   double* svec;         // [D]
-  double* part;         // [kFpsThreads] partial sums
-  double* slot_v;       // [2][kFpsWaves]
-  int* slot_i;          // [2][kFpsWaves]
-  int* picks;           // [256]
+  double* part;         // [NT]
+  double* dslot;        // [2][NW] exact argmin values
+  int* islot;           // [2][NW] exact / fp32 argmin indices
+  float* fslot1;        // [2][NW] fp32 best values
+  float* fslot2;        // [2][NW] fp32 runner-up values
+  int* picks;           // [kMaxRows]
+  int* ulist;           // [kMaxRows] candidates of an uncertain round
+  double* mexact;       // [kMaxRows] their binary64 max cosines
+  double* pairv;        // [kGroups]
+  int* pairu;           // [kGroups]
+  int* misc;            // [16]
 };
 
-template <int DT, int D>
-__device__ inline FpsSmem carve(unsigned char* smem, int nrows) {
-  using Lay = FpsLayout<DT, D>;
+template <int DT, int D, int NW>
+__host__ __device__ constexpr size_t fps_smem_bytes(int nrows) {
+  using F = Fps<DT, D, NW>;
+  return (((size_t)nrows * F::kRowStride + 15) & ~(size_t)15) + F::kMaxRows * (8 + 4 + 4 + 4 + 4 + 8) + D * 8 +
+         F::NT * 8 + 2 * NW * (8 + 4 + 4 + 4) + F::kGroups * (8 + 4) + 64 + 128;
+}
+
+template <int DT, int D, int NW>
+__device__ inline FpsSmem fps_carve(unsigned char* smem, int nrows) {
+  using F = Fps<DT, D, NW>;
   FpsSmem s;
-  size_t off = 0;
+  size_t off = ((size_t)nrows * F::kRowStride + 15) & ~(size_t)15;
   s.rows = smem;
-  off += (size_t)nrows * Lay::kRowStride;
-  off = (off + 15) & ~(size_t)15;
-  s.inv_n = reinterpret_cast<double*>(smem + off);
-  off += 256 * sizeof(double);
-  s.svec = reinterpret_cast<double*>(smem + off);
-  off += D * sizeof(double);
-  s.part = reinterpret_cast<double*>(smem + off);
-  off += kFpsThreads * sizeof(double);
-  s.slot_v = reinterpret_cast<double*>(smem + off);
-  off += 2 * kFpsWaves * sizeof(double);
-  s.slot_i = reinterpret_cast<int*>(smem + off);
-  off += 2 * kFpsWaves * sizeof(int);
-  s.picks = reinterpret_cast<int*>(smem + off);
+  auto take = [&](size_t bytes) {
+    unsigned char* p = smem + off;
+    off += (bytes + 7) & ~(size_t)7;
+    return p;
+  };
+  s.inv64 = reinterpret_cast<double*>(take(F::kMaxRows * 8));
+  s.mexact = reinterpret_cast<double*>(take(F::kMaxRows * 8));
+  s.svec = reinterpret_cast<double*>(take(D * 8));
+  s.part = reinterpret_cast<double*>(take(F::NT * 8));
+  s.dslot = reinterpret_cast<double*>(take(2 * NW * 8));
+  s.pairv = reinterpret_cast<double*>(take(F::kGroups * 8));
+  s.inv32 = reinterpret_cast<float*>(take(F::kMaxRows * 4));
+  s.rowbuf = reinterpret_cast<float*>(take(F::kMaxRows * 4));
+  s.fslot1 = reinterpret_cast<float*>(take(2 * NW * 4));
+  s.fslot2 = reinterpret_cast<float*>(take(2 * NW * 4));
+  s.islot = reinterpret_cast<int*>(take(2 * NW * 4));
+  s.picks = reinterpret_cast<int*>(take(F::kMaxRows * 4));
+  s.ulist = reinterpret_cast<int*>(take(F::kMaxRows * 4));
+  s.pairu = reinterpret_cast<int*>(take(F::kGroups * 4));
+  s.misc = reinterpret_cast<int*>(take(64));  // block-scan scratch (one int per wave)
   return s;
 }
 
-template <int DT, int D>
-__host__ __device__ constexpr size_t fps_smem_bytes(int nrows) {
-  return (((size_t)nrows * FpsLayout<DT, D>::kRowStride + 15) & ~(size_t)15) + 256 * sizeof(double) +
-         D * sizeof(double) + kFpsThreads * sizeof(double) + 2 * kFpsWaves * (sizeof(double) + sizeof(int)) +
-         256 * sizeof(int);
+template <int DT, int D, int NW>
+__device__ inline const typename Elem<DT>::T* fps_row(const FpsSmem& s, int r) {
+  return reinterpret_cast<const typename Elem<DT>::T*>(s.rows + (size_t)r * Fps<DT, D, NW>::kRowStride);
 }
 
-// Widen the 32-dimension slice `p` of LDS row `r` to binary64.
-template <int DT, int D>
-__device__ inline void load_slice(const FpsSmem& s, int r, int p, double (&x)[32]) {
-  using Lay = FpsLayout<DT, D>;
+// binary64 dot product of dims [32 q, 32 q + 32) of rows a and b
+template <int DT, int D, int NW>
+__device__ inline double dot_slice64(const FpsSmem& s, int a, int b, int q) {
   using E = Elem<DT>;
-  const typename E::T* row =
-      reinterpret_cast<const typename E::T*>(s.rows + (size_t)r * Lay::kRowStride) + p * 32;
-  constexpr int kPer16 = 16 / E::kBytes;
-#pragma unroll
-  for (int q = 0; q < 32 / kPer16; ++q) {
-    uint4 w = reinterpret_cast<const uint4*>(row)[q];
-    const typename E::T* e = reinterpret_cast<const typename E::T*>(&w);
-#pragma unroll
-    for (int k = 0; k < kPer16; ++k) x[q * kPer16 + k] = E::to_f64(e[k]);
-  }
+  const typename E::T* xa = fps_row<DT, D, NW>(s, a) + 32 * q;
+  const typename E::T* xb = fps_row<DT, D, NW>(s, b) + 32 * q;
+  double acc = 0.0;
+#pragma unroll 8
+  for (int t = 0; t < 32; ++t) acc = fma(E::to_f64(xa[t]), E::to_f64(xb[t]), acc);
+  return acc;
 }
 
 template <int P>
-__device__ inline double sum_over_p(double v) {
+__device__ inline double sum_lanes(double v) {
 #pragma unroll
   for (int off = 1; off < P; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
-// Block-wide argmin of (value, index) with the strict order of `better`.
-// Every thread passes its candidate; every thread receives the winner.
-template <int P>
-__device__ inline int block_argmin(double v, int i, const FpsSmem& s, int parity) {
+// Block-wide argmin of (value, index); every thread gets the winning index.
+template <int NW>
+__device__ inline int block_argmin64(double v, int i, const FpsSmem& s, int& parity) {
 #pragma unroll
-  for (int off = P; off < 64; off <<= 1) {
-    double ov = __shfl_xor(v, off, 64);
-    int oi = __shfl_xor(i, off, 64);
+  for (int off = 1; off < 64; off <<= 1) {
+    const double ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(i, off, 64);
     if (better(ov, oi, v, i)) {
       v = ov;
       i = oi;
@@ -123,75 +150,204 @@ __device__ inline int block_argmin(double v, int i, const FpsSmem& s, int parity
   }
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    s.slot_v[parity * kFpsWaves + wave] = v;
-    s.slot_i[parity * kFpsWaves + wave] = i;
+    s.dslot[parity * NW + wave] = v;
+    s.islot[parity * NW + wave] = i;
   }
   __syncthreads();
-  double bv = s.slot_v[parity * kFpsWaves];
-  int bi = s.slot_i[parity * kFpsWaves];
+  double bv = s.dslot[parity * NW];
+  int bi = s.islot[parity * NW];
 #pragma unroll
-  for (int w = 1; w < kFpsWaves; ++w) {
-    double ov = s.slot_v[parity * kFpsWaves + w];
-    int oi = s.slot_i[parity * kFpsWaves + w];
+  for (int w = 1; w < NW; ++w) {
+    const double ov = s.dslot[parity * NW + w];
+    const int oi = s.islot[parity * NW + w];
     if (better(ov, oi, bv, bi)) {
       bv = ov;
       bi = oi;
     }
   }
+  parity ^= 1;
   return bi;
 }
 
-// FPS over LDS rows [0, c): writes min(k, c) picks to s.picks and returns the
-// count.  All threads of the block must call it.
-template <int DT, int D>
+__device__ inline bool fbetter(float v, int i, float bv, int bi) { return v < bv || (v == bv && i < bi); }
+
+// Block-wide (best value, best index, runner-up value) over one fp32 value
+// per thread.
+template <int NW>
+__device__ inline void block_best2(float v, int i, const FpsSmem& s, int& parity, float& b1, int& bi, float& b2) {
+  float v2 = __builtin_huge_valf();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(i, off, 64);
+    const float ov2 = __shfl_xor(v2, off, 64);
+    if (fbetter(ov, oi, v, i)) {
+      v2 = fminf(ov2, v);
+      v = ov;
+      i = oi;
+    } else {
+      v2 = fminf(v2, ov);
+    }
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    s.fslot1[parity * NW + wave] = v;
+    s.fslot2[parity * NW + wave] = v2;
+    s.islot[parity * NW + wave] = i;
+  }
+  __syncthreads();
+  b1 = s.fslot1[parity * NW];
+  bi = s.islot[parity * NW];
+  b2 = s.fslot2[parity * NW];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    const float ov = s.fslot1[parity * NW + w];
+    const int oi = s.islot[parity * NW + w];
+    const float ov2 = s.fslot2[parity * NW + w];
+    if (fbetter(ov, oi, b1, bi)) {
+      b2 = fminf(ov2, b1);
+      b1 = ov;
+      bi = oi;
+    } else {
+      b2 = fminf(b2, ov);
+    }
+  }
+  parity ^= 1;
+}
+
+// Matrix-core fragment of k-step `ks` for row `r` (see the score kernel for
+// the lane layout: bf16 32x32x16 takes dims 16 ks + 8 (lane / 32) + [0, 8),
+// fp32 32x32x2 takes dim 2 ks + lane / 32).
+template <int DT>
+struct GramMma;
+
+template <>
+struct GramMma<BKV_BF16> {
+  template <int D>
+  static constexpr int steps() { return D / 16; }
+  __device__ static inline fps_bf16x8 frag(const unsigned char* row, int ks, int lane) {
+    uint4 w = *reinterpret_cast<const uint4*>(row + (size_t)(16 * ks + 8 * (lane >> 5)) * 2);
+    return __builtin_bit_cast(fps_bf16x8, w);
+  }
+  __device__ static inline fps_floatx16 mma(fps_bf16x8 a, fps_bf16x8 b, fps_floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct GramMma<BKV_F32> {
+  template <int D>
+  static constexpr int steps() { return D / 2; }
+  __device__ static inline float frag(const unsigned char* row, int ks, int lane) {
+    return *reinterpret_cast<const float*>(row + (size_t)(2 * ks + (lane >> 5)) * 4);
+  }
+  __device__ static inline fps_floatx16 mma(float a, float b, fps_floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Plain binary64 FPS over rows [0, c) (used when norms leave the fp32-safe
+// range).  Thread i owns candidate i; cosines are recomputed from the rows
+// for every pick.
+template <int DT, int D, int NW>
+__device__ int fps_exact(const FpsSmem& s, int c, int kk) {
+  using F = Fps<DT, D, NW>;
+  const int tid = threadIdx.x;
+  const double inf = __builtin_huge_val();
+  int parity = 0;
+  // mean cosines
+  double bv = inf;
+  if (tid < c) {
+    double acc = 0.0;
+    for (int j = 0; j < c; ++j) {
+      double dd = 0.0;
+      for (int q = 0; q < F::kP; ++q) dd += dot_slice64<DT, D, NW>(s, tid, j, q);
+      acc += dd * s.inv64[tid] * s.inv64[j];
+    }
+    bv = acc / (double)c;
+  }
+  int pick = block_argmin64<NW>(bv, tid < c ? tid : 0x7fffffff, s, parity);
+  if (tid == 0) s.picks[0] = pick;
+  double m = inf;
+  bool picked = tid == pick;
+  for (int t = 1; t < kk; ++t) {
+    if (tid < c && !picked) {
+      double dd = 0.0;
+      for (int q = 0; q < F::kP; ++q) dd += dot_slice64<DT, D, NW>(s, tid, pick, q);
+      const double cv = dd * s.inv64[tid] * s.inv64[pick];
+      m = (t == 1) ? cv : fmax(m, cv);
+    }
+    const bool cand = tid < c && !picked;
+    pick = block_argmin64<NW>(cand ? m : inf, cand ? tid : 0x7fffffff, s, parity);
+    if (tid == pick) picked = true;
+    if (tid == 0) s.picks[t] = pick;
+  }
+  __syncthreads();
+  return kk;
+}
+
+// FPS over LDS rows [0, c), c <= 32 NW: writes min(k, c) picks to s.picks
+// and returns the count.  Every thread of the block must call it; all 32 NW
+// LDS rows must be readable.
+template <int DT, int D, int NW>
 __device__ int fps_core(const FpsSmem& s, int c, int k) {
-  using Lay = FpsLayout<DT, D>;
+  using F = Fps<DT, D, NW>;
   using E = Elem<DT>;
-  constexpr int P = Lay::kP;
-  constexpr int NG = Lay::kGroups;
-  constexpr int KO = Lay::kMaxOwn;
+  using MM = GramMma<DT>;
+  constexpr int KS = MM::template steps<D>();
   const int kk = k < c ? k : c;
   if (kk <= 0) return 0;
   const int tid = threadIdx.x;
-  const int p = tid % P;
-  const int cg = tid / P;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const bool own = tid < c;
   const double inf = __builtin_huge_val();
+  const float finf = __builtin_huge_valf();
 
-  // 1. inverse norms of the owned candidates (norm clamped at 1e-12)
-  double inv_n[KO];
-  double m[KO];
-  double x[32];
+  // 1. binary64 norms (clamped at 1e-12) and the fp32-safety check
+  int unsafe = 0;
+  if (own) {
+    const typename E::T* x = fps_row<DT, D, NW>(s, tid);
+    double ss = 0.0;
+#pragma unroll 8
+    for (int t = 0; t < D; ++t) {
+      const double v = E::to_f64(x[t]);
+      ss = fma(v, v, ss);
+    }
+    const double n = sqrt(ss);
+    unsafe = (n > 0.0 && (n < 1e-15 || n > 1e18)) ? 1 : 0;
+    const double inv = 1.0 / (n < 1e-12 ? 1e-12 : n);
+    s.inv64[tid] = inv;
+    s.inv32[tid] = (float)inv;
+  }
+  if (__syncthreads_or(unsafe)) return fps_exact<DT, D, NW>(s, c, kk);
+
+  // 2. Gram rows of this wave's tile on the matrix cores.  Every wave
+  // multiplies every tile of the 32 NW LDS rows (rows at or beyond c hold
+  // unused values): the MFMA chain is branch-free, so the compiler's
+  // accumulator-read wait states cover every path to the reads below.
+  const int rt = (c + 31) >> 5;
+  fps_floatx16 acc[NW];
+  {
+    const unsigned char* arow = s.rows + (size_t)(32 * wave + (lane & 31)) * F::kRowStride;
 #pragma unroll
-  for (int o = 0; o < KO; ++o) {
-    const int i = cg + o * NG;
-    inv_n[o] = 0.0;
-    m[o] = inf;
-    if (i < c) {
-      load_slice<DT, D>(s, i, p, x);
-      double ss = 0.0;
+    for (int t = 0; t < NW; ++t) {
+      const unsigned char* brow = s.rows + (size_t)(32 * t + (lane & 31)) * F::kRowStride;
+      acc[t] = fps_floatx16{};
 #pragma unroll
-      for (int t = 0; t < 32; ++t) ss = fma(x[t], x[t], ss);
-      ss = sum_over_p<P>(ss);
-      double n = sqrt(ss);
-      if (n < 1e-12) n = 1e-12;
-      inv_n[o] = 1.0 / n;
-      if (p == 0) s.inv_n[i] = inv_n[o];
+      for (int ks = 0; ks < KS; ++ks) acc[t] = MM::mma(MM::frag(arow, ks, lane), MM::frag(brow, ks, lane), acc[t]);
     }
   }
-  __syncthreads();
 
-  // 2. sum of the normalised rows, svec = sum_i x_i / |x_i|
+  // 3. start: lowest mean cosine, in binary64
   {
-    constexpr int kParts = kFpsThreads / D;
     const int dim = tid % D;
+    constexpr int kParts = F::NT / D > 0 ? F::NT / D : 1;
     const int part = tid / D;
-    const typename E::T* col = nullptr;
-    double acc = 0.0;
-    for (int i = part; i < c; i += kParts) {
-      col = reinterpret_cast<const typename E::T*>(s.rows + (size_t)i * Lay::kRowStride);
-      acc = fma(E::to_f64(col[dim]), s.inv_n[i], acc);
-    }
-    s.part[tid] = acc;
+    double a = 0.0;
+    if (part < kParts)
+      for (int i = part; i < c; i += kParts) a = fma(E::to_f64(fps_row<DT, D, NW>(s, i)[dim]), s.inv64[i], a);
+    s.part[tid] = a;
     __syncthreads();
     if (tid < D) {
       double v = 0.0;
@@ -200,72 +356,97 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
     }
     __syncthreads();
   }
-
-  // 3. start: lowest mean cosine, mu_i = (x_i . svec) / (|x_i| c)
-  int parity = 0;
-  int start;
+  int parity = 0;  // one toggle for every block reduction: consecutive reductions use different slots
+  int pick;
   {
-    double sv[32];
-#pragma unroll
-    for (int t = 0; t < 32; ++t) sv[t] = s.svec[p * 32 + t];
-    double bv = inf;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int o = 0; o < KO; ++o) {
-      const int i = cg + o * NG;
-      if (i < c) {
-        load_slice<DT, D>(s, i, p, x);
-        double dd = 0.0;
-#pragma unroll
-        for (int t = 0; t < 32; ++t) dd = fma(x[t], sv[t], dd);
-        dd = sum_over_p<P>(dd);
-        const double mu = dd * inv_n[o] / (double)c;
-        if (better(mu, i, bv, bi)) {
-          bv = mu;
-          bi = i;
-        }
-      }
+    double mu = inf;
+    if (own) {
+      const typename E::T* x = fps_row<DT, D, NW>(s, tid);
+      double a = 0.0;
+#pragma unroll 8
+      for (int t = 0; t < D; ++t) a = fma(E::to_f64(x[t]), s.svec[t], a);
+      mu = a * s.inv64[tid] / (double)c;
     }
-    start = block_argmin<P>(bv, bi, s, parity);
-    parity ^= 1;
+    pick = block_argmin64<NW>(mu, own ? tid : 0x7fffffff, s, parity);
   }
-  if (tid == 0) s.picks[0] = start;
+  if (tid == 0) s.picks[0] = pick;
 
-  // 4. greedy rounds; round 0 initialises m with the cosines to the start
-  int pick = start;
-  for (int t = 0; t < kk; ++t) {
-    double xp[32];
-    load_slice<DT, D>(s, pick, p, xp);
-    const double inv_p = s.inv_n[pick];
-    double bv = inf;
-    int bi = 0x7fffffff;
+  // 4. greedy rounds on fp32 cosines with the certified window
+  const float eps2 = 2.0f * F::kEps;
+  float mt = finf;        // max fp32 cosine of this candidate to the picked set
+  bool picked = tid == pick;
+  const float inv_me = own ? s.inv32[tid] : 0.0f;
+  for (int t = 1; t < kk; ++t) {
+    // publish Gram row `pick`
+    {
+      const int pw = pick >> 5, m = pick & 31;
+      const int half = (m & 7) >> 2;
+      const int rr = ((m >> 3) << 2) | (m & 3);
+      if (wave == pw && (lane >> 5) == half) {
 #pragma unroll
-    for (int o = 0; o < KO; ++o) {
-      const int i = cg + o * NG;
-      if (i < c) {
-        load_slice<DT, D>(s, i, p, x);
-        double dd = 0.0;
+        for (int tt = 0; tt < NW; ++tt) {
+          if (tt < rt) {
+            float v = acc[tt][0];
 #pragma unroll
-        for (int q = 0; q < 32; ++q) dd = fma(x[q], xp[q], dd);
-        dd = sum_over_p<P>(dd);
-        const double cosv = dd * inv_n[o] * inv_p;
-        if (i == pick) {
-          m[o] = inf;  // picked rows leave the candidate set for good
-        } else if (t == 0) {
-          m[o] = cosv;
-        } else if (m[o] != inf && cosv > m[o]) {
-          m[o] = cosv;
-        }
-        if (better(m[o], i, bv, bi)) {
-          bv = m[o];
-          bi = i;
+            for (int q = 1; q < 16; ++q) v = (q == rr) ? acc[tt][q] : v;
+            s.rowbuf[32 * tt + (lane & 31)] = v;
+          }
         }
       }
     }
-    if (t + 1 == kk) break;
-    pick = block_argmin<P>(bv, bi, s, parity);
-    parity ^= 1;
-    if (tid == 0) s.picks[t + 1] = pick;
+    __syncthreads();
+    const bool cand = own && !picked;
+    if (cand) {
+      const float cv = s.rowbuf[tid] * inv_me * s.inv32[pick];
+      mt = (t == 1) ? cv : fmaxf(mt, cv);
+    }
+    float b1, b2;
+    int bi;
+    block_best2<NW>(cand ? mt : finf, cand ? tid : 0x7fffffff, s, parity, b1, bi, b2);
+    if (b2 <= b1 + eps2) {
+      // uncertain round: binary64 max cosines of every candidate in the window
+      const int inwin = (cand && mt <= b1 + eps2) ? 1 : 0;
+      int nu;
+      const int pos = block_exclusive_scan(inwin, s.misc + 0, &nu);  // misc used as scan scratch (<= 8 waves)
+      if (inwin) {
+        s.ulist[pos] = tid;
+        s.mexact[pos] = -inf;
+      }
+      __syncthreads();
+      const int ns = t;  // picks[0 .. t)
+      const int total = nu * ns;
+      const int q = tid % F::kP;
+      const int g = tid / F::kP;
+      for (int base = 0; base < total; base += F::kGroups) {
+        const int pr = base + g;
+        double cv = -inf;
+        int uu = -1;
+        if (pr < total) {
+          uu = pr / ns;
+          const int a = s.ulist[uu], b = s.picks[pr % ns];
+          cv = dot_slice64<DT, D, NW>(s, a, b, q);
+        }
+        cv = sum_lanes<F::kP>(cv);
+        if (pr < total) cv = cv * s.inv64[s.ulist[uu]] * s.inv64[s.picks[pr % ns]];
+        if (q == 0) {
+          s.pairv[g] = cv;
+          s.pairu[g] = uu;
+        }
+        __syncthreads();
+        if (tid < nu) {
+          double mx = s.mexact[tid];
+          for (int j = 0; j < F::kGroups; ++j)
+            if (s.pairu[j] == tid) mx = fmax(mx, s.pairv[j]);
+          s.mexact[tid] = mx;
+        }
+        __syncthreads();
+      }
+      const bool in = tid < nu;
+      bi = block_argmin64<NW>(in ? s.mexact[tid] : inf, in ? s.ulist[tid] : 0x7fffffff, s, parity);
+    }
+    pick = bi;
+    if (tid == pick) picked = true;
+    if (tid == 0) s.picks[t] = pick;
   }
   __syncthreads();
   return kk;
@@ -275,13 +456,15 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
 // Ingest
 // ---------------------------------------------------------------------------
 
-template <int DT, int D>
-__global__ __launch_bounds__(kFpsThreads) void fps_update_kernel(const typename Elem<DT>::T* __restrict__ q_new,
-                                                                 int T, typename Elem<DT>::T* __restrict__ qbuf,
-                                                                 int32_t* __restrict__ qcount, int C, int M,
-                                                                 int32_t* __restrict__ ws_words) {
-  using Lay = FpsLayout<DT, D>;
-  using ET = typename Elem<DT>::T;
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void fps_update_kernel(const typename Elem<DT>::T* __restrict__ q_new, int T,
+                                                             typename Elem<DT>::T* __restrict__ qbuf,
+                                                             int32_t* __restrict__ qcount, int C, int M,
+                                                             int32_t* __restrict__ ws_words) {
+  using F = Fps<DT, D, NW>;
+  using ET = typename F::ET;
+  constexpr int NT = F::NT;
+  constexpr int kU = F::kU;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
   const int tid = threadIdx.x;
@@ -293,16 +476,16 @@ __global__ __launch_bounds__(kFpsThreads) void fps_update_kernel(const typename 
     return;
   }
   if (c0 + T < C) {  // no shrink in this call: plain append
-    copy16(buf + (size_t)c0 * D, qn, T * Lay::kRowBytes, tid, kFpsThreads);
+    copy16(buf + (size_t)c0 * D, qn, T * F::kRowBytes, tid, NT);
     if (tid == 0) qcount[head] = c0 + T;
     return;
   }
-  FpsSmem s = carve<DT, D>(smem, C + M);
-  constexpr int kU = Lay::kRowBytes / 16;  // 16-byte units per row
+  constexpr int cpad = F::kMaxRows;  // rows [C, cpad) are readable padding, [cpad, cpad + M) the reorder area
+  FpsSmem s = fps_carve<DT, D, NW>(smem, cpad + M);
   auto load_rows = [&](int dst_row, const ET* src, int nrows) {
-    for (int u = tid; u < nrows * kU; u += kFpsThreads) {
+    for (int u = tid; u < nrows * kU; u += NT) {
       const int r = u / kU, q = u % kU;
-      reinterpret_cast<uint4*>(s.rows + (size_t)(dst_row + r) * Lay::kRowStride)[q] =
+      reinterpret_cast<uint4*>(s.rows + (size_t)(dst_row + r) * F::kRowStride)[q] =
           reinterpret_cast<const uint4*>(src + (size_t)r * D)[q];
     }
   };
@@ -316,27 +499,26 @@ __global__ __launch_bounds__(kFpsThreads) void fps_update_kernel(const typename 
     t += take;
     __syncthreads();
     if (c == C) {
-      const int n = fps_core<DT, D>(s, C, M);
-      // gather the picks, in pick order, through the spare rows [C, C+M)
-      for (int u = tid; u < n * kU; u += kFpsThreads) {
+      const int n = fps_core<DT, D, NW>(s, C, M);
+      for (int u = tid; u < n * kU; u += NT) {
         const int r = u / kU, q = u % kU;
-        reinterpret_cast<uint4*>(s.rows + (size_t)(C + r) * Lay::kRowStride)[q] =
-            reinterpret_cast<const uint4*>(s.rows + (size_t)s.picks[r] * Lay::kRowStride)[q];
+        reinterpret_cast<uint4*>(s.rows + (size_t)(cpad + r) * F::kRowStride)[q] =
+            reinterpret_cast<const uint4*>(s.rows + (size_t)s.picks[r] * F::kRowStride)[q];
       }
       __syncthreads();
-      for (int u = tid; u < n * kU; u += kFpsThreads) {
+      for (int u = tid; u < n * kU; u += NT) {
         const int r = u / kU, q = u % kU;
-        reinterpret_cast<uint4*>(s.rows + (size_t)r * Lay::kRowStride)[q] =
-            reinterpret_cast<const uint4*>(s.rows + (size_t)(C + r) * Lay::kRowStride)[q];
+        reinterpret_cast<uint4*>(s.rows + (size_t)r * F::kRowStride)[q] =
+            reinterpret_cast<const uint4*>(s.rows + (size_t)(cpad + r) * F::kRowStride)[q];
       }
       __syncthreads();
       c = n;
     }
   }
-  for (int u = tid; u < c * kU; u += kFpsThreads) {
+  for (int u = tid; u < c * kU; u += NT) {
     const int r = u / kU, q = u % kU;
     reinterpret_cast<uint4*>(buf + (size_t)r * D)[q] =
-        reinterpret_cast<const uint4*>(s.rows + (size_t)r * Lay::kRowStride)[q];
+        reinterpret_cast<const uint4*>(s.rows + (size_t)r * F::kRowStride)[q];
   }
   if (tid == 0) qcount[head] = c;
 }
@@ -386,14 +568,15 @@ __device__ inline void rotate_store(const typename Elem<DT>::T* x, float2 cs, in
   y[i + H] = E::from_f64(x1 * c + x0 * s);
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(kFpsThreads) void obs_build_kernel(
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void obs_build_kernel(
     const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
     const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid,
     int Hq, int Hkv, int RP, int32_t* __restrict__ ws_words) {
-  using Lay = FpsLayout<DT, D>;
-  using ET = typename Elem<DT>::T;
+  using F = Fps<DT, D, NW>;
+  using ET = typename F::ET;
+  constexpr int NT = F::NT;
   constexpr int H = D / 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
@@ -410,7 +593,7 @@ __global__ __launch_bounds__(kFpsThreads) void obs_build_kernel(
   const float2* tab_n = tab + (size_t)n * (R + 1) * H;
 
   // recent queries at their own positions
-  for (int e = tid; e < R * H; e += kFpsThreads) {
+  for (int e = tid; e < R * H; e += NT) {
     const int r = e / H, i = e % H;
     ET* y = obs_u + (size_t)(rowbase + r) * D;
     if (recent_pos[(size_t)n * R + r] >= 0) {
@@ -429,25 +612,24 @@ __global__ __launch_bounds__(kFpsThreads) void obs_build_kernel(
     c = 0;
   }
   const int want = nb < c ? nb : c;
-  FpsSmem s = carve<DT, D>(smem, C);
+  constexpr int cpad = F::kMaxRows;
+  FpsSmem s = fps_carve<DT, D, NW>(smem, cpad);
   int kk = 0;
   if (want > 0) {
     const ET* buf = qbuf + (size_t)head * C * D;
-    constexpr int kU = Lay::kRowBytes / 16;
-    for (int u = tid; u < c * kU; u += kFpsThreads) {
-      const int r = u / kU, q = u % kU;
-      reinterpret_cast<uint4*>(s.rows + (size_t)r * Lay::kRowStride)[q] =
+    for (int u = tid; u < c * F::kU; u += NT) {
+      const int r = u / F::kU, q = u % F::kU;
+      reinterpret_cast<uint4*>(s.rows + (size_t)r * F::kRowStride)[q] =
           reinterpret_cast<const uint4*>(buf + (size_t)r * D)[q];
     }
     __syncthreads();
-    kk = fps_core<DT, D>(s, c, want);
+    kk = fps_core<DT, D, NW>(s, c, want);
   }
-  for (int e = tid; e < nb * H; e += kFpsThreads) {
+  for (int e = tid; e < nb * H; e += NT) {
     const int b = e / H, i = e % H;
     ET* y = obs_u + (size_t)(rowbase + R + b) * D;
     if (b < kk) {
-      const ET* x = reinterpret_cast<const ET*>(s.rows + (size_t)s.picks[b] * Lay::kRowStride);
-      rotate_store<DT, D>(x, tab_n[R * H + i], i, y);
+      rotate_store<DT, D>(fps_row<DT, D, NW>(s, s.picks[b]), tab_n[R * H + i], i, y);
     } else {
       y[i] = ET(0);
       y[i + H] = ET(0);
@@ -458,25 +640,49 @@ __global__ __launch_bounds__(kFpsThreads) void obs_build_kernel(
   // padding rows of the unit (written once, by the last query head of the group)
   if (gl == G - 1) {
     const int first = G * (R + nb);
-    for (int e = tid; e < (RP - first) * D; e += kFpsThreads) obs_u[(size_t)first * D + e] = ET(0);
-    for (int r = first + tid; r < RP; r += kFpsThreads) val_u[r] = 0;
+    for (int e = tid; e < (RP - first) * D; e += NT) obs_u[(size_t)first * D + e] = ET(0);
+    for (int r = first + tid; r < RP; r += NT) val_u[r] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launchers
+// Host-side launchers (block size from the capacity: 32 rows per wave)
 // ---------------------------------------------------------------------------
+
+template <int DT, int D, int NW>
+static hipError_t launch_fps_update_nw(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M, int heads,
+                                       int32_t* ws_words, hipStream_t st) {
+  using ET = typename Elem<DT>::T;
+  const int cpad = Fps<DT, D, NW>::kMaxRows;
+  const size_t smem = fps_smem_bytes<DT, D, NW>(cpad + M);
+  auto kern = fps_update_kernel<DT, D, NW>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(heads), dim3(64 * NW), smem, st, (const ET*)q_new, T, (ET*)qbuf, qcount, C, M,
+                     ws_words);
+  return hipGetLastError();
+}
 
 template <int DT, int D>
 hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M, int heads,
                              int32_t* ws_words, hipStream_t st) {
+  if (C <= 64) return launch_fps_update_nw<DT, D, 2>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+  if (C <= 128) return launch_fps_update_nw<DT, D, 4>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+  return launch_fps_update_nw<DT, D, 8>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+}
+
+template <int DT, int D, int NW>
+static hipError_t launch_obs_nw(const void* qbuf, const int32_t* qcount, int C, int nb, const void* recent,
+                                const int32_t* recent_pos, int R, float2* tab, void* obs, int32_t* obs_valid, int N,
+                                int Hq, int Hkv, int RP, int32_t* ws_words, hipStream_t st) {
   using ET = typename Elem<DT>::T;
-  const size_t smem = fps_smem_bytes<DT, D>(C + M);
-  auto kern = fps_update_kernel<DT, D>;
+  const int cpad = Fps<DT, D, NW>::kMaxRows;
+  const size_t smem = fps_smem_bytes<DT, D, NW>(cpad);
+  auto kern = obs_build_kernel<DT, D, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(heads), dim3(kFpsThreads), smem, st, (const ET*)q_new, T, (ET*)qbuf, qcount, C, M,
-                     ws_words);
+  hipLaunchKernelGGL(kern, dim3(N * Hq), dim3(64 * NW), smem, st, (const ET*)qbuf, qcount, C, nb, (const ET*)recent,
+                     recent_pos, R, (const float2*)tab, (ET*)obs, obs_valid, Hq, Hkv, RP, ws_words);
   return hipGetLastError();
 }
 
@@ -485,18 +691,17 @@ hipError_t launch_obs_build(const void* qbuf, const int32_t* qcount, int C, int 
                             const int32_t* recent_pos, int R, const int32_t* pos_now, double theta, float2* tab,
                             void* obs, int32_t* obs_valid, int N, int Hq, int Hkv, int RP, int32_t* ws_words,
                             hipStream_t st) {
-  using ET = typename Elem<DT>::T;
   hipLaunchKernelGGL(rope_table_kernel<D>, dim3(N), dim3(256), 0, st, recent_pos, pos_now, R, theta, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t smem = fps_smem_bytes<DT, D>(C);
-  auto kern = obs_build_kernel<DT, D>;
-  e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(N * Hq), dim3(kFpsThreads), smem, st, (const ET*)qbuf, qcount, C, nb,
-                     (const ET*)recent, recent_pos, R, (const float2*)tab, (ET*)obs, obs_valid, Hq, Hkv, RP,
-                     ws_words);
-  return hipGetLastError();
+  if (C <= 64)
+    return launch_obs_nw<DT, D, 2>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
+                                   ws_words, st);
+  if (C <= 128)
+    return launch_obs_nw<DT, D, 4>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
+                                   ws_words, st);
+  return launch_obs_nw<DT, D, 8>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
+                                 ws_words, st);
 }
 
 template hipError_t launch_fps_update<BKV_F32, 64>(const void*, int, void*, int32_t*, int, int, int, int32_t*,

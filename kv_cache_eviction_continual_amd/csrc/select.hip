@@ -14,13 +14,12 @@
 // how many entries equal to tau are taken.  One more pass marks the kept
 // entries in index order (block prefix sums) and writes them ascending.
 //
-// compact_kernel: one wave per (slot, KV head, tensor).  Row i <- row
+// compact_kernel: one workgroup per (slot, KV head, tensor).  Row i <- row
 // kept[i] for i from the first evicted index up to the kept count.  Because
 // kept is ascending, kept[i] >= i: a row is only ever read by a destination
-// at or before its own index, never after it has been overwritten.  The wave
-// moves 32 rows per step; each step issues the loads of the next group,
-// waits for every outstanding memory operation, and only then stores, so no
-// row is written before every read of it has returned.
+// at or before its own index.  Rows move in steps of increasing index; a
+// block-wide barrier after each step's loads have returned orders every read
+// of a row before its overwrite.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -138,56 +137,64 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
 
 // ---------------------------------------------------------------------------
 
-constexpr int kCompactUnroll = 8;  // row-slices per lane per step
+constexpr int kCompactThreads = 256;
+constexpr int kCompactUnroll = 2;  // row groups per thread per step (more in flight measured slower)
 
-__global__ __launch_bounds__(64) void compact_kernel(unsigned char* __restrict__ K, unsigned char* __restrict__ V,
-                                                     const int32_t* __restrict__ kept,
-                                                     const int32_t* __restrict__ sel, int32_t* __restrict__ len,
-                                                     int Hkv, int Lmax, int B, int row_bytes,
-                                                     unsigned long long* __restrict__ rows_moved) {
+// One workgroup per (slot, KV head, tensor).  A step moves kCompactUnroll
+// groups of (256 / lanes per row) rows: every thread first waits for its own
+// loads and stores, the block synchronises, then the loads of the next step
+// are issued (they read rows at or beyond the next step's first index, which
+// this step's stores never touch) followed by this step's stores (whose rows
+// are read only by destinations at or before them, all loaded already).
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(unsigned char* __restrict__ K,
+                                                                  unsigned char* __restrict__ V,
+                                                                  const int32_t* __restrict__ kept,
+                                                                  const int32_t* __restrict__ sel,
+                                                                  int32_t* __restrict__ len, int Hkv, int Lmax, int B,
+                                                                  int row_bytes,
+                                                                  unsigned long long* __restrict__ rows_moved) {
   const size_t unit = blockIdx.x >> 1;
   const int tensor = blockIdx.x & 1;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int f = sel[2 * unit];
   const int cnt = sel[2 * unit + 1];
   if (cnt < 0) return;  // unit rejected by the selection
   const int n = (int)(unit / Hkv);
-  if (lane == 0) {
-    if (tensor == 0 && unit % Hkv == 0) len[n] = cnt;  // no compaction wave reads len
+  if (tid == 0) {
+    if (tensor == 0 && unit % Hkv == 0) len[n] = cnt;  // no compaction block reads len
     if (cnt > f) atomicAdd(rows_moved, (unsigned long long)(cnt - f));
   }
   if (cnt <= f) return;
   unsigned char* base = (tensor ? V : K) + unit * (size_t)Lmax * row_bytes;
   const int32_t* kept_u = kept + unit * (size_t)B;
   const int lanes_per_row = row_bytes / 16;
-  const int rows_per_slice = 64 / lanes_per_row;
-  const int col = (lane % lanes_per_row) * 16;
-  const int sub = lane / lanes_per_row;
-  const int rows_per_step = rows_per_slice * kCompactUnroll;
+  const int rows_per_group = kCompactThreads / lanes_per_row;
+  const int col = (tid % lanes_per_row) * 16;
+  const int sub = tid / lanes_per_row;
+  const int rows_per_step = rows_per_group * kCompactUnroll;
 
   uint4 cur[kCompactUnroll], nxt[kCompactUnroll];
-  auto load_group = [&](int i0, uint4 (&dst)[kCompactUnroll]) {
 #pragma unroll
-    for (int k = 0; k < kCompactUnroll; ++k) {
-      const int i = i0 + k * rows_per_slice + sub;
-      if (i < cnt) dst[k] = *reinterpret_cast<const uint4*>(base + (size_t)kept_u[i] * row_bytes + col);
-    }
-  };
-  auto store_group = [&](int i0, const uint4 (&src)[kCompactUnroll]) {
-#pragma unroll
-    for (int k = 0; k < kCompactUnroll; ++k) {
-      const int i = i0 + k * rows_per_slice + sub;
-      if (i < cnt) *reinterpret_cast<uint4*>(base + (size_t)i * row_bytes + col) = src[k];
-    }
-  };
-  load_group(f, cur);
+  for (int k = 0; k < kCompactUnroll; ++k) {
+    const int i = f + k * rows_per_group + sub;
+    if (i < cnt) cur[k] = *reinterpret_cast<const uint4*>(base + (size_t)kept_u[i] * row_bytes + col);
+  }
   for (int i0 = f; i0 < cnt; i0 += rows_per_step) {
-    // every load issued so far (this group) and every store of the previous
-    // group has completed before any store of this group is issued
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     const int nx = i0 + rows_per_step;
-    if (nx < cnt) load_group(nx, nxt);  // reads rows >= nx only, untouched by this group's stores
-    store_group(i0, cur);
+    if (nx < cnt) {
+#pragma unroll
+      for (int k = 0; k < kCompactUnroll; ++k) {
+        const int i = nx + k * rows_per_group + sub;
+        if (i < cnt) nxt[k] = *reinterpret_cast<const uint4*>(base + (size_t)kept_u[i] * row_bytes + col);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kCompactUnroll; ++k) {
+      const int i = i0 + k * rows_per_group + sub;
+      if (i < cnt) *reinterpret_cast<uint4*>(base + (size_t)i * row_bytes + col) = cur[k];
+    }
 #pragma unroll
     for (int k = 0; k < kCompactUnroll; ++k) cur[k] = nxt[k];
   }
@@ -202,7 +209,7 @@ hipError_t launch_select(const float* scores, const int32_t* len, int N, int Hkv
 
 hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* sel, int32_t* len, int N, int Hkv,
                           int Lmax, int B, int row_bytes, unsigned long long* rows_moved, hipStream_t st) {
-  hipLaunchKernelGGL(compact_kernel, dim3(N * Hkv * 2), dim3(64), 0, st, (unsigned char*)K, (unsigned char*)V, kept,
+  hipLaunchKernelGGL(compact_kernel, dim3(N * Hkv * 2), dim3(kCompactThreads), 0, st, (unsigned char*)K, (unsigned char*)V, kept,
                      sel, len, Hkv, Lmax, B, row_bytes, rows_moved);
   return hipGetLastError();
 }

@@ -53,6 +53,8 @@ def lib():
         L.orc_bf16_from_double.restype = ctypes.c_uint16
         L.orc_fps.argtypes = [P, I, I, I, P]
         L.orc_fps.restype = I
+        L.orc_fps_objectives.argtypes = [P, I, I, P, I, P]
+        L.orc_fps_objectives.restype = None
         L.orc_fps_stored.argtypes = [P, I, I, I, I, P]
         L.orc_fps_stored.restype = I
         L.orc_fps_ingest.argtypes = [P, I, I, I, I, P, P, I]
@@ -117,6 +119,34 @@ def fps(X: np.ndarray, k: int) -> np.ndarray:
     picks = np.empty(max(k, 1), dtype=np.int32)
     n = lib().orc_fps(_ptr(X), c, d, k, _ptr(picks))
     return picks[:n].copy()
+
+
+def fps_objectives(X: np.ndarray, prefix) -> np.ndarray:
+    """Per-row FPS objective given the picked prefix: the mean cosine to all
+    rows for an empty prefix, else the maximum cosine to the prefix."""
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    c, d = X.shape
+    pre = np.ascontiguousarray(np.asarray(prefix, dtype=np.int32).reshape(-1))
+    out = np.empty(max(c, 1), dtype=np.float64)
+    lib().orc_fps_objectives(_ptr(X), c, d, _ptr(pre) if pre.size else None, int(pre.size), _ptr(out))
+    return out[:c].copy()
+
+
+def check_fps_sequence(X: np.ndarray, picks, tol: float):
+    """Checks that ``picks`` is a valid FPS run over the rows of X: every pick
+    is an unpicked row whose objective is within ``tol`` of the round's
+    minimum.  Returns the largest excess over the minimum."""
+    picked = np.zeros(X.shape[0], dtype=bool)
+    worst = 0.0
+    for t, p in enumerate(picks):
+        obj = fps_objectives(X, list(picks[:t]))
+        assert not picked[p], "row %d picked twice" % p
+        best = np.min(obj[~picked])
+        excess = obj[p] - best
+        assert excess <= tol, "round %d: pick %d objective %r exceeds the minimum %r" % (t, p, obj[p], best)
+        worst = max(worst, excess)
+        picked[p] = True
+    return worst
 
 
 def fps_stored(buf: np.ndarray, count: int, k: int) -> np.ndarray:

@@ -136,6 +136,7 @@ int orc_fps(const double *X, int c, int d, int k, int *picks) {
       best_mu = mu;
     }
   }
+  if (start < 0) start = 0; /* unreachable for c >= 1; keeps the index provably valid */
   picks[0] = start;
   picked[start] = 1;
   for (int i = 0; i < c; ++i) m[i] = dot(xh + (size_t)i * d, xh + (size_t)start * d, d);
@@ -147,6 +148,7 @@ int orc_fps(const double *X, int c, int d, int k, int *picks) {
       if (picked[i]) continue;
       if (best < 0 || m[i] < m[best]) best = i;
     }
+    if (best < 0) best = 0; /* unreachable: kk <= c leaves an unpicked row */
     picks[t] = best;
     picked[best] = 1;
     for (int i = 0; i < c; ++i) {
@@ -158,6 +160,38 @@ int orc_fps(const double *X, int c, int d, int k, int *picks) {
   free(m);
   free(picked);
   return kk;
+}
+
+/*
+ * orc_fps_objectives: the quantity FPS minimises in a round, for every row of
+ * X[c][d], given the rows already picked (prefix[0..np)).  With an empty
+ * prefix it is the mean cosine to all c rows (the start rule); otherwise the
+ * maximum cosine to the picked rows (the farthest-point rule).  Same
+ * definitions and readings as orc_fps.  It lets a test check that a pick
+ * sequence is a valid FPS run when exact ties make several sequences valid.
+ */
+void orc_fps_objectives(const double *X, int c, int d, const int *prefix, int np, double *out) {
+  double *xh = (double *)malloc(sizeof(double) * (size_t)(c > 0 ? c : 1) * d);
+  for (int i = 0; i < c; ++i) {
+    double n = sqrt(dot(X + (size_t)i * d, X + (size_t)i * d, d));
+    if (n < 1e-12) n = 1e-12;
+    for (int t = 0; t < d; ++t) xh[(size_t)i * d + t] = X[(size_t)i * d + t] / n;
+  }
+  for (int i = 0; i < c; ++i) {
+    if (np == 0) {
+      double sum = 0.0;
+      for (int j = 0; j < c; ++j) sum += dot(xh + (size_t)i * d, xh + (size_t)j * d, d);
+      out[i] = sum / c;
+    } else {
+      double m = -INFINITY;
+      for (int k = 0; k < np; ++k) {
+        double s = dot(xh + (size_t)i * d, xh + (size_t)prefix[k] * d, d);
+        if (s > m) m = s;
+      }
+      out[i] = m;
+    }
+  }
+  free(xh);
 }
 
 /*

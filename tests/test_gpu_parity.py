@@ -232,3 +232,146 @@ def test_select_compact_exact_on_given_scores():
                 first = int(np.argmax(ko != np.arange(w.budget))) if not np.array_equal(ko, np.arange(w.budget)) else w.budget
                 moved += 2 * (w.budget - first)
         assert bkv.ws_rows_moved(ws) == moved
+
+
+def _ingest_and_compare(w, blocks, N):
+    """Feed the given query blocks to both sides; compare buffers after each
+    block, then the rotated beacon rows."""
+    shape = bkv.make_shape(N, w.n_kv_heads, w.n_q_heads, w.head_dim, 64, synth.storage_dtype(w))
+    ws = bkv.alloc_workspace(shape, w.n_recent, w.n_beacons)
+    qbuf = torch.zeros(N, w.n_q_heads, w.capacity, w.head_dim, dtype=synth.storage_dtype(w), device="cuda")
+    qcount = torch.zeros(N, w.n_q_heads, dtype=torch.int32, device="cuda")
+    dt = np.uint16 if w.dtype == "bf16" else np.float32
+    o_qbuf = np.zeros(tuple(qbuf.shape), dtype=dt)
+    o_qcount = np.zeros((N, w.n_q_heads), dtype=np.int32)
+    for b, blk in enumerate(blocks):
+        bkv.bkv_fps_update(shape, blk, blk.shape[2], qbuf, qcount, w.capacity, w.shrink_to, ws)
+        oracle.fps_update(np_storage(blk), o_qbuf, o_qcount, w.shrink_to)
+        torch.cuda.synchronize()
+        compare_buffers(qbuf, qcount, o_qbuf, o_qcount, "after block %d" % b)
+    # beacons of the final buffers, through the scoring entry point
+    K = torch.zeros(N, w.n_kv_heads, 64, w.head_dim, dtype=qbuf.dtype, device="cuda")
+    length = torch.full((N,), 64, dtype=torch.int32, device="cuda")
+    recent = torch.zeros(N, w.n_q_heads, w.n_recent, w.head_dim, dtype=qbuf.dtype, device="cuda")
+    rpos = torch.full((N, w.n_recent), -1, dtype=torch.int32, device="cuda")
+    pos_now = torch.full((N,), 77, dtype=torch.int32, device="cuda")
+    scores = torch.empty(N, w.n_kv_heads, 64, dtype=torch.float32, device="cuda")
+    bkv.bkv_score(shape, K, length, recent, rpos, w.n_recent, qbuf, qcount, w.capacity, w.n_beacons, pos_now,
+                  w.rope_theta, scores, ws)
+    torch.cuda.synchronize()
+    v = bkv.ws_views(shape, w.n_recent, w.n_beacons, ws)
+    obs_g = np_storage(v["obs"])
+    res = oracle.score(np_storage(K), np.full(N, 64), np_storage(recent), rpos.cpu().numpy(), o_qbuf, o_qcount,
+                       w.n_beacons, np.full(N, 77), w.rope_theta)
+    for (n, h), (_, obs_o, valid_o, _) in res.items():
+        assert np.array_equal(obs_g[n, h, :v["rows"]], obs_o), "beacon rows differ at %s" % ((n, h),)
+    assert bkv.bkv_read_device_status(ws) == 0
+
+
+def _sign_vectors(syn, shape, d, nnz=4):
+    """Vectors with `nnz` entries of +-1 and zeros elsewhere: every cosine
+    between two of them is an exact multiple of 1/nnz, in binary64 and in the
+    fp32 Gram alike, so ties are exact on both sides."""
+    N, H, T = shape
+    scores = syn.randn((N, H, T, d), block=7)
+    top = torch.topk(scores, nnz, dim=-1).indices
+    signs = torch.where(syn.randn((N, H, T, nnz), block=8) >= 0, 1.0, -1.0)
+    x = torch.zeros(N, H, T, d, device=scores.device)
+    x.scatter_(-1, top, signs)
+    return x
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_fps_exact_ties_bitwise(cfg):
+    """Streams of a handful of distinct sign vectors: many exact ties, so
+    rounds go through the binary64 tie path and the lowest index must win;
+    all arithmetic is exact, so both sides must agree bit for bit."""
+    w = configs.get(cfg)
+    N = 2
+    syn = synth.Synth(w, n_slots=N, seed=11, device="cuda")
+    base = _sign_vectors(syn, (N, w.n_q_heads, 6), w.head_dim)
+    idx = syn.randint(0, 6, (N, w.n_q_heads, 3 * w.capacity))
+    stream = torch.gather(base, 2, idx.unsqueeze(-1).expand(-1, -1, -1, w.head_dim))
+    stream = synth.to_storage(stream, w.dtype)
+    blocks = [stream[:, :, i:i + 100].contiguous() for i in range(0, stream.shape[2], 100)]
+    _ingest_and_compare(w, blocks, N)
+
+
+def _match_rows(rows, pool):
+    """Indices into `pool` of each row of `rows` (bitwise), taking the lowest
+    unused index among equal rows."""
+    used = np.zeros(pool.shape[0], dtype=bool)
+    out = []
+    for r in rows:
+        hits = np.where(np.all(pool == r, axis=1) & ~used)[0]
+        assert hits.size, "picked row not found in the buffer"
+        used[hits[0]] = True
+        out.append(int(hits[0]))
+    return out
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_fps_duplicates_give_valid_runs(cfg):
+    """Generic vectors with exact duplicates: several pick sequences differ
+    only at ties of a few ulps, so each GPU run (a shrink, then a beacon
+    selection) is checked to pick, every round, a row whose binary64
+    objective is within 1e-12 of the minimum."""
+    w = configs.get(cfg)
+    N = 2
+    syn = synth.Synth(w, n_slots=N, seed=13, device="cuda")
+    base = syn.randn((N, w.n_q_heads, 7, w.head_dim))
+    extra = w.n_beacons + 9
+    idx = syn.randint(0, 7, (N, w.n_q_heads, w.capacity + extra))
+    stream = torch.gather(base, 2, idx.unsqueeze(-1).expand(-1, -1, -1, w.head_dim))
+    stream = synth.to_storage(stream, w.dtype).contiguous()
+    shape = bkv.make_shape(N, w.n_kv_heads, w.n_q_heads, w.head_dim, 64, stream.dtype)
+    ws = bkv.alloc_workspace(shape, w.n_recent, w.n_beacons)
+    qbuf = torch.zeros(N, w.n_q_heads, w.capacity, w.head_dim, dtype=stream.dtype, device="cuda")
+    qcount = torch.zeros(N, w.n_q_heads, dtype=torch.int32, device="cuda")
+    bkv.bkv_fps_update(shape, stream, stream.shape[2], qbuf, qcount, w.capacity, w.shrink_to, ws)
+    # beacons at position 0 are the buffer rows themselves (rotation by angle 0)
+    K = torch.zeros(N, w.n_kv_heads, 64, w.head_dim, dtype=stream.dtype, device="cuda")
+    length = torch.full((N,), 64, dtype=torch.int32, device="cuda")
+    recent = torch.zeros(N, w.n_q_heads, w.n_recent, w.head_dim, dtype=stream.dtype, device="cuda")
+    rpos = torch.full((N, w.n_recent), -1, dtype=torch.int32, device="cuda")
+    pos_now = torch.zeros(N, dtype=torch.int32, device="cuda")
+    scores = torch.empty(N, w.n_kv_heads, 64, dtype=torch.float32, device="cuda")
+    bkv.bkv_score(shape, K, length, recent, rpos, w.n_recent, qbuf, qcount, w.capacity, w.n_beacons, pos_now,
+                  w.rope_theta, scores, ws)
+    torch.cuda.synchronize()
+    st = np_storage(stream)
+    qb = np_storage(qbuf)
+    qc = qcount.cpu().numpy()
+    obs = np_storage(bkv.ws_views(shape, w.n_recent, w.n_beacons, ws)["obs"])
+    G = w.group
+    worst = 0.0
+    for n in range(N):
+        for g in range(w.n_q_heads):
+            assert qc[n, g] == w.shrink_to + extra
+            pre = st[n, g, :w.capacity]             # the full buffer at the shrink
+            picks = _match_rows(qb[n, g, :w.shrink_to], pre)
+            worst = max(worst, oracle.check_fps_sequence(oracle.to_double(pre), picks, 1e-12))
+            assert np.array_equal(qb[n, g, w.shrink_to:qc[n, g]], st[n, g, w.capacity:])
+            live = qb[n, g, :qc[n, g]]
+            h, gl = g // G, g % G
+            row0 = gl * (w.n_recent + w.n_beacons) + w.n_recent
+            bpicks = _match_rows(obs[n, h, row0:row0 + w.n_beacons], live)
+            worst = max(worst, oracle.check_fps_sequence(oracle.to_double(live), bpicks, 1e-12))
+    log("  duplicate streams: worst objective excess %.3g" % worst)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fps_zero_rows_and_extreme_norms(cfg):
+    """Zero vectors (cosine 0 with everything) and rows with norms far outside
+    [1e-15, 1e18] (binary64 path) mixed into an ordinary stream."""
+    w = configs.get(cfg)
+    N = 2
+    syn = synth.Synth(w, n_slots=N, seed=12, device="cuda")
+    z = syn.randn((N, w.n_q_heads, 2 * w.capacity, w.head_dim))
+    u = syn.randint(0, 10, (N, w.n_q_heads, 2 * w.capacity)).unsqueeze(-1)
+    z = torch.where(u == 0, torch.zeros_like(z), z)
+    big = syn.randint(0, 2, (N, 1, 1, 1)).bool()   # slot 0 or 1: whole buffers with some huge rows
+    z = torch.where(big & (u == 1), z * 1e25, z)
+    stream = synth.to_storage(z, w.dtype)
+    blocks = [stream[:, :, i:i + 50].contiguous() for i in range(0, stream.shape[2], 50)]
+    _ingest_and_compare(w, blocks, N)

@@ -235,3 +235,35 @@ def test_count_cycle_of_capacity_128_shrink_16(orc):
         c = orc.fps_ingest(buf, c, q, M)
         seen.append(c)
     assert seen == [16, 32, 48, 64, 80, 96, 112, 16, 32]
+
+
+def test_objectives_match_closed_forms(orc):
+    rng = np.random.default_rng(30)
+    X = rng.normal(size=(20, 7))
+    U = X / np.linalg.norm(X, axis=1, keepdims=True)
+    np.testing.assert_allclose(orc.fps_objectives(X, []), U @ U.mean(axis=0), rtol=0, atol=1e-14)
+    pre = [3, 11, 5]
+    np.testing.assert_allclose(orc.fps_objectives(X, pre), (U @ U[pre].T).max(axis=1), rtol=0, atol=1e-14)
+
+
+def test_fps_picks_are_round_minimisers(orc):
+    rng = np.random.default_rng(31)
+    for _ in range(10):
+        X = rng.normal(size=(30, 6))
+        picks = orc.fps(X, 12)
+        assert orc.check_fps_sequence(X, picks, 0.0) == 0.0
+        picked = []
+        for p in picks:
+            obj = orc.fps_objectives(X, picked)
+            obj[picked] = np.inf
+            assert p == int(np.argmin(obj))
+            picked.append(p)
+
+
+def test_check_fps_sequence_rejects_a_wrong_pick(orc):
+    rng = np.random.default_rng(32)
+    X = rng.normal(size=(15, 5))
+    picks = list(orc.fps(X, 6))
+    bad = picks[:3] + [picks[4], picks[3]] + picks[5:]
+    with pytest.raises(AssertionError):
+        orc.check_fps_sequence(X, bad, 1e-12)
