@@ -36,7 +36,7 @@ from kv_cache_eviction_continual_amd import bkv, configs, synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 CFG = 3
-N_POOL = 4          # distinct 128-step query blocks cycled over the steps
+POOL_MAX = 64       # distinct 128-step query blocks (0.6 GB each) cycled over the steps
 N_EVENTS = 240      # evictions in a 32K-token generation (first at L = 2176)
 
 
@@ -55,16 +55,20 @@ def log(msg):
 class State:
     """Device-resident state of the metric workload."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, n_pool):
         self.w = w
+        self.n_pool = n_pool
         N, Hq, Hkv, d = w.n_slots, w.n_q_heads, w.n_kv_heads, w.head_dim
         self.N = N
         syn = synth.Synth(w, seed=0, device=dev)
         self.syn = syn
-        log("generating K/V %s x 2 and %d query blocks" % ((N, Hkv, w.max_len, d), N_POOL))
+        log("generating K/V %s x 2 and %d query blocks" % ((N, Hkv, w.max_len, d), n_pool))
         self.K = syn.keys()
         self.V = syn.values()
-        self.blocks = [syn.query_block(b) for b in range(N_POOL)]
+        # every decode period brings new queries: block b of the stream is only
+        # re-used after n_pool periods (a re-ingested query would duplicate a
+        # buffered one and turn FPS rounds into exact ties)
+        self.blocks = [syn.query_block(b) for b in range(n_pool)]
         R = w.n_recent
         self.recent = [blk[:, :, -R:].contiguous() for blk in self.blocks]
         self.shape = bkv.make_shape(N, Hkv, Hq, d, w.max_len, self.K.dtype)
@@ -82,14 +86,15 @@ class State:
         rp = pos_now[:, None] - np.arange(R - 1, -1, -1)[None, :]
         self.recent_pos = torch.from_numpy(np.repeat(rp[:, None, :], N, axis=1).astype(np.int32)).to(dev).contiguous()
         # warm the buffers with the first L queries of the stream (17 periods)
-        for b in range(w.warm_steps // w.interval):
-            blk = self.blocks[b % N_POOL]
+        self.n_warm = w.warm_steps // w.interval
+        for b in range(self.n_warm):
+            blk = self.blocks[b % n_pool]
             bkv.bkv_fps_update(self.shape, blk, blk.shape[2], self.qbuf, self.qcount, w.capacity, w.shrink_to, self.ws)
         torch.cuda.synchronize()
 
     def step(self, i, ev=None):
         w = self.w
-        p = i % N_POOL
+        p = (self.n_warm + i) % self.n_pool
         e = i % N_EVENTS
         if ev is not None:
             ev[0].record()
@@ -143,7 +148,7 @@ def cpu_baseline(st: State, budget_s: float = 10.0, min_units: int = 4, max_unit
     done = 0
     t_total = 0.0
     e = 0
-    p = 0
+    p = warm_blocks
     for (n, h) in units_all:
         g0 = h * G
         K_u = synth.to_numpy_storage(st.K_pristine[n, h])
@@ -154,9 +159,9 @@ def cpu_baseline(st: State, budget_s: float = 10.0, min_units: int = 4, max_unit
         qbuf = np.zeros((1, G, w.capacity, w.head_dim), dtype=np.uint16)
         qcount = np.zeros((1, G), dtype=np.int32)
         for b in range(warm_blocks):
-            key = (b % N_POOL, n, h)
+            key = (b, n, h)
             if key not in blocks_np:
-                blocks_np[key] = synth.to_numpy_storage(st.blocks[b % N_POOL][n:n + 1, g0:g0 + G])
+                blocks_np[key] = synth.to_numpy_storage(st.blocks[b][n:n + 1, g0:g0 + G])
             oracle.fps_update(blocks_np[key], qbuf, qcount, w.shrink_to)
         blk = blocks_np.setdefault((p, n, h), synth.to_numpy_storage(st.blocks[p][n:n + 1, g0:g0 + G]))
         recent = synth.to_numpy_storage(st.recent[p][n, g0:g0 + G])
@@ -218,7 +223,7 @@ def main():
     w = configs.get(CFG)
     bkv.load()
 
-    st = State(w, dev)
+    st = State(w, dev, n_pool=min(POOL_MAX, w.warm_steps // w.interval + args.warmup + args.steps))
     if not args.no_cpu_baseline:
         # pristine copies of the cache for the oracle sample, taken before any compaction
         st.K_pristine = st.K.clone()

@@ -52,35 +52,35 @@ struct Fps {
   static constexpr int kRowBytes = D * E::kBytes;
   static constexpr int kRowStride = kRowBytes + 16;
   static constexpr int kU = kRowBytes / 16;   // 16-byte units per row
+  static constexpr int kPer16 = 16 / E::kBytes;
   static constexpr int kP = D / 32;           // lanes per exact dot product (32 dims each)
   static constexpr int kGroups = NT / kP;     // exact dot products per sweep
-  static constexpr float kEps = 4.0f * (D + 8) * 5.9604644775390625e-8f;
+  static constexpr float kU32 = 5.9604644775390625e-8f;  // 2^-24
+  static constexpr float kEps = 4.0f * (D + 8) * kU32;   // bound on |fp32 cosine - cosine|
 };
 
 struct FpsSmem {
   unsigned char* rows;  // row r at rows + r * kRowStride
   double* inv64;        // [kMaxRows] 1 / max(|x|, 1e-12), binary64
   float* inv32;         // [kMaxRows] the same, binary32
-  float* rowbuf;        // [kMaxRows] published Gram row
-  double* svec;         // [D]
-  double* part;         // [NT]
+  float* colx;          // [NW][32] wave-private Gram column
   double* dslot;        // [2][NW] exact argmin values
-  int* islot;           // [2][NW] exact / fp32 argmin indices
+  int* islot;           // [2][NW] argmin indices
   float* fslot1;        // [2][NW] fp32 best values
   float* fslot2;        // [2][NW] fp32 runner-up values
   int* picks;           // [kMaxRows]
-  int* ulist;           // [kMaxRows] candidates of an uncertain round
-  double* mexact;       // [kMaxRows] their binary64 max cosines
+  int* ulist;           // [kMaxRows] candidates inside an uncertain window
+  double* uacc;         // [kMaxRows] their binary64 objectives
   double* pairv;        // [kGroups]
   int* pairu;           // [kGroups]
-  int* misc;            // [16]
+  int* misc;            // [16] block-scan scratch
 };
 
 template <int DT, int D, int NW>
 __host__ __device__ constexpr size_t fps_smem_bytes(int nrows) {
   using F = Fps<DT, D, NW>;
-  return (((size_t)nrows * F::kRowStride + 15) & ~(size_t)15) + F::kMaxRows * (8 + 4 + 4 + 4 + 4 + 8) + D * 8 +
-         F::NT * 8 + 2 * NW * (8 + 4 + 4 + 4) + F::kGroups * (8 + 4) + 64 + 128;
+  return (((size_t)nrows * F::kRowStride + 15) & ~(size_t)15) + F::kMaxRows * (8 + 4 + 4 + 4 + 8) +
+         NW * 32 * 4 + 2 * NW * (8 + 4 + 4 + 4) + F::kGroups * (8 + 4) + 64 + 128;
 }
 
 template <int DT, int D, int NW>
@@ -95,20 +95,18 @@ __device__ inline FpsSmem fps_carve(unsigned char* smem, int nrows) {
     return p;
   };
   s.inv64 = reinterpret_cast<double*>(take(F::kMaxRows * 8));
-  s.mexact = reinterpret_cast<double*>(take(F::kMaxRows * 8));
-  s.svec = reinterpret_cast<double*>(take(D * 8));
-  s.part = reinterpret_cast<double*>(take(F::NT * 8));
+  s.uacc = reinterpret_cast<double*>(take(F::kMaxRows * 8));
   s.dslot = reinterpret_cast<double*>(take(2 * NW * 8));
   s.pairv = reinterpret_cast<double*>(take(F::kGroups * 8));
   s.inv32 = reinterpret_cast<float*>(take(F::kMaxRows * 4));
-  s.rowbuf = reinterpret_cast<float*>(take(F::kMaxRows * 4));
+  s.colx = reinterpret_cast<float*>(take(NW * 32 * 4));
   s.fslot1 = reinterpret_cast<float*>(take(2 * NW * 4));
   s.fslot2 = reinterpret_cast<float*>(take(2 * NW * 4));
   s.islot = reinterpret_cast<int*>(take(2 * NW * 4));
   s.picks = reinterpret_cast<int*>(take(F::kMaxRows * 4));
   s.ulist = reinterpret_cast<int*>(take(F::kMaxRows * 4));
   s.pairu = reinterpret_cast<int*>(take(F::kGroups * 4));
-  s.misc = reinterpret_cast<int*>(take(64));  // block-scan scratch (one int per wave)
+  s.misc = reinterpret_cast<int*>(take(64));
   return s;
 }
 
@@ -120,12 +118,19 @@ __device__ inline const typename Elem<DT>::T* fps_row(const FpsSmem& s, int r) {
 // binary64 dot product of dims [32 q, 32 q + 32) of rows a and b
 template <int DT, int D, int NW>
 __device__ inline double dot_slice64(const FpsSmem& s, int a, int b, int q) {
+  using F = Fps<DT, D, NW>;
   using E = Elem<DT>;
-  const typename E::T* xa = fps_row<DT, D, NW>(s, a) + 32 * q;
-  const typename E::T* xb = fps_row<DT, D, NW>(s, b) + 32 * q;
+  const uint4* xa = reinterpret_cast<const uint4*>(fps_row<DT, D, NW>(s, a) + 32 * q);
+  const uint4* xb = reinterpret_cast<const uint4*>(fps_row<DT, D, NW>(s, b) + 32 * q);
   double acc = 0.0;
-#pragma unroll 8
-  for (int t = 0; t < 32; ++t) acc = fma(E::to_f64(xa[t]), E::to_f64(xb[t]), acc);
+#pragma unroll 1
+  for (int u = 0; u < 32 / F::kPer16; ++u) {
+    const uint4 wa = xa[u], wb = xb[u];
+    const typename E::T* ea = reinterpret_cast<const typename E::T*>(&wa);
+    const typename E::T* eb = reinterpret_cast<const typename E::T*>(&wb);
+#pragma unroll
+    for (int k = 0; k < F::kPer16; ++k) acc = fma(E::to_f64(ea[k]), E::to_f64(eb[k]), acc);
+  }
   return acc;
 }
 
@@ -134,6 +139,21 @@ __device__ inline double sum_lanes(double v) {
 #pragma unroll
   for (int off = 1; off < P; off <<= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// Rotate a value within each 16-lane row of the wave (row_ror DPP).
+template <int N>
+__device__ inline float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sum over the 32 lanes of each half wave (every lane of the half gets a sum).
+__device__ inline float half_wave_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v + __shfl_xor(v, 16, 64);
 }
 
 // Block-wide argmin of (value, index); every thread gets the winning index.
@@ -172,12 +192,12 @@ __device__ inline int block_argmin64(double v, int i, const FpsSmem& s, int& par
 __device__ inline bool fbetter(float v, int i, float bv, int bi) { return v < bv || (v == bv && i < bi); }
 
 // Block-wide (best value, best index, runner-up value) over one fp32 value
-// per thread.
+// per thread; only lanes 0..31 of each wave carry candidates.
 template <int NW>
 __device__ inline void block_best2(float v, int i, const FpsSmem& s, int& parity, float& b1, int& bi, float& b2) {
   float v2 = __builtin_huge_valf();
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
+  for (int off = 1; off < 32; off <<= 1) {
     const float ov = __shfl_xor(v, off, 64);
     const int oi = __shfl_xor(i, off, 64);
     const float ov2 = __shfl_xor(v2, off, 64);
@@ -215,9 +235,8 @@ __device__ inline void block_best2(float v, int i, const FpsSmem& s, int& parity
   parity ^= 1;
 }
 
-// Matrix-core fragment of k-step `ks` for row `r` (see the score kernel for
-// the lane layout: bf16 32x32x16 takes dims 16 ks + 8 (lane / 32) + [0, 8),
-// fp32 32x32x2 takes dim 2 ks + lane / 32).
+// Matrix-core fragment of k-step `ks` for row `r` (bf16 32x32x16 takes dims
+// 16 ks + 8 (lane / 32) + [0, 8); fp32 32x32x2 takes dim 2 ks + lane / 32).
 template <int DT>
 struct GramMma;
 
@@ -246,49 +265,54 @@ struct GramMma<BKV_F32> {
   }
 };
 
-// Plain binary64 FPS over rows [0, c) (used when norms leave the fp32-safe
-// range).  Thread i owns candidate i; cosines are recomputed from the rows
-// for every pick.
+// Binary64 decision among the candidates flagged `inwin` (row `myrow`):
+// objective = mean cosine to all c rows (sum_mode) or maximum cosine to the
+// picks so far (picks[0 .. npicked)).  Returns the row with the lowest
+// objective, ties to the lower row.  Every thread of the block must call it.
+// Wave w evaluates window members w, w + NW, ...; its lanes split the
+// partner rows in groups of kP lanes (32 dimensions each).
 template <int DT, int D, int NW>
-__device__ int fps_exact(const FpsSmem& s, int c, int kk) {
+__device__ int exact_window_argmin(const FpsSmem& s, bool inwin, int myrow, int c, int npicked, bool sum_mode,
+                                   int& parity) {
   using F = Fps<DT, D, NW>;
+  constexpr int kPerWave = 64 / F::kP;  // partner rows per sweep of a wave
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const double inf = __builtin_huge_val();
-  int parity = 0;
-  // mean cosines
-  double bv = inf;
-  if (tid < c) {
-    double acc = 0.0;
-    for (int j = 0; j < c; ++j) {
-      double dd = 0.0;
-      for (int q = 0; q < F::kP; ++q) dd += dot_slice64<DT, D, NW>(s, tid, j, q);
-      acc += dd * s.inv64[tid] * s.inv64[j];
+  int nu;
+  const int pos = block_exclusive_scan(inwin ? 1 : 0, s.misc, &nu);
+  if (inwin) s.ulist[pos] = myrow;
+  __syncthreads();
+  const int npart = sum_mode ? c : npicked;
+  const int q = lane % F::kP;
+  for (int u = wave; u < nu; u += NW) {
+    const int a = s.ulist[u];
+    double acc = sum_mode ? 0.0 : -inf;
+    for (int j0 = 0; j0 < npart; j0 += kPerWave) {
+      const int j = j0 + lane / F::kP;
+      const int b = j < npart ? (sum_mode ? j : s.picks[j]) : a;
+      double v = dot_slice64<DT, D, NW>(s, a, b, q);
+      v = sum_lanes<F::kP>(v) * s.inv64[a] * s.inv64[b];
+      if (j < npart) acc = sum_mode ? acc + v : fmax(acc, v);
     }
-    bv = acc / (double)c;
-  }
-  int pick = block_argmin64<NW>(bv, tid < c ? tid : 0x7fffffff, s, parity);
-  if (tid == 0) s.picks[0] = pick;
-  double m = inf;
-  bool picked = tid == pick;
-  for (int t = 1; t < kk; ++t) {
-    if (tid < c && !picked) {
-      double dd = 0.0;
-      for (int q = 0; q < F::kP; ++q) dd += dot_slice64<DT, D, NW>(s, tid, pick, q);
-      const double cv = dd * s.inv64[tid] * s.inv64[pick];
-      m = (t == 1) ? cv : fmax(m, cv);
+    // combine the partner groups of the wave (lanes 0, kP, 2 kP, ... hold them)
+#pragma unroll
+    for (int off = F::kP; off < 64; off <<= 1) {
+      const double o = __shfl_xor(acc, off, 64);
+      acc = sum_mode ? acc + o : fmax(acc, o);
     }
-    const bool cand = tid < c && !picked;
-    pick = block_argmin64<NW>(cand ? m : inf, cand ? tid : 0x7fffffff, s, parity);
-    if (tid == pick) picked = true;
-    if (tid == 0) s.picks[t] = pick;
+    if (lane == 0) s.uacc[u] = sum_mode ? acc / (double)c : acc;
   }
   __syncthreads();
-  return kk;
+  const bool in = tid < nu;
+  return block_argmin64<NW>(in ? s.uacc[tid] : inf, in ? s.ulist[tid] : 0x7fffffff, s, parity);
 }
 
 // FPS over LDS rows [0, c), c <= 32 NW: writes min(k, c) picks to s.picks
 // and returns the count.  Every thread of the block must call it; all 32 NW
-// LDS rows must be readable.
+// LDS rows must be readable.  Candidate row i is owned by lane i % 32 of wave
+// i / 32, the wave whose MFMA accumulators hold Gram rows [32 w, 32 w + 32).
 template <int DT, int D, int NW>
 __device__ int fps_core(const FpsSmem& s, int c, int k) {
   using F = Fps<DT, D, NW>;
@@ -300,19 +324,23 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool own = tid < c;
-  const double inf = __builtin_huge_val();
   const float finf = __builtin_huge_valf();
+  int parity = 0;  // one toggle for every block reduction: consecutive reductions use different slots
 
   // 1. binary64 norms (clamped at 1e-12) and the fp32-safety check
   int unsafe = 0;
-  if (own) {
-    const typename E::T* x = fps_row<DT, D, NW>(s, tid);
+  if (tid < c) {
+    const uint4* x = reinterpret_cast<const uint4*>(fps_row<DT, D, NW>(s, tid));
     double ss = 0.0;
-#pragma unroll 8
-    for (int t = 0; t < D; ++t) {
-      const double v = E::to_f64(x[t]);
-      ss = fma(v, v, ss);
+#pragma unroll 2
+    for (int u = 0; u < F::kU; ++u) {
+      const uint4 w = x[u];
+      const typename E::T* e = reinterpret_cast<const typename E::T*>(&w);
+#pragma unroll
+      for (int j = 0; j < F::kPer16; ++j) {
+        const double v = E::to_f64(e[j]);
+        ss = fma(v, v, ss);
+      }
     }
     const double n = sqrt(ss);
     unsafe = (n > 0.0 && (n < 1e-15 || n > 1e18)) ? 1 : 0;
@@ -320,13 +348,30 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
     s.inv64[tid] = inv;
     s.inv32[tid] = (float)inv;
   }
-  if (__syncthreads_or(unsafe)) return fps_exact<DT, D, NW>(s, c, kk);
+  const bool unsafe_any = __syncthreads_or(unsafe) != 0;
+
+  // candidate owned by this lane
+  const int myrow = 32 * wave + (lane & 31);
+  const bool owner = lane < 32 && myrow < c;
+
+  if (unsafe_any) {  // plain binary64 rounds over every candidate
+    int pick = exact_window_argmin<DT, D, NW>(s, owner, myrow, c, 0, true, parity);
+    if (tid == 0) s.picks[0] = pick;
+    bool picked = myrow == pick;
+    for (int t = 1; t < kk; ++t) {
+      __syncthreads();  // picks[t - 1] visible
+      pick = exact_window_argmin<DT, D, NW>(s, owner && !picked, myrow, c, t, false, parity);
+      if (myrow == pick) picked = true;
+      if (tid == 0) s.picks[t] = pick;
+    }
+    __syncthreads();
+    return kk;
+  }
 
   // 2. Gram rows of this wave's tile on the matrix cores.  Every wave
   // multiplies every tile of the 32 NW LDS rows (rows at or beyond c hold
   // unused values): the MFMA chain is branch-free, so the compiler's
   // accumulator-read wait states cover every path to the reads below.
-  const int rt = (c + 31) >> 5;
   fps_floatx16 acc[NW];
   {
     const unsigned char* arow = s.rows + (size_t)(32 * wave + (lane & 31)) * F::kRowStride;
@@ -338,114 +383,79 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
       for (int ks = 0; ks < KS; ++ks) acc[t] = MM::mma(MM::frag(arow, ks, lane), MM::frag(brow, ks, lane), acc[t]);
     }
   }
+  float* colx = s.colx + 32 * wave;
+  const int half = lane >> 5;
+  const float inv_me = owner ? s.inv32[myrow] : 0.0f;
 
-  // 3. start: lowest mean cosine, in binary64
-  {
-    const int dim = tid % D;
-    constexpr int kParts = F::NT / D > 0 ? F::NT / D : 1;
-    const int part = tid / D;
-    double a = 0.0;
-    if (part < kParts)
-      for (int i = part; i < c; i += kParts) a = fma(E::to_f64(fps_row<DT, D, NW>(s, i)[dim]), s.inv64[i], a);
-    s.part[tid] = a;
-    __syncthreads();
-    if (tid < D) {
-      double v = 0.0;
-      for (int q = 0; q < kParts; ++q) v += s.part[q * D + tid];
-      s.svec[tid] = v;
-    }
-    __syncthreads();
-  }
-  int parity = 0;  // one toggle for every block reduction: consecutive reductions use different slots
+  // 3. start: lowest mean cosine; fp32 row sums of the normalised Gram, with
+  // a binary64 decision when the best two are within the error window
   int pick;
   {
-    double mu = inf;
-    if (own) {
-      const typename E::T* x = fps_row<DT, D, NW>(s, tid);
-      double a = 0.0;
-#pragma unroll 8
-      for (int t = 0; t < D; ++t) a = fma(E::to_f64(x[t]), s.svec[t], a);
-      mu = a * s.inv64[tid] / (double)c;
+    float part[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NW; ++t) {
+      const int col = 32 * t + (lane & 31);
+      const bool ok = col < c;
+      const float w = ok ? s.inv32[col] : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[r] += ok ? acc[t][r] * w : 0.0f;
     }
-    pick = block_argmin64<NW>(mu, own ? tid : 0x7fffffff, s, parity);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[r] = half_wave_sum(part[r]);
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) colx[8 * (r >> 2) + 4 * half + (r & 3)] = part[r];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const float mu = owner ? colx[lane & 31] * inv_me / (float)c : finf;
+    __builtin_amdgcn_wave_barrier();
+    float b1, b2;
+    int bi;
+    block_best2<NW>(mu, owner ? myrow : 0x7fffffff, s, parity, b1, bi, b2);
+    const float eps_mu = F::kEps + 4.0f * (float)(c + 8) * F::kU32;
+    if (b2 <= b1 + 2.0f * eps_mu) {
+      const bool inwin = owner && mu <= b1 + 2.0f * eps_mu;
+      bi = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, 0, true, parity);
+    }
+    pick = bi;
   }
   if (tid == 0) s.picks[0] = pick;
 
   // 4. greedy rounds on fp32 cosines with the certified window
   const float eps2 = 2.0f * F::kEps;
-  float mt = finf;        // max fp32 cosine of this candidate to the picked set
-  bool picked = tid == pick;
-  const float inv_me = own ? s.inv32[tid] : 0.0f;
+  float mt = finf;  // max fp32 cosine of this candidate to the picked set
+  bool picked = myrow == pick;
   for (int t = 1; t < kk; ++t) {
-    // publish Gram row `pick`
+    // column `pick` of this wave's Gram tile, moved to the candidate owners
     {
-      const int pw = pick >> 5, m = pick & 31;
-      const int half = (m & 7) >> 2;
-      const int rr = ((m >> 3) << 2) | (m & 3);
-      if (wave == pw && (lane >> 5) == half) {
+      const int pt = pick >> 5;
+      fps_floatx16 colv = acc[0];
 #pragma unroll
-        for (int tt = 0; tt < NW; ++tt) {
-          if (tt < rt) {
-            float v = acc[tt][0];
+      for (int tt = 1; tt < NW; ++tt)
+        if (tt == pt) colv = acc[tt];
+      if ((lane & 31) == (pick & 31)) {
 #pragma unroll
-            for (int q = 1; q < 16; ++q) v = (q == rr) ? acc[tt][q] : v;
-            s.rowbuf[32 * tt + (lane & 31)] = v;
-          }
-        }
+        for (int r = 0; r < 16; ++r) colx[8 * (r >> 2) + 4 * half + (r & 3)] = colv[r];
       }
     }
-    __syncthreads();
-    const bool cand = own && !picked;
+    __builtin_amdgcn_wave_barrier();
+    const bool cand = owner && !picked;
     if (cand) {
-      const float cv = s.rowbuf[tid] * inv_me * s.inv32[pick];
+      const float cv = colx[lane & 31] * inv_me * s.inv32[pick];
       mt = (t == 1) ? cv : fmaxf(mt, cv);
     }
+    __builtin_amdgcn_wave_barrier();
     float b1, b2;
     int bi;
-    block_best2<NW>(cand ? mt : finf, cand ? tid : 0x7fffffff, s, parity, b1, bi, b2);
+    block_best2<NW>(cand ? mt : finf, cand ? myrow : 0x7fffffff, s, parity, b1, bi, b2);
     if (b2 <= b1 + eps2) {
-      // uncertain round: binary64 max cosines of every candidate in the window
-      const int inwin = (cand && mt <= b1 + eps2) ? 1 : 0;
-      int nu;
-      const int pos = block_exclusive_scan(inwin, s.misc + 0, &nu);  // misc used as scan scratch (<= 8 waves)
-      if (inwin) {
-        s.ulist[pos] = tid;
-        s.mexact[pos] = -inf;
-      }
-      __syncthreads();
-      const int ns = t;  // picks[0 .. t)
-      const int total = nu * ns;
-      const int q = tid % F::kP;
-      const int g = tid / F::kP;
-      for (int base = 0; base < total; base += F::kGroups) {
-        const int pr = base + g;
-        double cv = -inf;
-        int uu = -1;
-        if (pr < total) {
-          uu = pr / ns;
-          const int a = s.ulist[uu], b = s.picks[pr % ns];
-          cv = dot_slice64<DT, D, NW>(s, a, b, q);
-        }
-        cv = sum_lanes<F::kP>(cv);
-        if (pr < total) cv = cv * s.inv64[s.ulist[uu]] * s.inv64[s.picks[pr % ns]];
-        if (q == 0) {
-          s.pairv[g] = cv;
-          s.pairu[g] = uu;
-        }
-        __syncthreads();
-        if (tid < nu) {
-          double mx = s.mexact[tid];
-          for (int j = 0; j < F::kGroups; ++j)
-            if (s.pairu[j] == tid) mx = fmax(mx, s.pairv[j]);
-          s.mexact[tid] = mx;
-        }
-        __syncthreads();
-      }
-      const bool in = tid < nu;
-      bi = block_argmin64<NW>(in ? s.mexact[tid] : inf, in ? s.ulist[tid] : 0x7fffffff, s, parity);
+      const bool inwin = cand && mt <= b1 + eps2;
+      bi = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, t, false, parity);
     }
     pick = bi;
-    if (tid == pick) picked = true;
+    if (myrow == pick) picked = true;
     if (tid == 0) s.picks[t] = pick;
   }
   __syncthreads();
@@ -457,7 +467,7 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
 // ---------------------------------------------------------------------------
 
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void fps_update_kernel(const typename Elem<DT>::T* __restrict__ q_new, int T,
+__global__ __launch_bounds__(64 * NW, 2) void fps_update_kernel(const typename Elem<DT>::T* __restrict__ q_new, int T,
                                                              typename Elem<DT>::T* __restrict__ qbuf,
                                                              int32_t* __restrict__ qcount, int C, int M,
                                                              int32_t* __restrict__ ws_words) {
@@ -569,7 +579,7 @@ __device__ inline void rotate_store(const typename Elem<DT>::T* x, float2 cs, in
 }
 
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void obs_build_kernel(
+__global__ __launch_bounds__(64 * NW, 2) void obs_build_kernel(
     const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
     const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid,
