@@ -65,9 +65,7 @@ struct FpsSmem {
   float* inv32;         // [kMaxRows] the same, binary32
   float* colx;          // [NW][32] wave-private Gram column
   double* dslot;        // [2][NW] exact argmin values
-  int* islot;           // [2][NW] argmin indices
-  float* fslot1;        // [2][NW] fp32 best values
-  float* fslot2;        // [2][NW] fp32 runner-up values
+  int* islot;           // [2][2 NW] argmin indices / candidate-key pairs
   int* picks;           // [kMaxRows]
   int* ulist;           // [kMaxRows] candidates inside an uncertain window
   double* uacc;         // [kMaxRows] their binary64 objectives
@@ -80,7 +78,7 @@ template <int DT, int D, int NW>
 __host__ __device__ constexpr size_t fps_smem_bytes(int nrows) {
   using F = Fps<DT, D, NW>;
   return (((size_t)nrows * F::kRowStride + 15) & ~(size_t)15) + F::kMaxRows * (8 + 4 + 4 + 4 + 8) +
-         NW * 32 * 4 + 2 * NW * (8 + 4 + 4 + 4) + F::kGroups * (8 + 4) + 64 + 128;
+         NW * 32 * 4 + 2 * NW * (8 + 4 + 4 + 8) + F::kGroups * (8 + 4) + 64 + 128;
 }
 
 template <int DT, int D, int NW>
@@ -100,9 +98,7 @@ __device__ inline FpsSmem fps_carve(unsigned char* smem, int nrows) {
   s.pairv = reinterpret_cast<double*>(take(F::kGroups * 8));
   s.inv32 = reinterpret_cast<float*>(take(F::kMaxRows * 4));
   s.colx = reinterpret_cast<float*>(take(NW * 32 * 4));
-  s.fslot1 = reinterpret_cast<float*>(take(2 * NW * 4));
-  s.fslot2 = reinterpret_cast<float*>(take(2 * NW * 4));
-  s.islot = reinterpret_cast<int*>(take(2 * NW * 4));
+  s.islot = reinterpret_cast<int*>(take(2 * 2 * NW * 4));
   s.picks = reinterpret_cast<int*>(take(F::kMaxRows * 4));
   s.ulist = reinterpret_cast<int*>(take(F::kMaxRows * 4));
   s.pairu = reinterpret_cast<int*>(take(F::kGroups * 4));
@@ -189,49 +185,64 @@ __device__ inline int block_argmin64(double v, int i, const FpsSmem& s, int& par
   return bi;
 }
 
-__device__ inline bool fbetter(float v, int i, float bv, int bi) { return v < bv || (v == bv && i < bi); }
+// Candidate keys: an fp32 value made order-preserving as a uint32, its low 8
+// bits replaced by the row index (rows < 256).  The minimum key is the row
+// with the lowest value bucket, ties to the lower row; a bucket spans 256
+// ulps of the value, which the callers add to their decision window.
+__device__ inline uint32_t cand_key(float v, int row) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (ord & 0xFFFFFF00u) | (uint32_t)row;
+}
+// Lowest value of a key's bucket, and the lowest value of the next bucket.
+__device__ inline float key_lo(uint32_t k) {
+  const uint32_t ord = k & 0xFFFFFF00u;
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ inline float key_hi(uint32_t k) {
+  const uint32_t ord = (k | 0xFFu) + 1u;
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
 
-// Block-wide (best value, best index, runner-up value) over one fp32 value
-// per thread; only lanes 0..31 of each wave carry candidates.
+template <int N>
+__device__ inline uint32_t row_ror_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xF, 0xF, false);
+}
+
+// Merge two (smallest, second smallest) key pairs of disjoint sets.
+__device__ inline void merge2(uint32_t& a1, uint32_t& a2, uint32_t b1, uint32_t b2) {
+  const uint32_t lo = a1 < b1 ? a1 : b1;
+  const uint32_t hi = a1 < b1 ? b1 : a1;
+  const uint32_t m2 = a2 < b2 ? a2 : b2;
+  a1 = lo;
+  a2 = hi < m2 ? hi : m2;
+}
+
+// Block-wide two smallest keys; candidates sit in lanes 0..31 of each wave
+// (other lanes pass 0xFFFFFFFF).  Rows of 16 lanes reduce by DPP rotation,
+// the two rows of the half wave through scalar lane reads, the waves through
+// one LDS exchange.  Every thread returns the same pair.
 template <int NW>
-__device__ inline void block_best2(float v, int i, const FpsSmem& s, int& parity, float& b1, int& bi, float& b2) {
-  float v2 = __builtin_huge_valf();
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const float ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(i, off, 64);
-    const float ov2 = __shfl_xor(v2, off, 64);
-    if (fbetter(ov, oi, v, i)) {
-      v2 = fminf(ov2, v);
-      v = ov;
-      i = oi;
-    } else {
-      v2 = fminf(v2, ov);
-    }
-  }
+__device__ inline void block_min2_keys(uint32_t key, const FpsSmem& s, int& parity, uint32_t& k1, uint32_t& k2) {
+  uint32_t a1 = key, a2 = 0xFFFFFFFFu;
+  merge2(a1, a2, row_ror_u<8>(a1), row_ror_u<8>(a2));
+  merge2(a1, a2, row_ror_u<4>(a1), row_ror_u<4>(a2));
+  merge2(a1, a2, row_ror_u<2>(a1), row_ror_u<2>(a2));
+  merge2(a1, a2, row_ror_u<1>(a1), row_ror_u<1>(a2));
+  uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)a1, 0);
+  uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)a2, 0);
+  merge2(w1, w2, (uint32_t)__builtin_amdgcn_readlane((int)a1, 16), (uint32_t)__builtin_amdgcn_readlane((int)a2, 16));
   const int wave = threadIdx.x >> 6;
+  uint32_t* slot = reinterpret_cast<uint32_t*>(s.islot) + parity * 2 * NW;
   if ((threadIdx.x & 63) == 0) {
-    s.fslot1[parity * NW + wave] = v;
-    s.fslot2[parity * NW + wave] = v2;
-    s.islot[parity * NW + wave] = i;
+    slot[2 * wave] = w1;
+    slot[2 * wave + 1] = w2;
   }
   __syncthreads();
-  b1 = s.fslot1[parity * NW];
-  bi = s.islot[parity * NW];
-  b2 = s.fslot2[parity * NW];
+  k1 = slot[0];
+  k2 = slot[1];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    const float ov = s.fslot1[parity * NW + w];
-    const int oi = s.islot[parity * NW + w];
-    const float ov2 = s.fslot2[parity * NW + w];
-    if (fbetter(ov, oi, b1, bi)) {
-      b2 = fminf(ov2, b1);
-      b1 = ov;
-      bi = oi;
-    } else {
-      b2 = fminf(b2, ov);
-    }
-  }
+  for (int w = 1; w < NW; ++w) merge2(k1, k2, slot[2 * w], slot[2 * w + 1]);
   parity ^= 1;
 }
 
@@ -411,15 +422,16 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
     __builtin_amdgcn_wave_barrier();
     const float mu = owner ? colx[lane & 31] * inv_me / (float)c : finf;
     __builtin_amdgcn_wave_barrier();
-    float b1, b2;
-    int bi;
-    block_best2<NW>(mu, owner ? myrow : 0x7fffffff, s, parity, b1, bi, b2);
+    uint32_t k1, k2;
+    block_min2_keys<NW>(owner ? cand_key(mu, myrow) : 0xFFFFFFFFu, s, parity, k1, k2);
     const float eps_mu = F::kEps + 4.0f * (float)(c + 8) * F::kU32;
-    if (b2 <= b1 + 2.0f * eps_mu) {
-      const bool inwin = owner && mu <= b1 + 2.0f * eps_mu;
-      bi = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, 0, true, parity);
+    const float hi1 = key_hi(k1) + 2.0f * eps_mu;
+    if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
+      const bool inwin = owner && mu <= hi1;
+      pick = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, 0, true, parity);
+    } else {
+      pick = (int)(k1 & 0xFFu);
     }
-    pick = bi;
   }
   if (tid == 0) s.picks[0] = pick;
 
@@ -447,14 +459,15 @@ __device__ int fps_core(const FpsSmem& s, int c, int k) {
       mt = (t == 1) ? cv : fmaxf(mt, cv);
     }
     __builtin_amdgcn_wave_barrier();
-    float b1, b2;
-    int bi;
-    block_best2<NW>(cand ? mt : finf, cand ? myrow : 0x7fffffff, s, parity, b1, bi, b2);
-    if (b2 <= b1 + eps2) {
-      const bool inwin = cand && mt <= b1 + eps2;
-      bi = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, t, false, parity);
+    uint32_t k1, k2;
+    block_min2_keys<NW>(cand ? cand_key(mt, myrow) : 0xFFFFFFFFu, s, parity, k1, k2);
+    const float hi1 = key_hi(k1) + eps2;
+    if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
+      const bool inwin = cand && mt <= hi1;
+      pick = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, t, false, parity);
+    } else {
+      pick = (int)(k1 & 0xFFu);
     }
-    pick = bi;
     if (myrow == pick) picked = true;
     if (tid == 0) s.picks[t] = pick;
   }
