@@ -16,23 +16,29 @@
 // all rows; then repeatedly add the row with the lowest maximum cosine to the
 // picked set; ties go to the lower row.
 //
-// The decisions are those of binary64 evaluation:
-//   * the start (mean cosines) is evaluated in binary64;
-//   * the greedy rounds run on the Gram matrix X X^T from the matrix cores
-//     (bf16 or fp32 products are exact, sums are fp32), which bounds the
-//     error of every fp32 cosine by eps = 4 (d + 8) 2^-24 (fp32 dot-product
-//     error bound gamma_d plus the normalisation roundings, doubled).  When
-//     the best candidate is not ahead of the runner-up by more than 2 eps,
-//     the maximum cosines of every candidate inside that window are
-//     recomputed from the rows in binary64 and decide the pick;
-//   * rows whose norms leave [1e-15, 1e18] (where fp32 Gram entries could
-//     underflow or overflow) send the whole call to a plain binary64 path.
+// One wavefront per query head, no block barriers.  The head's rows stay in
+// global memory (they are read once into matrix-core fragments, and again
+// only for binary64 decisions and the write-back); LDS holds the packed
+// strict lower triangle of the fp32 Gram matrix (32.5 KB for 128 rows, so
+// four heads share a CU).
 //
-// One workgroup of 64 * NW threads per query head handles up to 32 * NW
-// rows; thread i owns candidate row i.  The live buffer sits in LDS in its
-// storage type (rows padded by 16 bytes); wave w keeps Gram rows
-// [32 w, 32 w + 32) in its MFMA accumulators, and each pick publishes one
-// Gram row through LDS.
+// The decisions are those of binary64 evaluation:
+//   * squared norms are fp32 sums of exact products (dot2 on bf16), so
+//     1/|x| carries a relative error below d u / 2 + 2 u (u = 2^-24); the
+//     Gram matrix comes from the matrix cores (exact bf16 products, fp32
+//     sums: error below d u |x_i| |x_j|).  Every fp32 cosine
+//     G_ij / (|x_i| |x_j|) is therefore within (2 d + 6) u of the exact one,
+//     plus at most 2^-19 for products flushed below the fp32 normal range;
+//     the decisions use the wider bound eps = 4 (d + 8) u, and the mean
+//     cosines eps + 4 (c + 8) u (c-term fp32 sum and one division more);
+//   * candidates are compared on keys (order-preserving fp32 bits, low 8
+//     bits replaced by the row index).  When the runner-up is not more than
+//     2 eps above the best, every candidate inside that window is evaluated
+//     from the rows in binary64 and the lowest value wins, ties to the lower
+//     row;
+//   * a row whose squared norm leaves [1e-30, 1e36], or a nonzero row whose
+//     fp32 squared norm underflows to 0, sends the whole call to binary64
+//     rounds over every candidate.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,148 +47,123 @@
 namespace bkv {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 fps_bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 fps_bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float fps_floatx16;
+typedef float fps_float8 __attribute__((ext_vector_type(8)));
 
-template <int DT, int D, int NW>
-struct Fps {
-  using E = Elem<DT>;
-  using ET = typename E::T;
-  static constexpr int NT = 64 * NW;
-  static constexpr int kMaxRows = 32 * NW;
-  static constexpr int kRowBytes = D * E::kBytes;
-  static constexpr int kRowStride = kRowBytes + 16;
-  static constexpr int kU = kRowBytes / 16;   // 16-byte units per row
-  static constexpr int kPer16 = 16 / E::kBytes;
-  static constexpr int kP = D / 32;           // lanes per exact dot product (32 dims each)
-  static constexpr int kGroups = NT / kP;     // exact dot products per sweep
-  static constexpr float kU32 = 5.9604644775390625e-8f;  // 2^-24
-  static constexpr float kEps = 4.0f * (D + 8) * kU32;   // bound on |fp32 cosine - cosine|
+constexpr float kFpsU = 5.9604644775390625e-8f;  // 2^-24
+
+// Offset of row i in the packed strict lower triangle (entries (i, j), j < i).
+__host__ __device__ constexpr int tri(int i) { return i * (i - 1) / 2; }
+
+// ---------------------------------------------------------------------------
+// Matrix-core fragments per storage type
+// ---------------------------------------------------------------------------
+
+template <int DT, int D>
+struct FpsFrag;
+
+// v_mfma_f32_32x32x16_bf16: lane (n, h) = (lane % 32, lane / 32) supplies
+// row n of its 32-row tile, dims 16 ks + 8 h + [0, 8).
+template <int D>
+struct FpsFrag<BKV_BF16, D> {
+  using T = uint16_t;
+  using V = uint4;
+  static constexpr int kSteps = D / 16;
+  __device__ static inline V load(const T* row, int ks, int h) {
+    return *reinterpret_cast<const uint4*>(row + 16 * ks + 8 * h);
+  }
+  __device__ static inline V zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  __device__ static inline fps_floatx16 mma(V a, V b, fps_floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(fps_bf16x8, a),
+                                                  __builtin_bit_cast(fps_bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static inline float sq2(uint32_t w, float acc) {
+    const fps_bf16x2 x = __builtin_bit_cast(fps_bf16x2, w);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+  }
+  __device__ static inline float sumsq(V v, float acc) {
+    return sq2(v.w, sq2(v.z, sq2(v.y, sq2(v.x, acc))));
+  }
+  __device__ static inline uint32_t nonzero(V v) { return (v.x | v.y | v.z | v.w) & 0x7FFF7FFFu; }
 };
 
-struct FpsSmem {
-  unsigned char* rows;  // row r at rows + r * kRowStride
-  double* inv64;        // [kMaxRows] 1 / max(|x|, 1e-12), binary64
-  float* inv32;         // [kMaxRows] the same, binary32
-  float* colx;          // [NW][32] wave-private Gram column
-  double* dslot;        // [2][NW] exact argmin values
-  int* islot;           // [2][2 NW] argmin indices / candidate-key pairs
-  int* picks;           // [kMaxRows]
-  int* ulist;           // [kMaxRows] candidates inside an uncertain window
-  double* uacc;         // [kMaxRows] their binary64 objectives
-  double* pairv;        // [kGroups]
-  int* pairu;           // [kGroups]
-  int* misc;            // [16] block-scan scratch
+// v_mfma_f32_32x32x2f32: lane (n, h) supplies row n, dim 2 ks + h.
+template <int D>
+struct FpsFrag<BKV_F32, D> {
+  using T = float;
+  using V = float;
+  static constexpr int kSteps = D / 2;
+  __device__ static inline V load(const T* row, int ks, int h) { return row[2 * ks + h]; }
+  __device__ static inline V zero() { return 0.0f; }
+  __device__ static inline fps_floatx16 mma(V a, V b, fps_floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline float sumsq(V v, float acc) { return fmaf(v, v, acc); }
+  __device__ static inline uint32_t nonzero(V v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
 };
 
-template <int DT, int D, int NW>
-__host__ __device__ constexpr size_t fps_smem_bytes(int nrows) {
-  using F = Fps<DT, D, NW>;
-  return (((size_t)nrows * F::kRowStride + 15) & ~(size_t)15) + F::kMaxRows * (8 + 4 + 4 + 4 + 8) +
-         NW * 32 * 4 + 2 * NW * (8 + 4 + 4 + 8) + F::kGroups * (8 + 4) + 64 + 128;
+// ---------------------------------------------------------------------------
+// Row sources and LDS layout
+// ---------------------------------------------------------------------------
+
+// Buffer row r lives at map[r]: values below C are rows of the buffer as it
+// was on entry, values C + t are arrival t of the call.
+template <int DT, int D>
+struct FpsRows {
+  const typename Elem<DT>::T* buf;
+  const typename Elem<DT>::T* qn;
+  const int* map;  // LDS
+  int C;
+  __device__ inline const typename Elem<DT>::T* row(int r) const {
+    const int v = map[r];
+    return v < C ? buf + (size_t)v * D : qn + (size_t)(v - C) * D;
+  }
+};
+
+struct FpsLds {
+  float* gram;           // packed strict lower triangle of the Gram matrix
+  unsigned char* stage;  // aliases gram: rows staged for the buffer write-back
+  float* inv32;          // [cap] fp32 1 / |x| (0 for rows past the count)
+  int* map;              // [cap]
+  int* picks;            // [cap]
+};
+
+template <int DT, int D>
+__host__ __device__ constexpr size_t fps_gram_bytes(int cap, int M) {
+  const size_t g = ((size_t)tri(cap) + 64) * 4;  // + a pad: the greedy may read one entry past the end
+  const size_t st = (size_t)M * D * Elem<DT>::kBytes;
+  return ((g > st ? g : st) + 15) & ~(size_t)15;
 }
 
-template <int DT, int D, int NW>
-__device__ inline FpsSmem fps_carve(unsigned char* smem, int nrows) {
-  using F = Fps<DT, D, NW>;
-  FpsSmem s;
-  size_t off = ((size_t)nrows * F::kRowStride + 15) & ~(size_t)15;
-  s.rows = smem;
-  auto take = [&](size_t bytes) {
-    unsigned char* p = smem + off;
-    off += (bytes + 7) & ~(size_t)7;
-    return p;
-  };
-  s.inv64 = reinterpret_cast<double*>(take(F::kMaxRows * 8));
-  s.uacc = reinterpret_cast<double*>(take(F::kMaxRows * 8));
-  s.dslot = reinterpret_cast<double*>(take(2 * NW * 8));
-  s.pairv = reinterpret_cast<double*>(take(F::kGroups * 8));
-  s.inv32 = reinterpret_cast<float*>(take(F::kMaxRows * 4));
-  s.colx = reinterpret_cast<float*>(take(NW * 32 * 4));
-  s.islot = reinterpret_cast<int*>(take(2 * 2 * NW * 4));
-  s.picks = reinterpret_cast<int*>(take(F::kMaxRows * 4));
-  s.ulist = reinterpret_cast<int*>(take(F::kMaxRows * 4));
-  s.pairu = reinterpret_cast<int*>(take(F::kGroups * 4));
-  s.misc = reinterpret_cast<int*>(take(64));
+template <int DT, int D>
+__host__ __device__ constexpr size_t fps_lds_bytes(int cap, int M) {
+  return fps_gram_bytes<DT, D>(cap, M) + (size_t)cap * (4 + 4 + 4);
+}
+
+template <int DT, int D>
+__device__ inline FpsLds fps_carve(unsigned char* smem, int cap, int M) {
+  const size_t gb = fps_gram_bytes<DT, D>(cap, M);
+  FpsLds s;
+  s.gram = reinterpret_cast<float*>(smem);
+  s.stage = smem;
+  s.inv32 = reinterpret_cast<float*>(smem + gb);
+  s.map = reinterpret_cast<int*>(smem + gb + (size_t)cap * 4);
+  s.picks = reinterpret_cast<int*>(smem + gb + (size_t)cap * 8);
   return s;
 }
 
-template <int DT, int D, int NW>
-__device__ inline const typename Elem<DT>::T* fps_row(const FpsSmem& s, int r) {
-  return reinterpret_cast<const typename Elem<DT>::T*>(s.rows + (size_t)r * Fps<DT, D, NW>::kRowStride);
-}
+// ---------------------------------------------------------------------------
+// Wave-level helpers
+// ---------------------------------------------------------------------------
 
-// binary64 dot product of dims [32 q, 32 q + 32) of rows a and b
-template <int DT, int D, int NW>
-__device__ inline double dot_slice64(const FpsSmem& s, int a, int b, int q) {
-  using F = Fps<DT, D, NW>;
-  using E = Elem<DT>;
-  const uint4* xa = reinterpret_cast<const uint4*>(fps_row<DT, D, NW>(s, a) + 32 * q);
-  const uint4* xb = reinterpret_cast<const uint4*>(fps_row<DT, D, NW>(s, b) + 32 * q);
-  double acc = 0.0;
-#pragma unroll 1
-  for (int u = 0; u < 32 / F::kPer16; ++u) {
-    const uint4 wa = xa[u], wb = xb[u];
-    const typename E::T* ea = reinterpret_cast<const typename E::T*>(&wa);
-    const typename E::T* eb = reinterpret_cast<const typename E::T*>(&wb);
-#pragma unroll
-    for (int k = 0; k < F::kPer16; ++k) acc = fma(E::to_f64(ea[k]), E::to_f64(eb[k]), acc);
-  }
-  return acc;
-}
+__device__ inline int fps_lane() { return threadIdx.x & 63; }
 
-template <int P>
-__device__ inline double sum_lanes(double v) {
-#pragma unroll
-  for (int off = 1; off < P; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Rotate a value within each 16-lane row of the wave (row_ror DPP).
-template <int N>
-__device__ inline float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
-}
-
-// Sum over the 32 lanes of each half wave (every lane of the half gets a sum).
-__device__ inline float half_wave_sum(float v) {
-  v += row_ror<8>(v);
-  v += row_ror<4>(v);
-  v += row_ror<2>(v);
-  v += row_ror<1>(v);
-  return v + __shfl_xor(v, 16, 64);
-}
-
-// Block-wide argmin of (value, index); every thread gets the winning index.
-template <int NW>
-__device__ inline int block_argmin64(double v, int i, const FpsSmem& s, int& parity) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double ov = __shfl_xor(v, off, 64);
-    const int oi = __shfl_xor(i, off, 64);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    s.dslot[parity * NW + wave] = v;
-    s.islot[parity * NW + wave] = i;
-  }
-  __syncthreads();
-  double bv = s.dslot[parity * NW];
-  int bi = s.islot[parity * NW];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) {
-    const double ov = s.dslot[parity * NW + w];
-    const int oi = s.islot[parity * NW + w];
-    if (better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-  parity ^= 1;
-  return bi;
+__device__ inline double readfirstlane_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // Candidate keys: an fp32 value made order-preserving as a uint32, its low 8
@@ -218,332 +199,434 @@ __device__ inline void merge2(uint32_t& a1, uint32_t& a2, uint32_t b1, uint32_t 
   a2 = hi < m2 ? hi : m2;
 }
 
-// Block-wide two smallest keys; candidates sit in lanes 0..31 of each wave
-// (other lanes pass 0xFFFFFFFF).  Rows of 16 lanes reduce by DPP rotation,
-// the two rows of the half wave through scalar lane reads, the waves through
-// one LDS exchange.  Every thread returns the same pair.
-template <int NW>
-__device__ inline void block_min2_keys(uint32_t key, const FpsSmem& s, int& parity, uint32_t& k1, uint32_t& k2) {
-  uint32_t a1 = key, a2 = 0xFFFFFFFFu;
+// Two smallest keys of the wave (each lane brings its own pair): rows of 16
+// lanes reduce by DPP rotation, the four rows through scalar lane reads.
+// The results are wave-uniform.
+__device__ inline void wave_min2(uint32_t a1, uint32_t a2, uint32_t& k1, uint32_t& k2) {
   merge2(a1, a2, row_ror_u<8>(a1), row_ror_u<8>(a2));
   merge2(a1, a2, row_ror_u<4>(a1), row_ror_u<4>(a2));
   merge2(a1, a2, row_ror_u<2>(a1), row_ror_u<2>(a2));
   merge2(a1, a2, row_ror_u<1>(a1), row_ror_u<1>(a2));
   uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)a1, 0);
   uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)a2, 0);
-  merge2(w1, w2, (uint32_t)__builtin_amdgcn_readlane((int)a1, 16), (uint32_t)__builtin_amdgcn_readlane((int)a2, 16));
-  const int wave = threadIdx.x >> 6;
-  uint32_t* slot = reinterpret_cast<uint32_t*>(s.islot) + parity * 2 * NW;
-  if ((threadIdx.x & 63) == 0) {
-    slot[2 * wave] = w1;
-    slot[2 * wave + 1] = w2;
-  }
-  __syncthreads();
-  k1 = slot[0];
-  k2 = slot[1];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) merge2(k1, k2, slot[2 * w], slot[2 * w + 1]);
-  parity ^= 1;
+  for (int r = 16; r < 64; r += 16)
+    merge2(w1, w2, (uint32_t)__builtin_amdgcn_readlane((int)a1, r), (uint32_t)__builtin_amdgcn_readlane((int)a2, r));
+  k1 = w1;
+  k2 = w2;
 }
 
-// Matrix-core fragment of k-step `ks` for row `r` (bf16 32x32x16 takes dims
-// 16 ks + 8 (lane / 32) + [0, 8); fp32 32x32x2 takes dim 2 ks + lane / 32).
-template <int DT>
-struct GramMma;
+// ---------------------------------------------------------------------------
+// Binary64 decisions
+// ---------------------------------------------------------------------------
 
-template <>
-struct GramMma<BKV_BF16> {
-  template <int D>
-  static constexpr int steps() { return D / 16; }
-  __device__ static inline fps_bf16x8 frag(const unsigned char* row, int ks, int lane) {
-    uint4 w = *reinterpret_cast<const uint4*>(row + (size_t)(16 * ks + 8 * (lane >> 5)) * 2);
-    return __builtin_bit_cast(fps_bf16x8, w);
-  }
-  __device__ static inline fps_floatx16 mma(fps_bf16x8 a, fps_bf16x8 b, fps_floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct GramMma<BKV_F32> {
-  template <int D>
-  static constexpr int steps() { return D / 2; }
-  __device__ static inline float frag(const unsigned char* row, int ks, int lane) {
-    return *reinterpret_cast<const float*>(row + (size_t)(2 * ks + (lane >> 5)) * 4);
-  }
-  __device__ static inline fps_floatx16 mma(float a, float b, fps_floatx16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-  }
-};
-
-// Binary64 decision among the candidates flagged `inwin` (row `myrow`):
-// objective = mean cosine to all c rows (sum_mode) or maximum cosine to the
-// picks so far (picks[0 .. npicked)).  Returns the row with the lowest
-// objective, ties to the lower row.  Every thread of the block must call it.
-// Wave w evaluates window members w, w + NW, ...; its lanes split the
-// partner rows in groups of kP lanes (32 dimensions each).
-template <int DT, int D, int NW>
-__device__ int exact_window_argmin(const FpsSmem& s, bool inwin, int myrow, int c, int npicked, bool sum_mode,
-                                   int& parity) {
-  using F = Fps<DT, D, NW>;
-  constexpr int kPerWave = 64 / F::kP;  // partner rows per sweep of a wave
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const double inf = __builtin_huge_val();
-  int nu;
-  const int pos = block_exclusive_scan(inwin ? 1 : 0, s.misc, &nu);
-  if (inwin) s.ulist[pos] = myrow;
-  __syncthreads();
-  const int npart = sum_mode ? c : npicked;
-  const int q = lane % F::kP;
-  for (int u = wave; u < nu; u += NW) {
-    const int a = s.ulist[u];
-    double acc = sum_mode ? 0.0 : -inf;
-    for (int j0 = 0; j0 < npart; j0 += kPerWave) {
-      const int j = j0 + lane / F::kP;
-      const int b = j < npart ? (sum_mode ? j : s.picks[j]) : a;
-      double v = dot_slice64<DT, D, NW>(s, a, b, q);
-      v = sum_lanes<F::kP>(v) * s.inv64[a] * s.inv64[b];
-      if (j < npart) acc = sum_mode ? acc + v : fmax(acc, v);
-    }
-    // combine the partner groups of the wave (lanes 0, kP, 2 kP, ... hold them)
-#pragma unroll
-    for (int off = F::kP; off < 64; off <<= 1) {
-      const double o = __shfl_xor(acc, off, 64);
-      acc = sum_mode ? acc + o : fmax(acc, o);
-    }
-    if (lane == 0) s.uacc[u] = sum_mode ? acc / (double)c : acc;
-  }
-  __syncthreads();
-  const bool in = tid < nu;
-  return block_argmin64<NW>(in ? s.uacc[tid] : inf, in ? s.ulist[tid] : 0x7fffffff, s, parity);
-}
-
-// FPS over LDS rows [0, c), c <= 32 NW: writes min(k, c) picks to s.picks
-// and returns the count.  Every thread of the block must call it; all 32 NW
-// LDS rows must be readable.  Candidate row i is owned by lane i % 32 of wave
-// i / 32, the wave whose MFMA accumulators hold Gram rows [32 w, 32 w + 32).
-template <int DT, int D, int NW>
-__device__ int fps_core(const FpsSmem& s, int c, int k) {
-  using F = Fps<DT, D, NW>;
+// binary64 a.b, a.a and b.b of two rows; each row's loads go out together
+// (up to 8 units of 16 bytes at a time) before the arithmetic
+template <int DT, int D>
+__device__ inline void fps_dots64(const typename Elem<DT>::T* a, const typename Elem<DT>::T* b, double& ab,
+                                  double& aa, double& bb) {
   using E = Elem<DT>;
-  using MM = GramMma<DT>;
-  constexpr int KS = MM::template steps<D>();
-  const int kk = k < c ? k : c;
-  if (kk <= 0) return 0;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const float finf = __builtin_huge_valf();
-  int parity = 0;  // one toggle for every block reduction: consecutive reductions use different slots
-
-  // 1. binary64 norms (clamped at 1e-12) and the fp32-safety check
-  int unsafe = 0;
-  if (tid < c) {
-    const uint4* x = reinterpret_cast<const uint4*>(fps_row<DT, D, NW>(s, tid));
-    double ss = 0.0;
-#pragma unroll 2
-    for (int u = 0; u < F::kU; ++u) {
-      const uint4 w = x[u];
-      const typename E::T* e = reinterpret_cast<const typename E::T*>(&w);
+  constexpr int kPer16 = 16 / E::kBytes;
+  constexpr int kU = D / kPer16;
+  constexpr int kC = kU < 8 ? kU : 8;
+  const uint4* xa = reinterpret_cast<const uint4*>(a);
+  const uint4* xb = reinterpret_cast<const uint4*>(b);
+  ab = aa = bb = 0.0;
 #pragma unroll
-      for (int j = 0; j < F::kPer16; ++j) {
-        const double v = E::to_f64(e[j]);
-        ss = fma(v, v, ss);
+  for (int u0 = 0; u0 < kU; u0 += kC) {
+    uint4 wa[kC], wb[kC];
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      wa[u] = xa[u0 + u];
+      wb[u] = xb[u0 + u];
+    }
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const typename E::T* ea = reinterpret_cast<const typename E::T*>(&wa[u]);
+      const typename E::T* eb = reinterpret_cast<const typename E::T*>(&wb[u]);
+#pragma unroll
+      for (int k = 0; k < kPer16; ++k) {
+        const double va = E::to_f64(ea[k]), vb = E::to_f64(eb[k]);
+        ab = fma(va, vb, ab);
+        aa = fma(va, va, aa);
+        bb = fma(vb, vb, bb);
+      }
+      // keep the binary64 conversions of one unit at a time in registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Lowest binary64 objective among the candidates flagged in `inmask` (bit b
+// of word w = row 64 w + b), ties to the lower row.  Objective: the mean
+// cosine to all c rows (sum_mode) or the maximum cosine to picks[0, npicked),
+// cosines as a.b / (max(|a|, 1e-12) max(|b|, 1e-12)).  The lanes split the
+// partner rows; the result is wave-uniform.
+template <int DT, int D, int SL>
+__device__ __attribute__((always_inline)) int fps_exact_argmin(const FpsRows<DT, D>& src, const FpsLds& s, const uint64_t* inmask, int c,
+                                int npicked, bool sum_mode) {
+  const int lane = fps_lane();
+  const int npart = sum_mode ? c : npicked;
+  const double inf = __builtin_huge_val();
+  double best = inf;
+  int besti = 0x7fffffff;
+#pragma unroll
+  for (int w = 0; w < SL; ++w) {
+    uint64_t m = inmask[w];
+    while (m) {
+      const int a = 64 * w + (int)__builtin_ctzll(m);
+      m &= m - 1;
+      const typename Elem<DT>::T* xa = src.row(a);
+      double acc = sum_mode ? 0.0 : -inf;
+#pragma unroll 1
+      for (int q = lane; q < npart; q += 64) {
+        const int b = sum_mode ? q : s.picks[q];
+        double ab, aa, bb;
+        fps_dots64<DT, D>(xa, src.row(b), ab, aa, bb);
+        const double na = sqrt(aa), nb = sqrt(bb);
+        const double v = ab * (1.0 / (na < 1e-12 ? 1e-12 : na)) * (1.0 / (nb < 1e-12 ? 1e-12 : nb));
+        acc = sum_mode ? acc + v : fmax(acc, v);
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const double o = __shfl_xor(acc, off, 64);
+        acc = sum_mode ? acc + o : fmax(acc, o);
+      }
+      const double obj = readfirstlane_f64(sum_mode ? acc / (double)c : acc);
+      if (obj < best) {  // candidates come in increasing row order: ties keep the lower row
+        best = obj;
+        besti = a;
       }
     }
-    const double n = sqrt(ss);
-    unsafe = (n > 0.0 && (n < 1e-15 || n > 1e18)) ? 1 : 0;
-    const double inv = 1.0 / (n < 1e-12 ? 1e-12 : n);
-    s.inv64[tid] = inv;
-    s.inv32[tid] = (float)inv;
   }
-  const bool unsafe_any = __syncthreads_or(unsafe) != 0;
+  return besti;
+}
 
-  // candidate owned by this lane
-  const int myrow = 32 * wave + (lane & 31);
-  const bool owner = lane < 32 && myrow < c;
+// ---------------------------------------------------------------------------
+// FPS of one head by one wavefront
+// ---------------------------------------------------------------------------
 
-  if (unsafe_any) {  // plain binary64 rounds over every candidate
-    int pick = exact_window_argmin<DT, D, NW>(s, owner, myrow, c, 0, true, parity);
-    if (tid == 0) s.picks[0] = pick;
-    bool picked = myrow == pick;
-    for (int t = 1; t < kk; ++t) {
-      __syncthreads();  // picks[t - 1] visible
-      pick = exact_window_argmin<DT, D, NW>(s, owner && !picked, myrow, c, t, false, parity);
-      if (myrow == pick) picked = true;
-      if (tid == 0) s.picks[t] = pick;
+// Writes the FPS picks of rows [0, c) (c <= 32 NT) to s.picks, min(k, c) of
+// them, and returns the count.  Every lane of the wave must call it.
+template <int DT, int D, int NT>
+__device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src, const FpsLds& s, int c, int k) {
+  using FR = FpsFrag<DT, D>;
+  using V = typename FR::V;
+  using T = typename Elem<DT>::T;
+  constexpr int KS = FR::kSteps;
+  constexpr int SL = (NT + 1) / 2;  // candidate slots per lane: rows lane + 64 sl
+  constexpr float kEps = 4.0f * (D + 8) * kFpsU;
+  const int kk = k < c ? k : c;
+  if (kk <= 0) return 0;
+  // the lane id passes through an empty asm statement, so the many
+  // lane-derived addresses below are computed where they are used rather
+  // than hoisted out of a caller's loop and held in registers
+  int lane = fps_lane();
+  __asm__ volatile("" : "+v"(lane));
+  const int n = lane & 31, h = lane >> 5;
+  const float finf = __builtin_huge_valf();
+
+  // 1. matrix-core fragments of every row (rows past the count are zero),
+  // held in registers when they fit in 128 of them, else reloaded per use
+  constexpr bool kHold = NT * KS * (int)(sizeof(V) / 4) <= 128;
+  const T* rowp[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) rowp[t] = 32 * t + n < c ? src.row(32 * t + n) : nullptr;
+  auto frag = [&](int t, int ks) -> V { return rowp[t] ? FR::load(rowp[t], ks, h) : FR::zero(); };
+  V fr[kHold ? NT : 1][kHold ? KS : 1];
+  if constexpr (kHold) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) fr[t][ks] = frag(t, ks);
     }
-    __syncthreads();
+  }
+
+  // 2. fp32 inverse norms; lane (n, h) keeps those of rows 32 t + n (vector
+  // types: per-lane selections below must not turn into indexed memory)
+  fps_float8 invr = {};
+  int unsafe = 0;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float ss = 0.0f;
+    uint32_t nz = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      V v;
+      if constexpr (kHold) v = fr[t][ks];
+      else v = frag(t, ks);
+      ss = FR::sumsq(v, ss);
+      nz |= FR::nonzero(v);
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    nz |= (uint32_t)__shfl_xor((int)nz, 32, 64);
+    const int r = 32 * t + n;
+    float inv = 0.0f;
+    if (r < c) {
+      if (ss > 0.0f) {
+        if (!(ss >= 1e-30f && ss <= 1e36f)) unsafe = 1;
+        inv = (float)(1.0 / sqrt((double)ss));
+      } else {
+        if (nz) unsafe = 1;  // nonzero row whose fp32 squares underflow
+        inv = 1e12f;         // zero row: norm clamped at 1e-12, every cosine 0
+      }
+    }
+    invr[t] = inv;
+    if (h == 0) s.inv32[r] = inv;
+  }
+  uint64_t valid[SL];
+#pragma unroll
+  for (int w = 0; w < SL; ++w) {
+    const int cnt = c - 64 * w;
+    valid[w] = cnt >= 64 ? ~0ull : (cnt > 0 ? ((1ull << cnt) - 1) : 0ull);
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  if (__ballot(unsafe) != 0) {  // binary64 rounds over every candidate
+    uint64_t avail[SL];
+#pragma unroll
+    for (int w = 0; w < SL; ++w) avail[w] = valid[w];
+    for (int t = 0; t < kk; ++t) {
+      const int pick = fps_exact_argmin<DT, D, SL>(src, s, avail, c, t, t == 0);
+#pragma unroll
+      for (int w = 0; w < SL; ++w)
+        if ((pick >> 6) == w) avail[w] &= ~(1ull << (pick & 63));
+      if (lane == 0) s.picks[t] = pick;
+      __builtin_amdgcn_wave_barrier();
+    }
     return kk;
   }
 
-  // 2. Gram rows of this wave's tile on the matrix cores.  Every wave
-  // multiplies every tile of the 32 NW LDS rows (rows at or beyond c hold
-  // unused values): the MFMA chain is branch-free, so the compiler's
-  // accumulator-read wait states cover every path to the reads below.
-  fps_floatx16 acc[NW];
-  {
-    const unsigned char* arow = s.rows + (size_t)(32 * wave + (lane & 31)) * F::kRowStride;
+  // 3. Gram matrix on the matrix cores, one 32-row tile at a time (the MFMA
+  // chain is straight-line code): column sums of G_ij / |x_i| for the mean
+  // cosines, and the strict lower triangle into LDS
+  fps_float8 cs = {};
 #pragma unroll
-    for (int t = 0; t < NW; ++t) {
-      const unsigned char* brow = s.rows + (size_t)(32 * t + (lane & 31)) * F::kRowStride;
-      acc[t] = fps_floatx16{};
+  for (int tr = 0; tr < NT; ++tr) {
+    fps_floatx16 acc[NT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc[t] = MM::mma(MM::frag(arow, ks, lane), MM::frag(brow, ks, lane), acc[t]);
-    }
-  }
-  float* colx = s.colx + 32 * wave;
-  const int half = lane >> 5;
-  const float inv_me = owner ? s.inv32[myrow] : 0.0f;
-
-  // 3. start: lowest mean cosine; fp32 row sums of the normalised Gram, with
-  // a binary64 decision when the best two are within the error window
-  int pick;
-  {
-    float part[16];
+    for (int tc = 0; tc < NT; ++tc) acc[tc] = fps_floatx16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[r] = 0.0f;
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (kHold) {
 #pragma unroll
-    for (int t = 0; t < NW; ++t) {
-      const int col = 32 * t + (lane & 31);
-      const bool ok = col < c;
-      const float w = ok ? s.inv32[col] : 0.0f;
+        for (int tc = 0; tc < NT; ++tc) acc[tc] = FR::mma(fr[tr][ks], fr[tc][ks], acc[tc]);
+      } else {
+        const V a = frag(tr, ks);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part[r] += ok ? acc[t][r] * w : 0.0f;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[r] = half_wave_sum(part[r]);
-    if ((lane & 31) == 0) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) colx[8 * (r >> 2) + 4 * half + (r & 3)] = part[r];
-    }
-    __builtin_amdgcn_wave_barrier();
-    const float mu = owner ? colx[lane & 31] * inv_me / (float)c : finf;
-    __builtin_amdgcn_wave_barrier();
-    uint32_t k1, k2;
-    block_min2_keys<NW>(owner ? cand_key(mu, myrow) : 0xFFFFFFFFu, s, parity, k1, k2);
-    const float eps_mu = F::kEps + 4.0f * (float)(c + 8) * F::kU32;
-    const float hi1 = key_hi(k1) + 2.0f * eps_mu;
-    if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
-      const bool inwin = owner && mu <= hi1;
-      pick = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, 0, true, parity);
-    } else {
-      pick = (int)(k1 & 0xFFu);
-    }
-  }
-  if (tid == 0) s.picks[0] = pick;
-
-  // 4. greedy rounds on fp32 cosines with the certified window
-  const float eps2 = 2.0f * F::kEps;
-  float mt = finf;  // max fp32 cosine of this candidate to the picked set
-  bool picked = myrow == pick;
-  for (int t = 1; t < kk; ++t) {
-    // column `pick` of this wave's Gram tile, moved to the candidate owners
-    {
-      const int pt = pick >> 5;
-      fps_floatx16 colv = acc[0];
-#pragma unroll
-      for (int tt = 1; tt < NW; ++tt)
-        if (tt == pt) colv = acc[tt];
-      if ((lane & 31) == (pick & 31)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) colx[8 * (r >> 2) + 4 * half + (r & 3)] = colv[r];
+        for (int tc = 0; tc < NT; ++tc) acc[tc] = FR::mma(a, frag(tc, ks), acc[tc]);
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    const bool cand = owner && !picked;
-    if (cand) {
-      const float cv = colx[lane & 31] * inv_me * s.inv32[pick];
-      mt = (t == 1) ? cv : fmaxf(mt, cv);
+    // accumulator r of lane (n, h) holds G(32 tr + 8 (r / 4) + 4 h + r % 4, 32 tc + n)
+    const float4* ivp = reinterpret_cast<const float4*>(s.inv32 + 32 * tr + 4 * h);
+    const float4 iv[4] = {ivp[0], ivp[2], ivp[4], ivp[6]};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i0 = 32 * tr + 8 * (r >> 2) + (r & 3);  // row for h = 0; i = i0 + 4 h
+      const int rowoff = tri(i0) + (h ? 4 * i0 + 6 : 0) + n;  // tri(i) + n
+      const float4 q = iv[r >> 2];
+      const float w = (r & 3) == 0 ? q.x : (r & 3) == 1 ? q.y : (r & 3) == 2 ? q.z : q.w;
+#pragma unroll
+      for (int tc = 0; tc < NT; ++tc) {
+        const float g = acc[tc][r];
+        cs[tc] = fmaf(g, w, cs[tc]);
+        if (tr > tc || (tr == tc && i0 + 4 * h > 32 * tc + n)) s.gram[rowoff + 32 * tc] = g;
+      }
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+  fps_float8 S = {};
+#pragma unroll
+  for (int tc = 0; tc < NT; ++tc) S[tc] = cs[tc] + __shfl_xor(cs[tc], 32, 64);
+
+  // candidate slots of this lane: row j = 64 sl + lane = 32 (2 sl + h) + n
+  float invj[SL];
+  int trij[SL];
+#pragma unroll
+  for (int w = 0; w < SL; ++w) {
+    invj[w] = (2 * w + 1 < NT) ? (h ? invr[2 * w + 1] : invr[2 * w]) : invr[2 * w];
+    trij[w] = tri(64 * w + lane);
+  }
+
+  // 4. start: lowest mean cosine
+  int pick;
+  {
+    float mu[SL];
+    uint32_t a1 = 0xFFFFFFFFu, a2 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < SL; ++w) {
+      const int j = 64 * w + lane;
+      const float sj = (2 * w + 1 < NT) ? (h ? S[2 * w + 1] : S[2 * w]) : S[2 * w];
+      mu[w] = j < c ? (sj * invj[w]) / (float)c : finf;
+      merge2(a1, a2, j < c ? cand_key(mu[w], j) : 0xFFFFFFFFu, 0xFFFFFFFFu);
+    }
     uint32_t k1, k2;
-    block_min2_keys<NW>(cand ? cand_key(mt, myrow) : 0xFFFFFFFFu, s, parity, k1, k2);
-    const float hi1 = key_hi(k1) + eps2;
+    wave_min2(a1, a2, k1, k2);
+    const float eps_mu = kEps + 4.0f * (float)(c + 8) * kFpsU;
+    const float hi1 = key_hi(k1) + 2.0f * eps_mu;
     if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
-      const bool inwin = cand && mt <= hi1;
-      pick = exact_window_argmin<DT, D, NW>(s, inwin, myrow, c, t, false, parity);
+      uint64_t inmask[SL];
+#pragma unroll
+      for (int w = 0; w < SL; ++w) inmask[w] = __ballot(64 * w + lane < c && mu[w] <= hi1);
+      pick = fps_exact_argmin<DT, D, SL>(src, s, inmask, c, 0, true);
     } else {
       pick = (int)(k1 & 0xFFu);
     }
-    if (myrow == pick) picked = true;
-    if (tid == 0) s.picks[t] = pick;
   }
-  __syncthreads();
+  if (lane == 0) s.picks[0] = pick;
+
+  // 5. greedy rounds on fp32 cosines with the certified window
+  const float eps2 = 2.0f * kEps;
+  float mt[SL];
+  bool picked[SL];
+#pragma unroll
+  for (int w = 0; w < SL; ++w) {
+    mt[w] = -finf;
+    picked[w] = 64 * w + lane == pick;
+  }
+  for (int t = 1; t < kk; ++t) {
+    const int p = pick;
+    const float inv_p = s.inv32[p];
+    const int tp = tri(p);
+    uint32_t a1 = 0xFFFFFFFFu, a2 = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < SL; ++w) {
+      const int j = 64 * w + lane;
+      if (j < c) {
+        const float g = s.gram[j < p ? tp + j : trij[w] + p];
+        mt[w] = fmaxf(mt[w], (g * invj[w]) * inv_p);
+        merge2(a1, a2, picked[w] ? 0xFFFFFFFFu : cand_key(mt[w], j), 0xFFFFFFFFu);
+      }
+    }
+    uint32_t k1, k2;
+    wave_min2(a1, a2, k1, k2);
+    const float hi1 = key_hi(k1) + eps2;
+    if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
+      uint64_t inmask[SL];
+#pragma unroll
+      for (int w = 0; w < SL; ++w) inmask[w] = __ballot(64 * w + lane < c && !picked[w] && mt[w] <= hi1);
+      __builtin_amdgcn_wave_barrier();
+      pick = fps_exact_argmin<DT, D, SL>(src, s, inmask, c, t, false);
+    } else {
+      pick = (int)(k1 & 0xFFu);
+    }
+#pragma unroll
+    for (int w = 0; w < SL; ++w) picked[w] = picked[w] || (64 * w + lane == pick);
+    if (lane == 0) s.picks[t] = pick;
+  }
+  __builtin_amdgcn_wave_barrier();
   return kk;
+}
+
+// FPS over rows [0, c) with the tile count of c (1 .. 4 tiles of 32, else 8).
+template <int DT, int D, int NTMAX>
+__device__ __attribute__((always_inline)) int fps_dispatch(const FpsRows<DT, D>& src, const FpsLds& s, int c, int k) {
+  const int nt = (c + 31) >> 5;
+  if (nt <= 1) return fps_wave<DT, D, 1>(src, s, c, k);
+  if (nt == 2) return fps_wave<DT, D, 2>(src, s, c, k);
+  if constexpr (NTMAX >= 4) {
+    if (nt == 3) return fps_wave<DT, D, 3>(src, s, c, k);
+    if (nt == 4) return fps_wave<DT, D, 4>(src, s, c, k);
+  }
+  if constexpr (NTMAX >= 8) return fps_wave<DT, D, 8>(src, s, c, k);  // 5 .. 8 tiles
+  return 0;
+}
+
+// Copies n 16-byte units, unit u from src_at(u) to dst_at(u, v), with eight
+// loads per lane in flight (clamped in bounds) ahead of their stores.
+template <typename SrcF, typename DstF>
+__device__ inline void copy_units(int n, SrcF src_at, DstF dst_at) {
+  const int l = fps_lane();
+  for (int u0 = 0; u0 < n; u0 += 512) {
+    const int m = n - 1;
+    const uint4 v0 = src_at(min(u0 + l, m));
+    const uint4 v1 = src_at(min(u0 + 64 + l, m));
+    const uint4 v2 = src_at(min(u0 + 128 + l, m));
+    const uint4 v3 = src_at(min(u0 + 192 + l, m));
+    const uint4 v4 = src_at(min(u0 + 256 + l, m));
+    const uint4 v5 = src_at(min(u0 + 320 + l, m));
+    const uint4 v6 = src_at(min(u0 + 384 + l, m));
+    const uint4 v7 = src_at(min(u0 + 448 + l, m));
+    if (u0 + l < n) dst_at(u0 + l, v0);
+    if (u0 + 64 + l < n) dst_at(u0 + 64 + l, v1);
+    if (u0 + 128 + l < n) dst_at(u0 + 128 + l, v2);
+    if (u0 + 192 + l < n) dst_at(u0 + 192 + l, v3);
+    if (u0 + 256 + l < n) dst_at(u0 + 256 + l, v4);
+    if (u0 + 320 + l < n) dst_at(u0 + 320 + l, v5);
+    if (u0 + 384 + l < n) dst_at(u0 + 384 + l, v6);
+    if (u0 + 448 + l < n) dst_at(u0 + 448 + l, v7);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Ingest
 // ---------------------------------------------------------------------------
 
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void fps_update_kernel(const typename Elem<DT>::T* __restrict__ q_new, int T,
-                                                             typename Elem<DT>::T* __restrict__ qbuf,
-                                                             int32_t* __restrict__ qcount, int C, int M,
-                                                             int32_t* __restrict__ ws_words) {
-  using F = Fps<DT, D, NW>;
-  using ET = typename F::ET;
-  constexpr int NT = F::NT;
-  constexpr int kU = F::kU;
+template <int DT, int D, int NT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void fps_update_kernel(
+    const typename Elem<DT>::T* __restrict__ q_new, int T, typename Elem<DT>::T* __restrict__ qbuf,
+    int32_t* __restrict__ qcount, int C, int M, int32_t* __restrict__ ws_words) {
+  using ET = typename Elem<DT>::T;
+  constexpr int kRowBytes = D * Elem<DT>::kBytes;
+  constexpr int kU = kRowBytes / 16;
+  constexpr int cap = 32 * NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int lane = fps_lane();
   ET* buf = qbuf + (size_t)head * C * D;
   const ET* qn = q_new + (size_t)head * T * D;
   const int c0 = qcount[head];
   if (c0 < 0 || c0 >= C) {
-    if (tid == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
+    if (lane == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
     return;
   }
   if (c0 + T < C) {  // no shrink in this call: plain append
-    copy16(buf + (size_t)c0 * D, qn, T * F::kRowBytes, tid, NT);
-    if (tid == 0) qcount[head] = c0 + T;
+    copy16(buf + (size_t)c0 * D, qn, T * kRowBytes, lane, 64);
+    if (lane == 0) qcount[head] = c0 + T;
     return;
   }
-  constexpr int cpad = F::kMaxRows;  // rows [C, cpad) are readable padding, [cpad, cpad + M) the reorder area
-  FpsSmem s = fps_carve<DT, D, NW>(smem, cpad + M);
-  auto load_rows = [&](int dst_row, const ET* src, int nrows) {
-    for (int u = tid; u < nrows * kU; u += NT) {
-      const int r = u / kU, q = u % kU;
-      reinterpret_cast<uint4*>(s.rows + (size_t)(dst_row + r) * F::kRowStride)[q] =
-          reinterpret_cast<const uint4*>(src + (size_t)r * D)[q];
-    }
-  };
-  load_rows(0, buf, c0);
-  int c = c0;
-  int t = 0;
+  FpsLds s = fps_carve<DT, D>(smem, cap, M);
+  const FpsRows<DT, D> src{buf, qn, s.map, C};
+  for (int r = lane; r < c0; r += 64) s.map[r] = r;
+  int c = c0, t = 0, nlast = 0;
   while (t < T) {
     const int take = (T - t) < (C - c) ? (T - t) : (C - c);
-    load_rows(c, qn + (size_t)t * D, take);
+    for (int u = lane; u < take; u += 64) s.map[c + u] = C + t + u;
     c += take;
     t += take;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     if (c == C) {
-      const int n = fps_core<DT, D, NW>(s, C, M);
-      for (int u = tid; u < n * kU; u += NT) {
-        const int r = u / kU, q = u % kU;
-        reinterpret_cast<uint4*>(s.rows + (size_t)(cpad + r) * F::kRowStride)[q] =
-            reinterpret_cast<const uint4*>(s.rows + (size_t)s.picks[r] * F::kRowStride)[q];
+      const int np = fps_wave<DT, D, NT>(src, s, C, M);
+      // the buffer becomes its picks, in pick order
+      constexpr int kQ = (cap + 63) / 64;
+      int nm[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) nm[q] = s.map[s.picks[min(lane + 64 * q, np - 1)]];
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int i = lane + 64 * q;
+        if (i < np) s.map[i] = nm[q];
       }
-      __syncthreads();
-      for (int u = tid; u < n * kU; u += NT) {
-        const int r = u / kU, q = u % kU;
-        reinterpret_cast<uint4*>(s.rows + (size_t)r * F::kRowStride)[q] =
-            reinterpret_cast<const uint4*>(s.rows + (size_t)(cpad + r) * F::kRowStride)[q];
-      }
-      __syncthreads();
-      c = n;
+      __builtin_amdgcn_wave_barrier();
+      c = np;
+      nlast = np;
     }
   }
-  for (int u = tid; u < c * kU; u += NT) {
-    const int r = u / kU, q = u % kU;
-    reinterpret_cast<uint4*>(buf + (size_t)r * D)[q] =
-        reinterpret_cast<const uint4*>(s.rows + (size_t)r * F::kRowStride)[q];
+  // write-back: the retained picks may be rows of the entry buffer, so they
+  // are staged in LDS before any row of the buffer is overwritten; the rows
+  // after them are the last arrivals of this call, contiguous in q_new
+  uint4* stage = reinterpret_cast<uint4*>(s.stage);
+  uint4* bufu = reinterpret_cast<uint4*>(buf);
+  copy_units(nlast * kU, [&](int u) { return reinterpret_cast<const uint4*>(src.row(u / kU))[u % kU]; },
+             [&](int u, uint4 v) { stage[u] = v; });
+  __builtin_amdgcn_wave_barrier();
+  copy_units(nlast * kU, [&](int u) { return stage[u]; }, [&](int u, uint4 v) { bufu[u] = v; });
+  if (c > nlast) {
+    const uint4* tail = reinterpret_cast<const uint4*>(src.row(nlast));
+    uint4* dst = bufu + (size_t)nlast * kU;
+    copy_units((c - nlast) * kU, [&](int u) { return tail[u]; }, [&](int u, uint4 v) { dst[u] = v; });
   }
-  if (tid == 0) qcount[head] = c;
+  if (lane == 0) qcount[head] = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -577,33 +660,69 @@ __global__ void rope_table_kernel(const int32_t* __restrict__ recent_pos, const 
 // recent queries (rotated to their own positions)
 // ---------------------------------------------------------------------------
 
-template <int DT, int D>
-__device__ inline void rotate_store(const typename Elem<DT>::T* x, float2 cs, int i, typename Elem<DT>::T* y) {
+// Rotates `nrows` rows into dst rows [0, nrows): row r comes from row_of(r)
+// (always a readable row) and is present when ok_of(r) (absent rows are
+// written as zeros); its (cos, sin) pairs start at cs_of(r).  A lane takes
+// one 16-byte chunk of the first half of a row and the matching chunk of the
+// second half; all loads of a pass go out before its stores.
+template <int DT, int D, typename RowF, typename OkF, typename CsF>
+__device__ inline void rotate_rows(int nrows, RowF row_of, OkF ok_of, CsF cs_of, typename Elem<DT>::T* dst) {
+  using ET = typename Elem<DT>::T;
   using E = Elem<DT>;
   constexpr int H = D / 2;
-  // binary64 products of a storage value and a binary32 cos/sin are exact,
-  // so each output is the correctly rounded binary64 value of the exact
-  // rotation, rounded once more to the storage type
-  const double x0 = E::to_f64(x[i]);
-  const double x1 = E::to_f64(x[i + H]);
-  const double c = (double)cs.x, s = (double)cs.y;
-  y[i] = E::from_f64(x0 * c - x1 * s);
-  y[i + H] = E::from_f64(x1 * c + x0 * s);
+  constexpr int kPer = 16 / E::kBytes;      // elements per chunk
+  constexpr int kLanes = H / kPer;          // lanes per row
+  constexpr int kRows = 64 / kLanes;        // rows per pass
+  const int lane = fps_lane();
+  const int q = lane % kLanes;
+  for (int r0 = 0; r0 < nrows; r0 += kRows) {
+    const int r = min(r0 + lane / kLanes, nrows - 1);
+    const ET* x = row_of(r);
+    const float2* cs = cs_of(r) + q * kPer;
+    const uint4 lo = *reinterpret_cast<const uint4*>(x + q * kPer);
+    const uint4 hi = *reinterpret_cast<const uint4*>(x + H + q * kPer);
+    float4 c4[kPer / 2];
+#pragma unroll
+    for (int k = 0; k < kPer / 2; ++k) c4[k] = reinterpret_cast<const float4*>(cs)[k];
+    const bool ok = ok_of(r);
+    uint4 ylo = make_uint4(0u, 0u, 0u, 0u), yhi = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) {
+      const ET* a = reinterpret_cast<const ET*>(&lo);
+      const ET* b = reinterpret_cast<const ET*>(&hi);
+      ET* ya = reinterpret_cast<ET*>(&ylo);
+      ET* yb = reinterpret_cast<ET*>(&yhi);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        // binary64 products of a storage value and a binary32 cos/sin are
+        // exact, so each output is the correctly rounded binary64 value of
+        // the exact rotation, rounded once more to the storage type
+        const float4 cc = c4[e >> 1];
+        const double c = (double)((e & 1) ? cc.z : cc.x), sn = (double)((e & 1) ? cc.w : cc.y);
+        const double xa = E::to_f64(a[e]), xb = E::to_f64(b[e]);
+        ya[e] = E::from_f64(xa * c - xb * sn);
+        yb[e] = E::from_f64(xb * c + xa * sn);
+      }
+    }
+    if (r0 + lane / kLanes < nrows) {
+      ET* y = dst + (size_t)r * D;
+      *reinterpret_cast<uint4*>(y + q * kPer) = ylo;
+      *reinterpret_cast<uint4*>(y + H + q * kPer) = yhi;
+    }
+  }
 }
 
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void obs_build_kernel(
+template <int DT, int D, int NTMAX>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void obs_build_kernel(
     const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
     const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid,
     int Hq, int Hkv, int RP, int32_t* __restrict__ ws_words) {
-  using F = Fps<DT, D, NW>;
-  using ET = typename F::ET;
-  constexpr int NT = F::NT;
+  using ET = typename Elem<DT>::T;
   constexpr int H = D / 2;
+  constexpr int cap = 32 * NTMAX;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int lane = fps_lane();
   const int n = head / Hq;
   const int gq = head % Hq;
   const int G = Hq / Hkv;
@@ -616,95 +735,81 @@ __global__ __launch_bounds__(64 * NW, 2) void obs_build_kernel(
   const float2* tab_n = tab + (size_t)n * (R + 1) * H;
 
   // recent queries at their own positions
-  for (int e = tid; e < R * H; e += NT) {
-    const int r = e / H, i = e % H;
-    ET* y = obs_u + (size_t)(rowbase + r) * D;
-    if (recent_pos[(size_t)n * R + r] >= 0) {
-      rotate_store<DT, D>(recent + ((size_t)head * R + r) * D, tab_n[r * H + i], i, y);
-    } else {
-      y[i] = ET(0);
-      y[i + H] = ET(0);
-    }
-  }
-  if (tid < R) val_u[rowbase + tid] = recent_pos[(size_t)n * R + tid] >= 0 ? 1 : 0;
+  const int32_t* rpos_n = recent_pos + (size_t)n * R;
+  rotate_rows<DT, D>(
+      R, [&](int r) -> const ET* { return recent + ((size_t)head * R + r) * D; },
+      [&](int r) { return rpos_n[r] >= 0; }, [&](int r) { return tab_n + r * H; }, obs_u + (size_t)rowbase * D);
+  for (int r = lane; r < R; r += 64) val_u[rowbase + r] = recent_pos[(size_t)n * R + r] >= 0 ? 1 : 0;
 
   // beacons: FPS over the live buffer
   int c = qcount[head];
   if (c < 0 || c >= C) {
-    if (tid == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
+    if (lane == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
     c = 0;
   }
   const int want = nb < c ? nb : c;
-  constexpr int cpad = F::kMaxRows;
-  FpsSmem s = fps_carve<DT, D, NW>(smem, cpad);
+  FpsLds s = fps_carve<DT, D>(smem, cap, 0);
+  const FpsRows<DT, D> src{qbuf + (size_t)head * C * D, nullptr, s.map, C};
   int kk = 0;
   if (want > 0) {
-    const ET* buf = qbuf + (size_t)head * C * D;
-    for (int u = tid; u < c * F::kU; u += NT) {
-      const int r = u / F::kU, q = u % F::kU;
-      reinterpret_cast<uint4*>(s.rows + (size_t)r * F::kRowStride)[q] =
-          reinterpret_cast<const uint4*>(buf + (size_t)r * D)[q];
-    }
-    __syncthreads();
-    kk = fps_core<DT, D, NW>(s, c, want);
+    for (int r = lane; r < c; r += 64) s.map[r] = r;
+    __builtin_amdgcn_wave_barrier();
+    kk = fps_dispatch<DT, D, NTMAX>(src, s, c, want);
   }
-  for (int e = tid; e < nb * H; e += NT) {
-    const int b = e / H, i = e % H;
-    ET* y = obs_u + (size_t)(rowbase + R + b) * D;
-    if (b < kk) {
-      rotate_store<DT, D>(fps_row<DT, D, NW>(s, s.picks[b]), tab_n[R * H + i], i, y);
-    } else {
-      y[i] = ET(0);
-      y[i + H] = ET(0);
-    }
-  }
-  if (tid < nb) val_u[rowbase + R + tid] = tid < kk ? 1 : 0;
+  rotate_rows<DT, D>(
+      nb, [&](int b) -> const ET* { return b < kk ? src.row(s.picks[b]) : src.buf; },
+      [&](int b) { return b < kk; }, [&](int) { return tab_n + R * H; }, obs_u + (size_t)(rowbase + R) * D);
+  for (int b = lane; b < nb; b += 64) val_u[rowbase + R + b] = b < kk ? 1 : 0;
 
   // padding rows of the unit (written once, by the last query head of the group)
   if (gl == G - 1) {
     const int first = G * (R + nb);
-    for (int e = tid; e < (RP - first) * D; e += NT) obs_u[(size_t)first * D + e] = ET(0);
-    for (int r = first + tid; r < RP; r += NT) val_u[r] = 0;
+    for (int e = lane; e < (RP - first) * D; e += 64) obs_u[(size_t)first * D + e] = ET(0);
+    for (int r = first + lane; r < RP; r += 64) val_u[r] = 0;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launchers (block size from the capacity: 32 rows per wave)
+// Host-side launchers (tile capacity from the buffer capacity)
 // ---------------------------------------------------------------------------
 
-template <int DT, int D, int NW>
-static hipError_t launch_fps_update_nw(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M, int heads,
-                                       int32_t* ws_words, hipStream_t st) {
+template <int DT, int D, int NT>
+static hipError_t launch_fps_update_nt(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M,
+                                       int heads, int32_t* ws_words, hipStream_t st) {
   using ET = typename Elem<DT>::T;
-  const int cpad = Fps<DT, D, NW>::kMaxRows;
-  const size_t smem = fps_smem_bytes<DT, D, NW>(cpad + M);
-  auto kern = fps_update_kernel<DT, D, NW>;
+  const size_t smem = fps_lds_bytes<DT, D>(32 * NT, M);
+  auto kern = fps_update_kernel<DT, D, NT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(heads), dim3(64 * NW), smem, st, (const ET*)q_new, T, (ET*)qbuf, qcount, C, M,
+  hipLaunchKernelGGL(kern, dim3(heads), dim3(64), smem, st, (const ET*)q_new, T, (ET*)qbuf, qcount, C, M,
                      ws_words);
   return hipGetLastError();
 }
 
+// one instantiation per 32-row tile count of the capacity (5 .. 8 tiles share
+// the 8-tile kernel)
 template <int DT, int D>
 hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M, int heads,
                              int32_t* ws_words, hipStream_t st) {
-  if (C <= 64) return launch_fps_update_nw<DT, D, 2>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
-  if (C <= 128) return launch_fps_update_nw<DT, D, 4>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
-  return launch_fps_update_nw<DT, D, 8>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+  switch ((C + 31) / 32) {
+    case 1: return launch_fps_update_nt<DT, D, 1>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+    case 2: return launch_fps_update_nt<DT, D, 2>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+    case 3: return launch_fps_update_nt<DT, D, 3>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+    case 4: return launch_fps_update_nt<DT, D, 4>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+    default: return launch_fps_update_nt<DT, D, 8>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+  }
 }
 
-template <int DT, int D, int NW>
-static hipError_t launch_obs_nw(const void* qbuf, const int32_t* qcount, int C, int nb, const void* recent,
+template <int DT, int D, int NTMAX>
+static hipError_t launch_obs_nt(const void* qbuf, const int32_t* qcount, int C, int nb, const void* recent,
                                 const int32_t* recent_pos, int R, float2* tab, void* obs, int32_t* obs_valid, int N,
                                 int Hq, int Hkv, int RP, int32_t* ws_words, hipStream_t st) {
   using ET = typename Elem<DT>::T;
-  const int cpad = Fps<DT, D, NW>::kMaxRows;
-  const size_t smem = fps_smem_bytes<DT, D, NW>(cpad);
-  auto kern = obs_build_kernel<DT, D, NW>;
+  const size_t smem = fps_lds_bytes<DT, D>(32 * NTMAX, 0);
+  auto kern = obs_build_kernel<DT, D, NTMAX>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(N * Hq), dim3(64 * NW), smem, st, (const ET*)qbuf, qcount, C, nb, (const ET*)recent,
+  hipLaunchKernelGGL(kern, dim3(N * Hq), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, (const ET*)recent,
                      recent_pos, R, (const float2*)tab, (ET*)obs, obs_valid, Hq, Hkv, RP, ws_words);
   return hipGetLastError();
 }
@@ -718,12 +823,12 @@ hipError_t launch_obs_build(const void* qbuf, const int32_t* qcount, int C, int 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (C <= 64)
-    return launch_obs_nw<DT, D, 2>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
+    return launch_obs_nt<DT, D, 2>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
                                    ws_words, st);
   if (C <= 128)
-    return launch_obs_nw<DT, D, 4>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
+    return launch_obs_nt<DT, D, 4>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
                                    ws_words, st);
-  return launch_obs_nw<DT, D, 8>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
+  return launch_obs_nt<DT, D, 8>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
                                  ws_words, st);
 }
 
