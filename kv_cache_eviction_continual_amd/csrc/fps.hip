@@ -32,10 +32,10 @@
 //     the decisions use the wider bound eps = 4 (d + 8) u, and the mean
 //     cosines eps + 4 (c + 8) u (c-term fp32 sum and one division more);
 //   * candidates are compared on keys (order-preserving fp32 bits, low 8
-//     bits replaced by the row index).  When the runner-up is not more than
-//     2 eps above the best, every candidate inside that window is evaluated
-//     from the rows in binary64 and the lowest value wins, ties to the lower
-//     row;
+//     bits replaced by the row index).  Every candidate whose fp32 value is
+//     within 2 eps of the best key's bucket could hold the true minimum; when
+//     there is more than one, they are evaluated from the rows in binary64
+//     and the lowest value wins, ties to the lower row;
 //   * a row whose squared norm leaves [1e-30, 1e36], or a nonzero row whose
 //     fp32 squared norm underflows to 0, sends the whole call to binary64
 //     rounds over every candidate.
@@ -74,6 +74,9 @@ struct FpsFrag<BKV_BF16, D> {
     return *reinterpret_cast<const uint4*>(row + 16 * ks + 8 * h);
   }
   __device__ static inline V zero() { return make_uint4(0u, 0u, 0u, 0u); }
+  __device__ static inline void store(T* row, int ks, int h, V v) {
+    *reinterpret_cast<uint4*>(row + 16 * ks + 8 * h) = v;
+  }
   __device__ static inline fps_floatx16 mma(V a, V b, fps_floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(fps_bf16x8, a),
                                                   __builtin_bit_cast(fps_bf16x8, b), c, 0, 0, 0);
@@ -96,6 +99,7 @@ struct FpsFrag<BKV_F32, D> {
   static constexpr int kSteps = D / 2;
   __device__ static inline V load(const T* row, int ks, int h) { return row[2 * ks + h]; }
   __device__ static inline V zero() { return 0.0f; }
+  __device__ static inline void store(T* row, int ks, int h, V v) { row[2 * ks + h] = v; }
   __device__ static inline fps_floatx16 mma(V a, V b, fps_floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
@@ -127,6 +131,7 @@ struct FpsLds {
   float* inv32;          // [cap] fp32 1 / |x| (0 for rows past the count)
   int* map;              // [cap]
   int* picks;            // [cap]
+  int* pos;              // [cap] position of a row among the picks, -1 if not picked
 };
 
 template <int DT, int D>
@@ -138,7 +143,7 @@ __host__ __device__ constexpr size_t fps_gram_bytes(int cap, int M) {
 
 template <int DT, int D>
 __host__ __device__ constexpr size_t fps_lds_bytes(int cap, int M) {
-  return fps_gram_bytes<DT, D>(cap, M) + (size_t)cap * (4 + 4 + 4);
+  return fps_gram_bytes<DT, D>(cap, M) + (size_t)cap * (4 + 4 + 4 + 4);
 }
 
 template <int DT, int D>
@@ -150,6 +155,7 @@ __device__ inline FpsLds fps_carve(unsigned char* smem, int cap, int M) {
   s.inv32 = reinterpret_cast<float*>(smem + gb);
   s.map = reinterpret_cast<int*>(smem + gb + (size_t)cap * 4);
   s.picks = reinterpret_cast<int*>(smem + gb + (size_t)cap * 8);
+  s.pos = reinterpret_cast<int*>(smem + gb + (size_t)cap * 12);
   return s;
 }
 
@@ -175,11 +181,8 @@ __device__ inline uint32_t cand_key(float v, int row) {
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return (ord & 0xFFFFFF00u) | (uint32_t)row;
 }
-// Lowest value of a key's bucket, and the lowest value of the next bucket.
-__device__ inline float key_lo(uint32_t k) {
-  const uint32_t ord = k & 0xFFFFFF00u;
-  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
+// Lowest value of the bucket after a key's bucket (an upper bound of every
+// value in the key's bucket).
 __device__ inline float key_hi(uint32_t k) {
   const uint32_t ord = (k | 0xFFu) + 1u;
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
@@ -190,30 +193,18 @@ __device__ inline uint32_t row_ror_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x120 + N, 0xF, 0xF, false);
 }
 
-// Merge two (smallest, second smallest) key pairs of disjoint sets.
-__device__ inline void merge2(uint32_t& a1, uint32_t& a2, uint32_t b1, uint32_t b2) {
-  const uint32_t lo = a1 < b1 ? a1 : b1;
-  const uint32_t hi = a1 < b1 ? b1 : a1;
-  const uint32_t m2 = a2 < b2 ? a2 : b2;
-  a1 = lo;
-  a2 = hi < m2 ? hi : m2;
-}
-
-// Two smallest keys of the wave (each lane brings its own pair): rows of 16
-// lanes reduce by DPP rotation, the four rows through scalar lane reads.
-// The results are wave-uniform.
-__device__ inline void wave_min2(uint32_t a1, uint32_t a2, uint32_t& k1, uint32_t& k2) {
-  merge2(a1, a2, row_ror_u<8>(a1), row_ror_u<8>(a2));
-  merge2(a1, a2, row_ror_u<4>(a1), row_ror_u<4>(a2));
-  merge2(a1, a2, row_ror_u<2>(a1), row_ror_u<2>(a2));
-  merge2(a1, a2, row_ror_u<1>(a1), row_ror_u<1>(a2));
-  uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)a1, 0);
-  uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)a2, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16)
-    merge2(w1, w2, (uint32_t)__builtin_amdgcn_readlane((int)a1, r), (uint32_t)__builtin_amdgcn_readlane((int)a2, r));
-  k1 = w1;
-  k2 = w2;
+// Smallest key of the wave: rows of 16 lanes reduce by DPP rotation, the
+// four rows through scalar lane reads.  The result is wave-uniform.
+__device__ inline uint32_t wave_min_key(uint32_t a) {
+  a = min(a, row_ror_u<8>(a));
+  a = min(a, row_ror_u<4>(a));
+  a = min(a, row_ror_u<2>(a));
+  a = min(a, row_ror_u<1>(a));
+  uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)a, 0);
+  w = min(w, (uint32_t)__builtin_amdgcn_readlane((int)a, 16));
+  w = min(w, (uint32_t)__builtin_amdgcn_readlane((int)a, 32));
+  w = min(w, (uint32_t)__builtin_amdgcn_readlane((int)a, 48));
+  return w;
 }
 
 // ---------------------------------------------------------------------------
@@ -306,10 +297,44 @@ __device__ __attribute__((always_inline)) int fps_exact_argmin(const FpsRows<DT,
 // FPS of one head by one wavefront
 // ---------------------------------------------------------------------------
 
-// Writes the FPS picks of rows [0, c) (c <= 32 NT) to s.picks, min(k, c) of
-// them, and returns the count.  Every lane of the wave must call it.
+// Whether fps_wave keeps every row's matrix-core fragments in registers (at
+// most 128 of them per lane) rather than reloading them per use.
 template <int DT, int D, int NT>
-__device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src, const FpsLds& s, int c, int k) {
+__host__ __device__ constexpr bool fps_holds() {
+  return NT * FpsFrag<DT, D>::kSteps * (int)(sizeof(typename FpsFrag<DT, D>::V) / 4) <= 128;
+}
+
+// Rows of the picks written to wb + i d (pick i) straight from the matrix-core
+// fragments of their owner lanes (lane (n, h) holds half of row 32 t + n of
+// every tile t).  No-op when wb is null.
+template <int DT, int D, int NT>
+__device__ __forceinline__ void fps_write_picks(const FpsLds& s, int kk,
+                                                const typename FpsFrag<DT, D>::V (&fr)[NT][FpsFrag<DT, D>::kSteps],
+                                                typename Elem<DT>::T* wb, int lane) {
+  using FR = FpsFrag<DT, D>;
+  if (wb == nullptr) return;
+  const int n = lane & 31, h = lane >> 5;
+  for (int r = lane; r < 32 * NT; r += 64) s.pos[r] = -1;
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < kk; i += 64) s.pos[s.picks[i]] = i;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int i = s.pos[32 * t + n];
+    if (i >= 0) {
+#pragma unroll
+      for (int ks = 0; ks < FR::kSteps; ++ks) FR::store(wb + (size_t)i * D, ks, h, fr[t][ks]);
+    }
+  }
+}
+
+// Writes the FPS picks of rows [0, c) (c <= 32 NT) to s.picks, min(k, c) of
+// them, and returns the count.  When `wb` is given and the fragments are held
+// in registers, also writes pick i's row to wb + i d straight from them.
+// Every lane of the wave must call it.
+template <int DT, int D, int NT>
+__device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src, const FpsLds& s, int c, int k,
+                                                       typename Elem<DT>::T* wb = nullptr) {
   using FR = FpsFrag<DT, D>;
   using V = typename FR::V;
   using T = typename Elem<DT>::T;
@@ -328,7 +353,7 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
 
   // 1. matrix-core fragments of every row (rows past the count are zero),
   // held in registers when they fit in 128 of them, else reloaded per use
-  constexpr bool kHold = NT * KS * (int)(sizeof(V) / 4) <= 128;
+  constexpr bool kHold = fps_holds<DT, D, NT>();
   const T* rowp[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) rowp[t] = 32 * t + n < c ? src.row(32 * t + n) : nullptr;
@@ -394,6 +419,7 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
       if (lane == 0) s.picks[t] = pick;
       __builtin_amdgcn_wave_barrier();
     }
+    if constexpr (kHold) fps_write_picks<DT, D, NT>(s, kk, fr, wb, lane);
     return kk;
   }
 
@@ -401,6 +427,7 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
   // chain is straight-line code): column sums of G_ij / |x_i| for the mean
   // cosines, and the strict lower triangle into LDS
   fps_float8 cs = {};
+  const int pad = tri(32 * NT) + lane;  // per-lane slot in the LDS pad past the triangle
 #pragma unroll
   for (int tr = 0; tr < NT; ++tr) {
     fps_floatx16 acc[NT];
@@ -430,7 +457,11 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
       for (int tc = 0; tc < NT; ++tc) {
         const float g = acc[tc][r];
         cs[tc] = fmaf(g, w, cs[tc]);
-        if (tr > tc || (tr == tc && i0 + 4 * h > 32 * tc + n)) s.gram[rowoff + 32 * tc] = g;
+        if (tr > tc) {
+          s.gram[rowoff + 32 * tc] = g;
+        } else if (tr == tc) {  // strict lower half of a diagonal tile; the rest goes to a pad slot
+          s.gram[i0 + 4 * h > 32 * tc + n ? rowoff + 32 * tc : pad] = g;
+        }
       }
     }
   }
@@ -444,29 +475,34 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
 #pragma unroll
   for (int w = 0; w < SL; ++w) {
     invj[w] = (2 * w + 1 < NT) ? (h ? invr[2 * w + 1] : invr[2 * w]) : invr[2 * w];
-    trij[w] = tri(64 * w + lane);
+    trij[w] = tri(min(64 * w + lane, c - 1));
   }
 
   // 4. start: lowest mean cosine
   int pick;
   {
     float mu[SL];
-    uint32_t a1 = 0xFFFFFFFFu, a2 = 0xFFFFFFFFu;
+    uint32_t a = 0xFFFFFFFFu;
 #pragma unroll
     for (int w = 0; w < SL; ++w) {
       const int j = 64 * w + lane;
       const float sj = (2 * w + 1 < NT) ? (h ? S[2 * w + 1] : S[2 * w]) : S[2 * w];
       mu[w] = j < c ? (sj * invj[w]) / (float)c : finf;
-      merge2(a1, a2, j < c ? cand_key(mu[w], j) : 0xFFFFFFFFu, 0xFFFFFFFFu);
+      a = min(a, j < c ? cand_key(mu[w], j) : 0xFFFFFFFFu);
     }
-    uint32_t k1, k2;
-    wave_min2(a1, a2, k1, k2);
+    const uint32_t k1 = wave_min_key(a);
+    // every candidate within 2 eps of the best one's bucket could be the
+    // true minimum: decide in binary64 when there is more than one
     const float eps_mu = kEps + 4.0f * (float)(c + 8) * kFpsU;
     const float hi1 = key_hi(k1) + 2.0f * eps_mu;
-    if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
-      uint64_t inmask[SL];
+    uint64_t inmask[SL];
+    int inwin = 0;
 #pragma unroll
-      for (int w = 0; w < SL; ++w) inmask[w] = __ballot(64 * w + lane < c && mu[w] <= hi1);
+    for (int w = 0; w < SL; ++w) {
+      inmask[w] = __ballot(64 * w + lane < c && mu[w] <= hi1);
+      inwin += __builtin_popcountll(inmask[w]);
+    }
+    if (inwin > 1) {
       pick = fps_exact_argmin<DT, D, SL>(src, s, inmask, c, 0, true);
     } else {
       pick = (int)(k1 & 0xFFu);
@@ -487,23 +523,32 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
     const int p = pick;
     const float inv_p = s.inv32[p];
     const int tp = tri(p);
-    uint32_t a1 = 0xFFFFFFFFu, a2 = 0xFFFFFFFFu;
+    // every slot reads (rows past the count read row c - 1 and are ignored),
+    // so the reads of all slots go out together
+    float g[SL];
+#pragma unroll
+    for (int w = 0; w < SL; ++w) {
+      const int jj = min(64 * w + lane, c - 1);
+      g[w] = s.gram[jj < p ? tp + jj : trij[w] + p];
+    }
+    uint32_t a = 0xFFFFFFFFu;
 #pragma unroll
     for (int w = 0; w < SL; ++w) {
       const int j = 64 * w + lane;
-      if (j < c) {
-        const float g = s.gram[j < p ? tp + j : trij[w] + p];
-        mt[w] = fmaxf(mt[w], (g * invj[w]) * inv_p);
-        merge2(a1, a2, picked[w] ? 0xFFFFFFFFu : cand_key(mt[w], j), 0xFFFFFFFFu);
-      }
+      const bool live = j < c && !picked[w];
+      mt[w] = fmaxf(mt[w], (g[w] * invj[w]) * inv_p);
+      a = min(a, live ? cand_key(mt[w], j) : 0xFFFFFFFFu);
     }
-    uint32_t k1, k2;
-    wave_min2(a1, a2, k1, k2);
+    const uint32_t k1 = wave_min_key(a);
     const float hi1 = key_hi(k1) + eps2;
-    if (k2 != 0xFFFFFFFFu && key_lo(k2) <= hi1) {
-      uint64_t inmask[SL];
+    uint64_t inmask[SL];
+    int inwin = 0;
 #pragma unroll
-      for (int w = 0; w < SL; ++w) inmask[w] = __ballot(64 * w + lane < c && !picked[w] && mt[w] <= hi1);
+    for (int w = 0; w < SL; ++w) {
+      inmask[w] = __ballot(64 * w + lane < c && !picked[w] && mt[w] <= hi1);
+      inwin += __builtin_popcountll(inmask[w]);
+    }
+    if (inwin > 1) {
       __builtin_amdgcn_wave_barrier();
       pick = fps_exact_argmin<DT, D, SL>(src, s, inmask, c, t, false);
     } else {
@@ -514,6 +559,7 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
     if (lane == 0) s.picks[t] = pick;
   }
   __builtin_amdgcn_wave_barrier();
+  if constexpr (kHold) fps_write_picks<DT, D, NT>(s, kk, fr, wb, lane);
   return kk;
 }
 
@@ -588,6 +634,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   const FpsRows<DT, D> src{buf, qn, s.map, C};
   for (int r = lane; r < c0; r += 64) s.map[r] = r;
   int c = c0, t = 0, nlast = 0;
+  bool written = false;
   while (t < T) {
     const int take = (T - t) < (C - c) ? (T - t) : (C - c);
     for (int u = lane; u < take; u += 64) s.map[c + u] = C + t + u;
@@ -595,32 +642,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     t += take;
     __builtin_amdgcn_wave_barrier();
     if (c == C) {
-      const int np = fps_wave<DT, D, NT>(src, s, C, M);
-      // the buffer becomes its picks, in pick order
-      constexpr int kQ = (cap + 63) / 64;
-      int nm[kQ];
+      // the last shrink of the call (no refill from the remaining arrivals)
+      // writes its picks to the buffer from registers; an earlier one turns
+      // the buffer into its picks through the row map
+      const bool direct = fps_holds<DT, D, NT>() && M + (T - t) < C;
+      const int np = fps_wave<DT, D, NT>(src, s, C, M, direct ? buf : nullptr);
+      if (direct) {
+        written = true;
+      } else {
+        constexpr int kQ = (cap + 63) / 64;
+        int nm[kQ];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) nm[q] = s.map[s.picks[min(lane + 64 * q, np - 1)]];
-      __builtin_amdgcn_wave_barrier();
+        for (int q = 0; q < kQ; ++q) nm[q] = s.map[s.picks[min(lane + 64 * q, np - 1)]];
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const int i = lane + 64 * q;
-        if (i < np) s.map[i] = nm[q];
+        for (int q = 0; q < kQ; ++q) {
+          const int i = lane + 64 * q;
+          if (i < np) s.map[i] = nm[q];
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
       c = np;
       nlast = np;
     }
   }
-  // write-back: the retained picks may be rows of the entry buffer, so they
-  // are staged in LDS before any row of the buffer is overwritten; the rows
-  // after them are the last arrivals of this call, contiguous in q_new
-  uint4* stage = reinterpret_cast<uint4*>(s.stage);
   uint4* bufu = reinterpret_cast<uint4*>(buf);
-  copy_units(nlast * kU, [&](int u) { return reinterpret_cast<const uint4*>(src.row(u / kU))[u % kU]; },
-             [&](int u, uint4 v) { stage[u] = v; });
-  __builtin_amdgcn_wave_barrier();
-  copy_units(nlast * kU, [&](int u) { return stage[u]; }, [&](int u, uint4 v) { bufu[u] = v; });
+  if (!written) {
+    // the retained picks may be rows of the entry buffer, so they are staged
+    // in LDS before any row of the buffer is overwritten
+    uint4* stage = reinterpret_cast<uint4*>(s.stage);
+    copy_units(nlast * kU, [&](int u) { return reinterpret_cast<const uint4*>(src.row(u / kU))[u % kU]; },
+               [&](int u, uint4 v) { stage[u] = v; });
+    __builtin_amdgcn_wave_barrier();
+    copy_units(nlast * kU, [&](int u) { return stage[u]; }, [&](int u, uint4 v) { bufu[u] = v; });
+  }
+  // the rows after the picks are the last arrivals of the call, contiguous in q_new
   if (c > nlast) {
     const uint4* tail = reinterpret_cast<const uint4*>(src.row(nlast));
     uint4* dst = bufu + (size_t)nlast * kU;
