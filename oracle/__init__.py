@@ -67,6 +67,8 @@ def lib():
         L.orc_select.restype = I
         L.orc_compact.argtypes = [P, LONG, P, I]
         L.orc_compact.restype = None
+        L.orc_select_fill.argtypes = [P, P, I, I, I, P]
+        L.orc_select_fill.restype = I
         _lib = L
     return _lib
 
@@ -261,11 +263,27 @@ def select(scores: np.ndarray, L: int, B: int, W: int) -> np.ndarray:
 
 
 def compact(X: np.ndarray, kept: np.ndarray) -> None:
-    """In-place order-preserving gather of the rows of X [Lmax, d] (storage)."""
+    """In-place gather X[i] <- X_old[kept[i]] of the rows of X [Lmax, d]
+    (storage), or of the entries of a 1-D array (positions)."""
     assert X.flags["C_CONTIGUOUS"]
     k = np.ascontiguousarray(kept, dtype=np.int32)
-    row_bytes = X.shape[-1] * X.itemsize
+    row_bytes = (X.shape[-1] if X.ndim > 1 else 1) * X.itemsize
     lib().orc_compact(_ptr(X), row_bytes, _ptr(k), int(k.shape[0]))
+
+
+def select_fill(scores: np.ndarray, pos: np.ndarray, L: int, B: int, W: int) -> np.ndarray:
+    """Gather map of the hole-filling layout: the window is the W newest
+    positions, the other B-W rows the top scores (older position, then lower
+    row, first at ties); evicted rows of [0, B) take the kept rows of [B, L)
+    in ascending order.  kept[i] = pre-eviction row that row i holds."""
+    s = np.ascontiguousarray(scores[:L], dtype=np.float64)
+    p = np.ascontiguousarray(pos[:L], dtype=np.int64)
+    assert p.dtype.itemsize == ctypes.sizeof(ctypes.c_long)
+    kept = np.empty(max(min(L, B), 1), dtype=np.int32)
+    n = lib().orc_select_fill(_ptr(s), _ptr(p), L, B, W, _ptr(kept))
+    if n < 0:
+        raise ValueError("oracle select_fill rejected B=%d W=%d" % (B, W))
+    return kept[:n].copy()
 
 
 def evict(K, V, lens, scores_by_unit, B, W):

@@ -476,3 +476,86 @@ void orc_compact(void *X, long row_bytes, const int *kept, int n) {
   memcpy(x, old, (size_t)row_bytes * n);
   free(old);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Hole-filling layout (positions carried with the rows)                      */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  double score;
+  long pos;
+  int row;
+} placed_t;
+
+/* Newest first: position descending, then the lower row. */
+static int by_pos_desc_row_asc(const void *pa, const void *pb) {
+  const placed_t *a = (const placed_t *)pa, *b = (const placed_t *)pb;
+  if (a->pos > b->pos) return -1;
+  if (a->pos < b->pos) return 1;
+  return (a->row > b->row) - (a->row < b->row);
+}
+
+/* Highest score first, then the older position, then the lower row. */
+static int by_score_desc_pos_asc_row_asc(const void *pa, const void *pb) {
+  const placed_t *a = (const placed_t *)pa, *b = (const placed_t *)pb;
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+  if (a->pos < b->pos) return -1;
+  if (a->pos > b->pos) return 1;
+  return (a->row > b->row) - (a->row < b->row);
+}
+
+/*
+ * orc_select_fill: the kept set of one KV head when rows are not kept in
+ * position order, and the gather map that fills the evicted rows.
+ * [IK, 三]: keep I = TopK(score, B_KV); [AM, "Beacon queries anticipate what
+ * will be revisited"]: the recent sliding window is always kept.
+ *
+ * Readings: row j holds the token at position pos[j].  The window is the W
+ * newest tokens, i.e. the first W rows by (position descending, row
+ * ascending); the other B-W kept rows are the first ones of the remaining
+ * rows by (score descending, position ascending, row ascending).  With
+ * positions ascending in the row index this is exactly orc_select's kept set
+ * (window = last W rows, ties to the lower index).  Layout after eviction:
+ * the rows of [0, B) that are evicted ("holes", ascending) take, in order,
+ * the kept rows of [B, L) (ascending), so only those rows move.
+ *
+ * kept[i] (i < min(L, B)) receives the pre-eviction row that row i holds
+ * afterwards: i itself for a kept row below B, else the filling row.
+ * Returns min(L, B), or -1 if W > B, W < 0 or B < 0.
+ */
+int orc_select_fill(const double *scores, const long *pos, int L, int B, int W, int *kept) {
+  if (B < 0 || W < 0 || W > B || L < 0) return -1;
+  if (L <= B) {
+    for (int i = 0; i < L; ++i) kept[i] = i;
+    return L;
+  }
+  placed_t *v = (placed_t *)malloc(sizeof(placed_t) * L);
+  for (int j = 0; j < L; ++j) {
+    v[j].score = scores[j];
+    v[j].pos = pos[j];
+    v[j].row = j;
+  }
+  char *keep = (char *)calloc(L, 1);
+  /* the window: the W newest rows */
+  qsort(v, L, sizeof(placed_t), by_pos_desc_row_asc);
+  for (int i = 0; i < W; ++i) keep[v[i].row] = 1;
+  /* the others: top B-W of the rest */
+  int n = 0;
+  for (int i = W; i < L; ++i) v[n++] = v[i];
+  qsort(v, n, sizeof(placed_t), by_score_desc_pos_asc_row_asc);
+  for (int i = 0; i < B - W; ++i) keep[v[i].row] = 1;
+  /* pair the holes of [0, B) with the kept rows of [B, L), both ascending */
+  int next_src = B;
+  for (int i = 0; i < B; ++i) {
+    if (keep[i]) {
+      kept[i] = i;
+    } else {
+      while (!keep[next_src]) ++next_src;
+      kept[i] = next_src++;
+    }
+  }
+  free(v);
+  free(keep);
+  return B;
+}
