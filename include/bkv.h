@@ -191,6 +191,62 @@ int bkv_select_compact(const bkv_shape *shape, const float *scores, void *K, voi
                        int32_t *len, int32_t budget, int32_t window, int32_t *kept, void *ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Hole-filling layout.  The order-preserving compaction above moves every
+ * kept row after the first evicted one.  In this layout the rows need not be
+ * in position order: each row carries its token position, and eviction only
+ * moves the kept rows that lie at or beyond the budget into the evicted rows
+ * below it.  The kept set is the one bkv_select computes when the rows are
+ * in position order (same sources: [IK] 三, TopK of the scores; [AM], the
+ * recent window always kept), with the window and the tie order stated by
+ * position instead of by row.
+ *
+ * bkv_select_fill
+ *   scores [N][Hkv][Lmax]  non-negative finite floats, j < len[n] read
+ *   pos    [N][Hkv][Lmax]  int32 token position of each row, j < len[n] read;
+ *                          positions are expected to be distinct per (slot,
+ *                          KV head) (equal ones are ordered by row)
+ *   len    [N]             current lengths (read only)
+ *   budget, window         B_KV (window included) and W, 0 <= W <= B_KV <= Lmax
+ *   kept   [N][Hkv][B_KV]  output gather map: after compaction row i holds
+ *                          the pre-eviction row kept[i]
+ *
+ * If L <= B_KV every row is kept (kept[i] = i for i < L, -1 after).
+ * Otherwise the window is the W rows of highest position (ties: lower row)
+ * and the other B_KV - W kept rows are the highest scores among the rest
+ * (ties: lower position, then lower row).  The evicted rows of [0, B_KV),
+ * ascending, are paired with the kept rows of [B_KV, L), ascending:
+ * kept[i] = i for a kept row i < B_KV, else its partner.  Selection is exact
+ * on the binary32 scores.  Records the first evicted row below B_KV and the
+ * kept count in the workspace for bkv_compact_fill.
+ */
+int bkv_select_fill(const bkv_shape *shape, const float *scores, const int32_t *pos,
+                    const int32_t *len, int32_t budget, int32_t window, int32_t *kept, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bkv_compact_fill -- in-place hole filling.
+ *
+ *   K, V [N][Hkv][Lmax][d]  in/out; row i <- row kept[i] for every i below
+ *                           the kept count with kept[i] != i (bit copies);
+ *                           all other rows are left as they were
+ *   pos  [N][Hkv][Lmax]     in/out; moved with the rows
+ *   len  [N]                set to min(len, budget)
+ *   kept                    the output of bkv_select_fill with the same
+ *                           workspace
+ *
+ * Must follow bkv_select_fill on the same workspace, budget and stream.
+ * Adds the number of moved K and V rows to the statistic rows_moved.
+ */
+int bkv_compact_fill(const bkv_shape *shape, void *K, void *V, int32_t *pos, int32_t *len,
+                     int32_t budget, const int32_t *kept, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* bkv_select_fill followed by bkv_compact_fill. */
+int bkv_select_compact_fill(const bkv_shape *shape, const float *scores, void *K, void *V,
+                            int32_t *pos, int32_t *len, int32_t budget, int32_t window,
+                            int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Text for a bkv_status value (static string). */
 const char *bkv_status_string(int status);
 

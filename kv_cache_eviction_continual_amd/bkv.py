@@ -35,6 +35,9 @@ EXPORTS = (
     "bkv_select",
     "bkv_compact",
     "bkv_select_compact",
+    "bkv_select_fill",
+    "bkv_compact_fill",
+    "bkv_select_compact_fill",
     "bkv_status_string",
     "bkv_read_device_status",
     "bkv_reset_device_status",
@@ -88,6 +91,12 @@ def load() -> ctypes.CDLL:
     L.bkv_compact.restype = ctypes.c_int
     L.bkv_select_compact.argtypes = [SP, P, P, P, P, I32, I32, P, P, SZ, P]
     L.bkv_select_compact.restype = ctypes.c_int
+    L.bkv_select_fill.argtypes = [SP, P, P, P, I32, I32, P, P, SZ, P]
+    L.bkv_select_fill.restype = ctypes.c_int
+    L.bkv_compact_fill.argtypes = [SP, P, P, P, P, I32, P, P, SZ, P]
+    L.bkv_compact_fill.restype = ctypes.c_int
+    L.bkv_select_compact_fill.argtypes = [SP, P, P, P, P, P, I32, I32, P, P, SZ, P]
+    L.bkv_select_compact_fill.restype = ctypes.c_int
     L.bkv_status_string.argtypes = [ctypes.c_int]
     L.bkv_status_string.restype = ctypes.c_char_p
     L.bkv_read_device_status.argtypes = [P, ctypes.POINTER(I32), P]
@@ -171,6 +180,23 @@ def bkv_compact(shape: Shape, K, V, length, budget: int, kept, ws, stream=None) 
 def bkv_select_compact(shape: Shape, scores, K, V, length, budget: int, window: int, kept, ws, stream=None) -> None:
     _check(load().bkv_select_compact(ctypes.byref(shape), _ptr(scores), _ptr(K), _ptr(V), _ptr(length), budget,
                                      window, _ptr(kept), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_select_fill(shape: Shape, scores, pos, length, budget: int, window: int, kept, ws, stream=None) -> None:
+    _check(load().bkv_select_fill(ctypes.byref(shape), _ptr(scores), _ptr(pos), _ptr(length), budget, window,
+                                  _ptr(kept), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_compact_fill(shape: Shape, K, V, pos, length, budget: int, kept, ws, stream=None) -> None:
+    _check(load().bkv_compact_fill(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(pos), _ptr(length), budget,
+                                   _ptr(kept), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_select_compact_fill(shape: Shape, scores, K, V, pos, length, budget: int, window: int, kept, ws,
+                            stream=None) -> None:
+    _check(load().bkv_select_compact_fill(ctypes.byref(shape), _ptr(scores), _ptr(K), _ptr(V), _ptr(pos),
+                                          _ptr(length), budget, window, _ptr(kept), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bkv_status_string(status: int) -> str:

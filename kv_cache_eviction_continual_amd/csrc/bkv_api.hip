@@ -20,6 +20,10 @@ hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, 
                          hipStream_t);
 hipError_t launch_compact(void*, void*, const int32_t*, const int32_t*, int32_t*, int, int, int, int, int,
                           unsigned long long*, hipStream_t);
+hipError_t launch_select_fill(const float*, const int32_t*, const int32_t*, int, int, int, int, int, int32_t*,
+                              int32_t*, int32_t*, hipStream_t);
+hipError_t launch_compact_fill(void*, void*, int32_t*, const int32_t*, const int32_t*, int32_t*, int, int, int, int,
+                               int, unsigned long long*, hipStream_t);
 
 __global__ void zero_header_kernel(int32_t* w) {
   if (threadIdx.x < (int)(kHeaderBytes / 4)) w[threadIdx.x] = 0;
@@ -216,6 +220,45 @@ int bkv_select_compact(const bkv_shape* shape, const float* scores, void* K, voi
   int st = bkv_select(shape, scores, len, budget, window, kept, ws, ws_bytes, stream);
   if (st != BKV_OK) return st;
   return bkv_compact(shape, K, V, len, budget, kept, ws, ws_bytes, stream);
+}
+
+int bkv_select_fill(const bkv_shape* shape, const float* scores, const int32_t* pos, const int32_t* len,
+                    int32_t budget, int32_t window, int32_t* kept, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (window < 0 || budget < window || budget < 1 || budget > shape->max_len) return BKV_E_BUDGET;
+  if (!scores || !pos || !len || !kept) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, select_end(shape))) != BKV_OK) return st;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  int32_t* words = (int32_t*)ws;
+  int32_t* sel = (int32_t*)((unsigned char*)ws + kHeaderBytes);
+  return hip_status(
+      launch_select_fill(scores, pos, len, N, Hkv, shape->max_len, budget, window, kept, sel, words, stream));
+}
+
+int bkv_compact_fill(const bkv_shape* shape, void* K, void* V, int32_t* pos, int32_t* len, int32_t budget,
+                     const int32_t* kept, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (budget < 1 || budget > shape->max_len) return BKV_E_BUDGET;
+  if (!K || !V || !pos || !len || !kept) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, select_end(shape))) != BKV_OK) return st;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  const int32_t* sel = (const int32_t*)((unsigned char*)ws + kHeaderBytes);
+  unsigned long long* moved = (unsigned long long*)((unsigned char*)ws + 8);
+  const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
+  return hip_status(
+      launch_compact_fill(K, V, pos, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, stream));
+}
+
+int bkv_select_compact_fill(const bkv_shape* shape, const float* scores, void* K, void* V, int32_t* pos,
+                            int32_t* len, int32_t budget, int32_t window, int32_t* kept, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  int st = bkv_select_fill(shape, scores, pos, len, budget, window, kept, ws, ws_bytes, stream);
+  if (st != BKV_OK) return st;
+  return bkv_compact_fill(shape, K, V, pos, len, budget, kept, ws, ws_bytes, stream);
 }
 
 const char* bkv_status_string(int status) {

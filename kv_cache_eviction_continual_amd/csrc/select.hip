@@ -210,6 +210,282 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(unsigned char*
   }
 }
 
+// ---------------------------------------------------------------------------
+// Hole-filling layout
+//
+// Rows carry their token positions (pos[N][Hkv][Lmax]), so the cache need not
+// stay in position order.  select_fill_kernel keeps the W newest positions
+// (ties: the lower row) and the B - W highest scores of the other rows (ties:
+// the older position, then the lower row).  Each of these orders is found by
+// MSB-first radix selections over 32-bit keys that order like the quantity;
+// a further selection runs only when entries tie at a cut.  The evicted rows
+// of [0, B) ("holes") are then paired, in ascending order, with the kept rows
+// of [B, L) ("fillers"): kept[i] = i for a kept row below B, else its filler.
+// compact_fill_kernel moves only the fillers.  Destinations lie below B and
+// sources at or beyond it, so no copy reads a row that another one writes.
+
+constexpr int kFillChunk = 1024;  // fillers paired per sweep (LDS list)
+
+// Largest-first radix cut over the entries j in [0, n) for which key(j, k)
+// returns true (and sets their key k).  Finds the want-th largest key, for
+// 1 <= want <= the number of such entries; *take receives how many entries
+// equal to it the first `want` include, *n_eq how many entries equal it.
+// Every thread of the block must call it with the same arguments.
+template <class KeyFn>
+__device__ inline uint32_t radix_cut(KeyFn key, int n, int want, int* hist, int* scan_tmp, int* bcast, int* take,
+                                     int* n_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = want, eq = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += kSelThreads) {
+      uint32_t k;
+      if (key(j, k) && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    const int b = 255 - tid;  // thread t owns bucket 255 - t (kSelThreads == 256)
+    const int cnt = hist[b];
+    int total;
+    const int above = block_exclusive_scan(cnt, scan_tmp, &total);
+    if (above < remaining && remaining <= above + cnt) {
+      bcast[0] = b;
+      bcast[1] = remaining - above;
+      bcast[2] = cnt;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bcast[0] << shift;
+    mask |= 255u << shift;
+    remaining = bcast[1];
+    eq = bcast[2];
+    __syncthreads();
+  }
+  *take = remaining;
+  *n_eq = eq;
+  return prefix;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* __restrict__ scores,
+                                                                  const int32_t* __restrict__ pos,
+                                                                  const int32_t* __restrict__ len, int Hkv, int Lmax,
+                                                                  int B, int W, int32_t* __restrict__ kept,
+                                                                  int32_t* __restrict__ sel,
+                                                                  int32_t* __restrict__ ws_words) {
+  static_assert(kSelThreads == 256, "one radix bucket per thread");
+  __shared__ int hist[256];
+  __shared__ int scan_tmp[16];
+  __shared__ int bcast[4];
+  __shared__ int fillers[kFillChunk];
+  const size_t unit = blockIdx.x;
+  const int n = (int)(unit / Hkv);
+  const int tid = threadIdx.x;
+  const int L = len[n];
+  int32_t* kept_u = kept + unit * (size_t)B;
+  if (L < 0 || L > Lmax) {
+    if (tid == 0) {
+      set_status(ws_words, BKV_DEV_BAD_LEN);
+      sel[2 * unit] = 0;
+      sel[2 * unit + 1] = -1;  // compaction skips the unit
+    }
+    return;
+  }
+  if (L <= B) {  // nothing to evict
+    for (int i = tid; i < B; i += kSelThreads) kept_u[i] = i < L ? i : -1;
+    if (tid == 0) {
+      sel[2 * unit] = L;
+      sel[2 * unit + 1] = L;
+    }
+    return;
+  }
+  const uint32_t* u = reinterpret_cast<const uint32_t*>(scores + unit * (size_t)Lmax);
+  const int32_t* pp = pos + unit * (size_t)Lmax;
+  // signed positions -> unsigned keys in the same order
+  auto pkey = [pp](int j) { return (uint32_t)pp[j] ^ 0x80000000u; };
+
+  // the window: the W largest position keys, ties to the lower row
+  uint32_t wt = 0;
+  int wrow = 0x7fffffff;
+  if (W > 0) {
+    int take, neq;
+    wt = radix_cut([&](int j, uint32_t& k) { k = pkey(j); return true; }, L, W, hist, scan_tmp, bcast, &take, &neq);
+    if (take < neq) {  // equal positions straddle the cut: the lowest `take` rows of them
+      int t2, n2;
+      wrow = (int)~radix_cut([&](int j, uint32_t& k) { k = ~(uint32_t)j; return pkey(j) == wt; }, L, take, hist,
+                             scan_tmp, bcast, &t2, &n2);
+    }
+  }
+  auto in_win = [&](int j) -> bool {
+    if (W == 0) return false;
+    const uint32_t k = pkey(j);
+    return k > wt || (k == wt && j <= wrow);
+  };
+
+  // the others: B - W highest scores, ties to the older position, then the lower row
+  const int want = B - W;
+  uint32_t st = 0, pt = 0;
+  bool all_st = true, all_pt = true;
+  int prow = 0x7fffffff;
+  if (want > 0) {
+    int take, neq;
+    st = radix_cut([&](int j, uint32_t& k) { k = u[j]; return !in_win(j); }, L, want, hist, scan_tmp, bcast, &take,
+                   &neq);
+    if (take < neq) {
+      all_st = false;
+      int t2, n2;
+      pt = radix_cut([&](int j, uint32_t& k) { k = ~pkey(j); return u[j] == st && !in_win(j); }, L, take, hist,
+                     scan_tmp, bcast, &t2, &n2);
+      if (t2 < n2) {
+        all_pt = false;
+        int t3, n3;
+        prow = (int)~radix_cut(
+            [&](int j, uint32_t& k) {
+              k = ~(uint32_t)j;
+              return u[j] == st && ~pkey(j) == pt && !in_win(j);
+            },
+            L, t2, hist, scan_tmp, bcast, &t3, &n3);
+      }
+    }
+  }
+  auto keep = [&](int j) -> bool {
+    if (in_win(j)) return true;
+    if (want <= 0) return false;
+    const uint32_t x = u[j];
+    if (x != st) return x > st;
+    if (all_st) return true;
+    const uint32_t k2 = ~pkey(j);
+    if (k2 != pt) return k2 > pt;
+    return all_pt || j <= prow;
+  };
+
+  // pair the holes of [0, B) with the fillers of [B, L), kFillChunk at a time
+  int first_hole = B;
+  for (int r0 = 0;; r0 += kFillChunk) {
+    int base = 0;
+    for (int j0 = B; j0 < L; j0 += kSelThreads) {
+      const int j = j0 + tid;
+      const bool f = j < L && keep(j);
+      int tot;
+      const int r = base + block_exclusive_scan(f ? 1 : 0, scan_tmp, &tot);
+      if (f && r >= r0 && r < r0 + kFillChunk) fillers[r - r0] = j;
+      base += tot;
+    }
+    const int nfill = base;
+    __syncthreads();
+    int hbase = 0;
+    for (int i0 = 0; i0 < B; i0 += kSelThreads) {
+      const int i = i0 + tid;
+      const bool h = i < B && !keep(i);
+      int tot;
+      const int r = hbase + block_exclusive_scan(h ? 1 : 0, scan_tmp, &tot);
+      if (i < B) {
+        if (!h) {
+          if (r0 == 0) kept_u[i] = i;
+        } else {
+          if (i < first_hole) first_hole = i;
+          // r < nfill always (as many holes as fillers); the guard keeps every
+          // LDS read inside the filled part of the list
+          if (r >= r0 && r < r0 + kFillChunk) kept_u[i] = r < nfill ? fillers[r - r0] : i;
+        }
+      }
+      hbase += tot;
+    }
+    __syncthreads();
+    if (r0 + kFillChunk >= nfill) break;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const int o = __shfl_xor(first_hole, off, 64);
+    first_hole = o < first_hole ? o : first_hole;
+  }
+  if ((tid & 63) == 0) scan_tmp[tid >> 6] = first_hole;
+  __syncthreads();
+  if (tid == 0) {
+    int f = scan_tmp[0];
+    for (int w = 1; w < kSelThreads / 64; ++w) f = scan_tmp[w] < f ? scan_tmp[w] : f;
+    sel[2 * unit] = f;
+    sel[2 * unit + 1] = B;
+  }
+}
+
+constexpr int kFillBatch = 8;  // 16-byte pieces in flight per thread (named registers below)
+
+// One workgroup per (slot, KV head): K, V and the positions.  Rows from the
+// first hole to the kept count are scanned kCompactThreads at a time; the
+// rows whose gather index differs from their own are listed in LDS and their
+// K and V pieces copied in batches of kFillBatch loads per thread before the
+// matching stores.
+__global__ __launch_bounds__(kCompactThreads) void compact_fill_kernel(unsigned char* __restrict__ K,
+                                                                       unsigned char* __restrict__ V,
+                                                                       int32_t* __restrict__ pos,
+                                                                       const int32_t* __restrict__ kept,
+                                                                       const int32_t* __restrict__ sel,
+                                                                       int32_t* __restrict__ len, int Hkv, int Lmax,
+                                                                       int B, int row_bytes,
+                                                                       unsigned long long* __restrict__ rows_moved) {
+  __shared__ int mv_dst[kCompactThreads];
+  __shared__ int mv_src[kCompactThreads];
+  __shared__ int scan_tmp[16];
+  const size_t unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int f = sel[2 * unit];
+  const int cnt = sel[2 * unit + 1];
+  if (cnt < 0) return;  // unit rejected by the selection
+  const int n = (int)(unit / Hkv);
+  if (tid == 0 && unit % Hkv == 0) len[n] = cnt;  // no compaction block reads len
+  if (cnt <= f) return;
+  const int32_t* kept_u = kept + unit * (size_t)B;
+  unsigned char* kb = K + unit * (size_t)Lmax * row_bytes;
+  unsigned char* vb = V + unit * (size_t)Lmax * row_bytes;
+  int32_t* pu = pos + unit * (size_t)Lmax;
+  const int lpr = row_bytes / 16;  // 16-byte pieces per row
+  int moved = 0;
+  for (int i0 = f; i0 < cnt; i0 += kCompactThreads) {
+    const int i = i0 + tid;
+    const int src = i < cnt ? kept_u[i] : i;
+    // fillers lie at or beyond the kept count (and inside the allocation)
+    const bool m = src != i && src >= cnt && src < Lmax;
+    int nm;
+    const int r = block_exclusive_scan(m ? 1 : 0, scan_tmp, &nm);
+    if (m) {
+      mv_dst[r] = i;
+      mv_src[r] = src;
+    }
+    __syncthreads();
+    const int items = nm * 2 * lpr;  // (row, tensor, piece)
+    // byte offset of piece `it` in the K (tensor 0) or V row of mover `mv`
+    auto piece = [&](int it, const int* rows, unsigned char** base) -> size_t {
+      const int mv = it / (2 * lpr), rem = it - mv * 2 * lpr;
+      *base = rem >= lpr ? vb : kb;
+      return (size_t)rows[mv] * row_bytes + (size_t)(rem >= lpr ? rem - lpr : rem) * 16;
+    };
+    for (int it0 = tid; it0 < items; it0 += kCompactThreads * kFillBatch) {
+      // kFillBatch (8) loads in flight per thread, held in named registers;
+      // past the end the last piece is loaded again and not stored
+      unsigned char* b;
+#define BKV_FILL_LD(k)                                                                     \
+  const int pc##k = min(it0 + (k) * kCompactThreads, items - 1);                          \
+  const size_t so##k = piece(pc##k, mv_src, &b);                                          \
+  const uint4 v##k = *reinterpret_cast<const uint4*>(b + so##k);
+#define BKV_FILL_ST(k)                                                                     \
+  if (it0 + (k) * kCompactThreads < items) {                                              \
+    const size_t d##k = piece(pc##k, mv_dst, &b);                                         \
+    *reinterpret_cast<uint4*>(b + d##k) = v##k;                                            \
+  }
+      BKV_FILL_LD(0) BKV_FILL_LD(1) BKV_FILL_LD(2) BKV_FILL_LD(3)
+      BKV_FILL_LD(4) BKV_FILL_LD(5) BKV_FILL_LD(6) BKV_FILL_LD(7)
+      BKV_FILL_ST(0) BKV_FILL_ST(1) BKV_FILL_ST(2) BKV_FILL_ST(3)
+      BKV_FILL_ST(4) BKV_FILL_ST(5) BKV_FILL_ST(6) BKV_FILL_ST(7)
+#undef BKV_FILL_LD
+#undef BKV_FILL_ST
+    }
+    if (tid < nm) pu[mv_dst[tid]] = pu[mv_src[tid]];
+    moved += nm;
+    __syncthreads();  // the lists are rewritten by the next sweep
+  }
+  if (tid == 0 && moved > 0) atomicAdd(rows_moved, 2ull * (unsigned long long)moved);  // K and V rows
+}
+
 hipError_t launch_select(const float* scores, const int32_t* len, int N, int Hkv, int Lmax, int B, int W,
                          int32_t* kept, int32_t* sel, int32_t* ws_words, hipStream_t st) {
   hipLaunchKernelGGL(select_kernel, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, len, Hkv, Lmax, B, W, kept, sel,
@@ -221,6 +497,21 @@ hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* 
                           int Lmax, int B, int row_bytes, unsigned long long* rows_moved, hipStream_t st) {
   hipLaunchKernelGGL(compact_kernel, dim3(N * Hkv * 2), dim3(kCompactThreads), 0, st, (unsigned char*)K, (unsigned char*)V, kept,
                      sel, len, Hkv, Lmax, B, row_bytes, rows_moved);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_fill(const float* scores, const int32_t* pos, const int32_t* len, int N, int Hkv, int Lmax,
+                              int B, int W, int32_t* kept, int32_t* sel, int32_t* ws_words, hipStream_t st) {
+  hipLaunchKernelGGL(select_fill_kernel, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, pos, len, Hkv, Lmax, B, W,
+                     kept, sel, ws_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_fill(void* K, void* V, int32_t* pos, const int32_t* kept, const int32_t* sel, int32_t* len,
+                               int N, int Hkv, int Lmax, int B, int row_bytes, unsigned long long* rows_moved,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(compact_fill_kernel, dim3(N * Hkv), dim3(kCompactThreads), 0, st, (unsigned char*)K,
+                     (unsigned char*)V, pos, kept, sel, len, Hkv, Lmax, B, row_bytes, rows_moved);
   return hipGetLastError();
 }
 

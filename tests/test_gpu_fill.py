@@ -1,0 +1,324 @@
+"""GPU parity of the hole-filling eviction layout (bkv_select_fill,
+bkv_compact_fill) against the oracle.
+
+Acceptance: on binary32 scores given to both sides the gather map is
+identical (ties at the cut included), and K, V and the positions after
+compaction are bit-exact.  On the full path (beacon-guided scores computed by
+the GPU, binary64 by the oracle) the kept sets may differ only at rows whose
+oracle score lies within 1e-4 (relative) of the cut; the GPU's map must then
+be the pairing of its own kept set.  At a first eviction (positions ascending
+in the row) the kept set must equal the order-preserving selection's on the
+same scores, on every unit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import TIE_RTOL, log
+from kv_cache_eviction_continual_amd import bkv, configs, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def np_storage(t):
+    return synth.to_numpy_storage(t)
+
+
+def _bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
+def _pairing(keep_set, L, B):
+    """The gather map of a kept set: holes of [0, B) take the kept rows of
+    [B, L), both ascending."""
+    if L <= B:
+        return list(range(L))
+    holes = [i for i in range(B) if i not in keep_set]
+    fillers = sorted(j for j in keep_set if j >= B)
+    assert len(holes) == len(fillers)
+    out = list(range(B))
+    for h, f in zip(holes, fillers):
+        out[h] = f
+    return out
+
+
+def _check_unit_exact(s, pos, L, B, W, g_map):
+    o_map = oracle.select_fill(s.astype(np.float64), pos.astype(np.int64), L, B, W)
+    n = min(L, B)
+    assert np.array_equal(g_map[:n], o_map), "gather map differs"
+    if L <= B:
+        assert np.all(g_map[n:] == -1)
+    return o_map
+
+
+def _given_scores_case(w, N, s, pos, lengths, B, W, Lmax):
+    """Runs select_fill + compact_fill on given scores and positions and
+    checks every unit against the oracle, bit for bit."""
+    Hkv = w.n_kv_heads
+    syn = synth.Synth(w, n_slots=N, seed=11, device="cuda")
+    K = syn.keys(max_len=Lmax)
+    V = syn.values(max_len=Lmax)
+    shape = bkv.make_shape(N, Hkv, w.n_q_heads, w.head_dim, Lmax, K.dtype)
+    ws = bkv.alloc_workspace(shape, w.n_recent, w.n_beacons)
+    length = torch.from_numpy(np.asarray(lengths, np.int32)).cuda()
+    kept = torch.full((N, Hkv, B), -7, dtype=torch.int32, device="cuda")
+    posd = pos.clone()
+    K_old, V_old, P_old = np_storage(K), np_storage(V), pos.cpu().numpy()
+    bkv.bkv_select_compact_fill(shape, s, K, V, posd, length, B, W, kept, ws)
+    torch.cuda.synchronize()
+    assert bkv.bkv_read_device_status(ws) == 0
+    sn, kg = s.cpu().numpy(), kept.cpu().numpy()
+    Kn, Vn, Pn = np_storage(K), np_storage(V), posd.cpu().numpy()
+    moved = 0
+    for n in range(N):
+        L = int(lengths[n])
+        assert int(length[n]) == min(L, B)
+        for h in range(Hkv):
+            o_map = _check_unit_exact(sn[n, h], P_old[n, h], L, B, W, kg[n, h])
+            for old, new in ((K_old, Kn), (V_old, Vn), (P_old, Pn)):
+                ref = np.ascontiguousarray(old[n, h])
+                oracle.compact(ref, o_map)
+                assert np.array_equal(new[n, h], ref), "rows after compaction differ at unit %s" % ((n, h),)
+            moved += 2 * int(np.sum(o_map != np.arange(len(o_map))))
+    assert bkv.ws_rows_moved(ws) == moved
+    return kg
+
+
+@pytest.mark.parametrize("tie_fraction", [0.0, 0.3, 0.95])
+@pytest.mark.parametrize("pos_kind", ["ascending", "permuted", "duplicates"])
+def test_select_compact_fill_exact_on_given_scores(tie_fraction, pos_kind):
+    w = configs.get(2)
+    N, L, Hkv = 3, w.length, w.n_kv_heads
+    log("case: fill on given scores, %s positions, tie fraction %.2f" % (pos_kind, tie_fraction))
+    syn = synth.Synth(w, n_slots=N, seed=5, device="cuda")
+    s = syn.scores(L, tie_fraction=tie_fraction)
+    if pos_kind == "ascending":
+        pos = torch.arange(L, dtype=torch.int32, device="cuda").expand(N, Hkv, L).contiguous()
+    elif pos_kind == "permuted":  # distinct, negative ones included
+        pos = (torch.argsort(syn.randn((N, Hkv, L)), dim=-1) - 300).to(torch.int32).contiguous()
+    else:  # a few distinct values: every cut falls inside a run of equal positions
+        pos = syn.randint(0, 40, (N, Hkv, L)).to(torch.int32).contiguous()
+    _given_scores_case(w, N, s, pos, [L] * N, w.budget, w.window, L)
+
+
+def test_fill_window_zero_window_budget_and_ragged_lengths():
+    w = configs.get(2)
+    N, Lmax, Hkv = 6, w.length + 8, w.n_kv_heads
+    syn = synth.Synth(w, n_slots=N, seed=21, device="cuda")
+    s = syn.scores(Lmax, tie_fraction=0.2)
+    pos = (torch.argsort(syn.randn((N, Hkv, Lmax)), dim=-1)).to(torch.int32).contiguous()
+    B = w.budget
+    lengths = [0, B - 5, B, B + 1, w.length, Lmax]
+    for W in (0, 32, B):
+        log("case: fill, window %d, lengths %s" % (W, lengths))
+        _given_scores_case(w, N, s, pos, lengths, B, W, Lmax)
+
+
+def test_fill_pairs_more_holes_than_one_lds_sweep():
+    """More than 1024 fillers per unit: the pairing runs several sweeps."""
+    w = configs.get(2)
+    N, Lmax, Hkv, B, W = 2, 4096, w.n_kv_heads, 2048, 32
+    syn = synth.Synth(w, n_slots=N, seed=31, device="cuda")
+    # low scores below B, high ones beyond it: almost every kept row is a filler
+    s = syn.scores(Lmax)
+    s[:, :, :B] *= 1e-3
+    pos = torch.arange(Lmax, dtype=torch.int32, device="cuda").expand(N, Hkv, Lmax).contiguous()
+    log("case: fill, %d fillers per unit" % (Lmax - B))
+    kg = _given_scores_case(w, N, s, pos, [Lmax] * N, B, W, Lmax)
+    assert np.sum(kg[0, 0] != np.arange(B)) > 1024
+
+
+def test_fill_kept_set_equals_order_preserving_at_first_eviction():
+    """Positions ascending in the row: the same kept set as bkv_select."""
+    w = configs.get(2)
+    N, L, Hkv = 4, w.length, w.n_kv_heads
+    syn = synth.Synth(w, n_slots=N, seed=41, device="cuda")
+    s = syn.scores(L, tie_fraction=0.5)
+    pos = (torch.arange(L, dtype=torch.int32, device="cuda") * 3 + 7).expand(N, Hkv, L).contiguous()
+    shape = bkv.make_shape(N, Hkv, w.n_q_heads, w.head_dim, L, torch.bfloat16)
+    ws = bkv.alloc_workspace(shape, w.n_recent, w.n_beacons)
+    length = torch.full((N,), L, dtype=torch.int32, device="cuda")
+    ks = torch.empty(N, Hkv, w.budget, dtype=torch.int32, device="cuda")
+    kf = torch.empty_like(ks)
+    bkv.bkv_select(shape, s, length, w.budget, w.window, ks, ws)
+    bkv.bkv_select_fill(shape, s, pos, length, w.budget, w.window, kf, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.sort(kf, dim=-1).values, ks)
+
+
+def _fill_step_vs_oracle(g_map, o_scores, pos, L, B, W):
+    """Full-path comparison: kept sets equal except at oracle ties near the
+    cut (among the rows outside the window); the map is the pairing of the
+    GPU's kept set."""
+    o_map = oracle.select_fill(o_scores, pos.astype(np.int64), L, B, W)
+    n = min(L, B)
+    g = set(int(x) for x in g_map[:n])
+    o = set(int(x) for x in o_map)
+    assert len(g) == len(o) == n
+    assert list(g_map[:n]) == _pairing(g, L, B)
+    if g == o:
+        return 0
+    newest = set(np.argsort(-pos[:L].astype(np.int64), kind="stable")[:W].tolist())
+    rest = np.array([j for j in range(L) if j not in newest])
+    cand = o_scores[rest]
+    tau = np.sort(cand)[::-1][B - W - 1]
+    for j in g ^ o:
+        assert j not in newest, "window row %d differs" % j
+        assert abs(o_scores[j] - tau) <= TIE_RTOL * tau, "kept differs at row %d: %r vs cut %r" % (j, o_scores[j], tau)
+    return len(g ^ o)
+
+
+def _same_buffers(qbuf, qcount, o_qbuf, o_qcount):
+    """The oracle scores with its own FPS buffers; they must be the GPU's."""
+    gc = qcount.cpu().numpy()
+    assert np.array_equal(gc, o_qcount)
+    gq = synth.to_numpy_storage(qbuf)
+    for g in range(gc.shape[1]):
+        assert np.array_equal(gq[0, g, :gc[0, g]], o_qbuf[0, g, :gc[0, g]])
+
+
+@pytest.mark.parametrize("interval", [128, 16])
+def test_fill_full_path_over_evictions(interval):
+    """Ingest, score, select and fill over several evictions, new tokens
+    appended after each (interval 16 is below the window of 32, so the window
+    reaches rows that an earlier eviction filled)."""
+    w = configs.get(2)
+    N, Hkv, G, d = 1, w.n_kv_heads, w.group, w.head_dim
+    R, nb, B, W = w.n_recent, w.n_beacons, w.budget, w.window
+    Lmax = B + max(interval, 128)
+    events = 4
+    log("case: fill full path, interval %d, %d evictions" % (interval, events))
+    syn = synth.Synth(w, n_slots=N, seed=3, device="cuda")
+    pool_K = syn.keys(max_len=Lmax + interval * events, block=1)
+    pool_V = syn.values(max_len=Lmax + interval * events, block=1)
+    K = pool_K[:, :, :Lmax].clone()
+    V = pool_V[:, :, :Lmax].clone()
+    shape = bkv.make_shape(N, Hkv, w.n_q_heads, d, Lmax, K.dtype)
+    ws = bkv.alloc_workspace(shape, R, nb)
+    qbuf = torch.zeros(N, w.n_q_heads, w.capacity, d, dtype=K.dtype, device="cuda")
+    qcount = torch.zeros(N, w.n_q_heads, dtype=torch.int32, device="cuda")
+    scores = torch.empty(N, Hkv, Lmax, dtype=torch.float32, device="cuda")
+    kept = torch.empty(N, Hkv, B, dtype=torch.int32, device="cuda")
+    pos = torch.zeros(N, Hkv, Lmax, dtype=torch.int32, device="cuda")
+    o_qbuf = np.zeros((1, w.n_q_heads, w.capacity, d), dtype=np.uint16)
+    o_qcount = np.zeros((1, w.n_q_heads), dtype=np.int32)
+
+    # the first w.length tokens of the stream fill rows [0, L0)
+    L0 = w.length
+    pos[:, :, :L0] = torch.arange(L0, dtype=torch.int32, device="cuda")
+    t = L0
+    nxt = L0  # next unused row of the key/value pools
+    for b in range(L0 // w.interval):
+        blk = syn.query_block(b)
+        bkv.bkv_fps_update(shape, blk, blk.shape[2], qbuf, qcount, w.capacity, w.shrink_to, ws)
+        oracle.fps_update(synth.to_numpy_storage(blk), o_qbuf, o_qcount, w.shrink_to)
+    _same_buffers(qbuf, qcount, o_qbuf, o_qcount)
+    L = L0
+    ndiff = 0
+    for e in range(events):
+        now = t - 1
+        blk = syn.query_block(100 + e)[:, :, -R:].contiguous()  # the recent queries of this eviction
+        recent_pos_np = synth.recent_positions(N, R, now)
+        length = torch.full((N,), L, dtype=torch.int32, device="cuda")
+        pos_now = torch.full((N,), now, dtype=torch.int32, device="cuda")
+        bkv.bkv_score(shape, K, length, blk, torch.from_numpy(recent_pos_np).cuda(), R, qbuf, qcount, w.capacity, nb,
+                      pos_now, w.rope_theta, scores, ws)
+        K_old, V_old, P_old = np_storage(K), np_storage(V), pos.cpu().numpy()
+        bkv.bkv_select_compact_fill(shape, scores, K, V, pos, length, B, W, kept, ws)
+        torch.cuda.synchronize()
+        assert bkv.bkv_read_device_status(ws) == 0
+        kg = kept.cpu().numpy()
+        Kn, Vn, Pn = np_storage(K), np_storage(V), pos.cpu().numpy()
+        for h in range(Hkv):
+            g0 = h * G
+            s_o, _, _, _ = oracle.score_unit(np.ascontiguousarray(K_old[0, h]), L,
+                                             synth.to_numpy_storage(blk[0, g0:g0 + G]), recent_pos_np[0],
+                                             o_qbuf[0, g0:g0 + G], o_qcount[0, g0:g0 + G], nb, now, w.rope_theta)
+            ndiff += _fill_step_vs_oracle(kg[0, h], np.asarray(s_o, np.float64), P_old[0, h], L, B, W)
+            g_map = kg[0, h, :min(L, B)]
+            for old, new in ((K_old, Kn), (V_old, Vn), (P_old, Pn)):
+                ref = np.ascontiguousarray(old[0, h])
+                oracle.compact(ref, g_map)
+                assert np.array_equal(new[0, h], ref)
+            # the window: the W newest positions survive
+            assert set(range(now - W + 1, now + 1)) <= set(Pn[0, h, :B].tolist())
+        L = min(L, B)
+        # append `interval` new tokens (and their queries)
+        K[:, :, L:L + interval] = pool_K[:, :, nxt:nxt + interval]
+        V[:, :, L:L + interval] = pool_V[:, :, nxt:nxt + interval]
+        pos[:, :, L:L + interval] = torch.arange(t, t + interval, dtype=torch.int32, device="cuda")
+        qb = syn.query_block(200 + e)[:, :, :interval].contiguous()
+        bkv.bkv_fps_update(shape, qb, interval, qbuf, qcount, w.capacity, w.shrink_to, ws)
+        oracle.fps_update(synth.to_numpy_storage(qb), o_qbuf, o_qcount, w.shrink_to)
+        _same_buffers(qbuf, qcount, o_qbuf, o_qcount)
+        nxt += interval
+        t += interval
+        L += interval
+    log("  %d kept rows differ at oracle ties" % ndiff)
+
+
+def test_fill_full_size_qwen3_4b_36_layers_batch16():
+    """The benchmark's workload (576 slots x 8 KV heads) in the hole-filling
+    layout: a first eviction with positions in row order (kept set equal to
+    the order-preserving selection's on every unit), 128 new tokens, then a
+    second eviction with permuted rows; every unit checked on the device,
+    sampled units against the oracle on the GPU's scores."""
+    w = configs.get(3)
+    N, Hkv, L, B, W = w.n_slots, w.n_kv_heads, w.length, w.budget, w.window
+    log("case: fill full size %s" % w.name)
+    syn = synth.Synth(w, seed=0, device="cuda")
+    K = syn.keys()
+    V = syn.values()
+    shape = bkv.make_shape(N, Hkv, w.n_q_heads, w.head_dim, w.max_len, K.dtype)
+    ws = bkv.alloc_workspace(shape, w.n_recent, w.n_beacons)
+    length = torch.full((N,), L, dtype=torch.int32, device="cuda")
+    pos = torch.arange(w.max_len, dtype=torch.int32, device="cuda").expand(N, Hkv, w.max_len).contiguous()
+    ks = torch.empty(N, Hkv, B, dtype=torch.int32, device="cuda")
+    kf = torch.empty_like(ks)
+    rng = np.random.default_rng(7)
+    units = sorted({(0, 0), (N - 1, Hkv - 1)} | {(int(rng.integers(0, N)), int(rng.integers(0, Hkv)))
+                                                  for _ in range(10)})
+    for ev in range(2):
+        s = syn.scores(L, tie_fraction=0.1, block=ev)
+        scores = torch.zeros(N, Hkv, w.max_len, dtype=torch.float32, device="cuda")
+        scores[:, :, :L] = s
+        if ev == 0:
+            bkv.bkv_select(shape, scores, length, B, W, ks, ws)
+        K_old, V_old, P_old = K.clone(), V.clone(), pos.clone()
+        bkv.bkv_select_compact_fill(shape, scores, K, V, pos, length, B, W, kf, ws)
+        torch.cuda.synchronize()
+        assert bkv.bkv_read_device_status(ws) == 0
+        assert torch.all(length == B)
+        if ev == 0:
+            assert torch.equal(torch.sort(kf, dim=-1).values, ks), "kept set differs from the order-preserving one"
+        # every unit: a valid map, the window kept, rows and positions gathered
+        k = kf.long()
+        ar = torch.arange(B, device="cuda")
+        assert torch.all((k == ar) | (k >= B)) and torch.all(k < L)
+        assert torch.equal(torch.sort(k, dim=-1).values.diff(dim=-1).clamp(max=1), torch.ones_like(k[:, :, 1:]))
+        newest = torch.topk(P_old[:, :, :L], W, dim=-1).values
+        kept_pos = torch.gather(P_old, 2, kf.long())
+        for n0 in range(0, N, 64):
+            n1 = min(N, n0 + 64)
+            kp = kept_pos[n0:n1]
+            nw = newest[n0:n1]
+            assert torch.all((nw.unsqueeze(-1) == kp.unsqueeze(-2)).any(dim=-1)), "a window row was evicted"
+        assert torch.equal(pos[:, :, :B], kept_pos)
+        assert torch.equal(pos[:, :, B:], P_old[:, :, B:])
+        for n0 in range(0, N, 128):
+            n1 = min(N, n0 + 128)
+            idx = k[n0:n1].unsqueeze(-1).expand(n1 - n0, Hkv, B, w.head_dim)
+            for old, new in ((K_old, K), (V_old, V)):
+                assert torch.equal(_bits(new[n0:n1, :, :B]), _bits(torch.gather(old[n0:n1], 2, idx)))
+                assert torch.equal(_bits(new[n0:n1, :, B:]), _bits(old[n0:n1, :, B:]))
+        # sampled units against the oracle on the same binary32 scores
+        sn = scores[:, :, :L]
+        for (n, h) in units:
+            o_map = oracle.select_fill(sn[n, h].cpu().numpy().astype(np.float64),
+                                       P_old[n, h, :L].cpu().numpy().astype(np.int64), L, B, W)
+            assert np.array_equal(kf[n, h].cpu().numpy(), o_map), "map differs at unit %s" % ((n, h),)
+        del K_old, V_old
+        # 128 new tokens at rows [B, L): fresh positions
+        pos[:, :, B:L] = torch.arange(L + ev * (L - B), L + (ev + 1) * (L - B), dtype=torch.int32, device="cuda")
+        length.fill_(L)
