@@ -117,6 +117,74 @@ class State:
             ev[5].record()
 
 
+def time_hole_fill(st, warmup, steps):
+    """The same eviction pass in the hole-filling layout (rows carry their
+    positions; only kept rows beyond the budget move).  Runs on the state the
+    order-preserving phase left; each pass first appends the positions of the
+    interval's new tokens at rows [B, L)."""
+    w = st.w
+    N, Hkv, B, L = st.N, w.n_kv_heads, w.budget, w.length
+    dev = st.K.device
+    pos = torch.arange(w.max_len, dtype=torch.int32, device=dev).expand(N, Hkv, w.max_len).contiguous()
+    new_rows = L - B
+    # positions of the new tokens of pass i: above every earlier one
+    fresh = [torch.full((N, Hkv, new_rows), w.max_len + new_rows * i, dtype=torch.int32, device=dev)
+             + torch.arange(new_rows, dtype=torch.int32, device=dev) for i in range(min(steps + warmup, 64))]
+
+    def step(i, ev=None):
+        p = (st.n_warm + i) % st.n_pool
+        e = i % N_EVENTS
+        if ev is not None:
+            ev[0].record()
+        st.length.copy_(st.len_full)
+        pos[:, :, B:L].copy_(fresh[i % len(fresh)] + new_rows * len(fresh) * (i // len(fresh)))
+        if ev is not None:
+            ev[1].record()
+        bkv.bkv_fps_update(st.shape, st.blocks[p], w.interval, st.qbuf, st.qcount, w.capacity, w.shrink_to, st.ws)
+        if ev is not None:
+            ev[2].record()
+        bkv.bkv_score(st.shape, st.K, st.length, st.recent[p], st.recent_pos[e], w.n_recent, st.qbuf, st.qcount,
+                      w.capacity, w.n_beacons, st.pos_now[e], w.rope_theta, st.scores, st.ws)
+        if ev is not None:
+            ev[3].record()
+        bkv.bkv_select_fill(st.shape, st.scores, pos, st.length, B, w.window, st.kept, st.ws)
+        if ev is not None:
+            ev[4].record()
+        bkv.bkv_compact_fill(st.shape, st.K, st.V, pos, st.length, B, st.kept, st.ws)
+        if ev is not None:
+            ev[5].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    bkv.bkv_reset_device_status(st.ws)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = bkv.bkv_read_device_status(st.ws)
+    assert status == 0, "device status %d" % status
+    rows_moved = bkv.ws_rows_moved(st.ws)
+    names = ["grow", "fps_update", "score", "select", "compact"]
+    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                for j, n in enumerate(names)}
+    row_bytes = w.head_dim * 2
+    moved_per_pass = rows_moved / steps                       # K and V rows
+    compact_bytes = moved_per_pass * row_bytes * 2 + moved_per_pass / 2 * 4 * 2  # rows + positions, read + write
+    return {
+        "layout": "hole-filling (rows carry positions; kept rows beyond the budget fill the evicted rows below it)",
+        "passes_per_s": steps / elapsed,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "stage_ms": stage_ms,
+        "rows_moved_per_pass": moved_per_pass,
+        "compact_algorithmic_bytes": compact_bytes,
+        "compact_GBps": compact_bytes / (stage_ms["compact"] * 1e6),
+    }
+
+
 def copy_probe(dev, nbytes=1 << 30, reps=10):
     """Bandwidth of a plain device copy of known size (read + write bytes)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -211,6 +279,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--no-hole-fill", action="store_true", help="skip the hole-filling layout phase")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -307,6 +376,9 @@ def main():
         },
         "kernel_source_hash": src_hash,
     }
+    if not args.no_hole_fill:
+        log("timing the hole-filling layout on the same workload")
+        result["hole_fill"] = time_hole_fill(st, args.warmup, K)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(st, budget_s=args.cpu_budget)

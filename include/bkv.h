@@ -95,11 +95,13 @@ typedef struct bkv_shape {
  *   [2] lse     : float [N][Hkv][RP], natural-log row normaliser of the
  *                 softmax (+inf for absent rows);
  *   [3] select  : int32 [N][Hkv][2] = {first evicted index, kept count};
- *   [4] rope    : float2 [N][R+1][d/2] (cos, sin) tables.
+ *   [4] rope    : float2 [N][R+1][d/2] (cos, sin) tables;
+ *   [5] beacons : int32 [N][Hq][nb+1]: the pick count, then the buffer rows
+ *                 of the beacons in pick order.
  * Zero the first 256 bytes once before first use (bkv_reset_device_status).
  */
 size_t bkv_workspace_size(const bkv_shape *shape, int32_t R, int32_t nb);
-int bkv_workspace_layout(const bkv_shape *shape, int32_t R, int32_t nb, size_t offsets[5]);
+int bkv_workspace_layout(const bkv_shape *shape, int32_t R, int32_t nb, size_t offsets[6]);
 
 /*
  * bkv_fps_update -- Continual FPS ingest ([WZ] 怎么挑出这几个信标: a bounded

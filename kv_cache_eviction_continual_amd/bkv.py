@@ -24,7 +24,7 @@ E_NULL, E_SHAPE, E_DTYPE, E_BUDGET, E_CAPACITY, E_WORKSPACE, E_HIP = range(1, 8)
 DEV_BAD_LEN = 0x1
 DEV_BAD_COUNT = 0x2
 
-WS_OBS, WS_VALID, WS_LSE, WS_SELECT, WS_ROPE = range(5)
+WS_OBS, WS_VALID, WS_LSE, WS_SELECT, WS_ROPE, WS_BEACONS = range(6)
 WS_HEADER_BYTES = 256
 
 EXPORTS = (
@@ -150,7 +150,7 @@ def bkv_workspace_size(shape: Shape, R: int, nb: int) -> int:
 
 
 def bkv_workspace_layout(shape: Shape, R: int, nb: int):
-    offs = (ctypes.c_size_t * 5)()
+    offs = (ctypes.c_size_t * 6)()
     _check(load().bkv_workspace_layout(ctypes.byref(shape), R, nb, offs))
     return [int(o) for o in offs]
 
@@ -233,7 +233,7 @@ def ws_rows_moved(ws) -> int:
 
 def ws_views(shape: Shape, R: int, nb: int, ws):
     """Typed views of the workspace regions: obs rows, valid flags, lse,
-    select table, rope tables."""
+    select table, beacon picks."""
     offs = bkv_workspace_layout(shape, R, nb)
     G = shape.n_q_heads // shape.n_kv_heads
     rows = G * (R + nb)
@@ -246,4 +246,7 @@ def ws_views(shape: Shape, R: int, nb: int, ws):
     valid = ws[offs[WS_VALID]:offs[WS_VALID] + units * RP * 4].view(torch.int32).view(shape.n_seq, shape.n_kv_heads, RP)
     lse = ws[offs[WS_LSE]:offs[WS_LSE] + units * RP * 4].view(torch.float32).view(shape.n_seq, shape.n_kv_heads, RP)
     sel = ws[offs[WS_SELECT]:offs[WS_SELECT] + units * 8].view(torch.int32).view(shape.n_seq, shape.n_kv_heads, 2)
-    return {"obs": obs, "valid": valid, "lse": lse, "select": sel, "rows": rows, "RP": RP}
+    nbk = shape.n_seq * shape.n_q_heads * (nb + 1)
+    beacons = ws[offs[WS_BEACONS]:offs[WS_BEACONS] + nbk * 4].view(torch.int32).view(shape.n_seq, shape.n_q_heads,
+                                                                                       nb + 1)
+    return {"obs": obs, "valid": valid, "lse": lse, "select": sel, "beacons": beacons, "rows": rows, "RP": RP}

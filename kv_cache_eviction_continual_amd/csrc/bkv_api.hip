@@ -11,11 +11,11 @@ namespace bkv {
 template <int DT, int D>
 hipError_t launch_fps_update(const void*, int, void*, int32_t*, int, int, int, int32_t*, hipStream_t);
 template <int DT, int D>
-hipError_t launch_obs_build(const void*, const int32_t*, int, int, const void*, const int32_t*, int, const int32_t*,
-                            double, float2*, void*, int32_t*, int, int, int, int, int32_t*, hipStream_t);
+hipError_t launch_beacon_picks(const void*, const int32_t*, int, int, int, int32_t*, int32_t*, hipStream_t);
 template <int DT, int D>
-hipError_t launch_score(const void*, const int32_t*, int, int, int, const void*, const int32_t*, int, float*, float*,
-                        int32_t*, hipStream_t);
+hipError_t launch_score(const void*, const int32_t*, int, int, int, int, const void*, const int32_t*, int,
+                        const void*, int, const int32_t*, int, const int32_t*, double, float2*, void*, int32_t*, int,
+                        float*, float*, int32_t*, hipStream_t);
 hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
                          hipStream_t);
 hipError_t launch_compact(void*, void*, const int32_t*, const int32_t*, int32_t*, int, int, int, int, int,
@@ -51,7 +51,7 @@ int check_shape(const bkv_shape* s) {
 }
 
 struct WsLayout {
-  size_t obs, valid, lse, select, rope, total;
+  size_t obs, valid, lse, select, rope, beacons, total;
   int RP;
 };
 
@@ -78,6 +78,8 @@ bool layout(const bkv_shape* s, int R, int nb, WsLayout* out) {
   off = align256(off + units * RP * sizeof(float));
   out->rope = off;
   off = align256(off + (size_t)s->n_seq * (R + 1) * (s->head_dim / 2) * sizeof(float2));
+  out->beacons = off;
+  off = align256(off + (size_t)s->n_seq * s->n_q_heads * (nb + 1) * sizeof(int32_t));
   out->total = off;
   return true;
 }
@@ -105,7 +107,7 @@ size_t bkv_workspace_size(const bkv_shape* shape, int32_t R, int32_t nb) {
   return w.total;
 }
 
-int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t offsets[5]) {
+int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t offsets[6]) {
   int st = check_shape(shape);
   if (st != BKV_OK) return st;
   if (!offsets) return BKV_E_NULL;
@@ -116,6 +118,7 @@ int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t o
   offsets[2] = w.lse;
   offsets[3] = w.select;
   offsets[4] = w.rope;
+  offsets[5] = w.beacons;
   return BKV_OK;
 }
 
@@ -164,11 +167,12 @@ int bkv_score(const bkv_shape* shape, const void* K, const int32_t* len, const v
   int32_t* valid = (int32_t*)(base + w.valid);
   float* lse = (float*)(base + w.lse);
   hipError_t e;
+  int32_t* beacons = (int32_t*)(base + w.beacons);
 #define BKV_SCORE_CASE(DT, D)                                                                                  \
-  e = launch_obs_build<DT, D>(qbuf, qcount, C, nb, recent, recent_pos, R, pos_now, rope_theta, tab, obs, valid, \
-                              N, Hq, Hkv, w.RP, words, stream);                                                 \
+  e = launch_beacon_picks<DT, D>(qbuf, qcount, C, nb, N * Hq, beacons, words, stream);                         \
   if (e == hipSuccess)                                                                                         \
-    e = launch_score<DT, D>(K, len, N, Hkv, shape->max_len, obs, valid, w.RP, scores, lse, words, stream);
+    e = launch_score<DT, D>(K, len, N, Hkv, Hq, shape->max_len, recent, recent_pos, R, qbuf, C, beacons, nb,   \
+                            pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, stream);
   if (shape->dtype == BKV_BF16) {
     if (shape->head_dim == 128) {
       BKV_SCORE_CASE(BKV_BF16, 128)

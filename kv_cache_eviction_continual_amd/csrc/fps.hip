@@ -6,11 +6,10 @@
 //                      fills (wzjinhao.cn news article 56682 on BeaconKV,
 //                      section 怎么挑出这几个信标: bounded buffer per head,
 //                      FPS compression back to a smaller size when full);
-//   obs_build_kernel   beacon selection by FPS over the live buffer, then
-//                      RoPE of the beacons (to the current decode position)
-//                      and of the recent queries (to their own positions)
-//                      into the observation rows the score kernel consumes
-//                      (same article, section 信标查询怎么用).
+//   beacon_pick_kernel beacon selection by FPS over the live buffer (same
+//                      article, section 信标查询怎么用: the beacons are the
+//                      FPS representatives of the buffer); the score kernel
+//                      rotates the picked rows itself.
 //
 // FPS on cosine similarity: start at the row with the lowest mean cosine to
 // all rows; then repeatedly add the row with the lowest maximum cosine to the
@@ -689,115 +688,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 // RoPE tables: (cos, sin) per slot for the R recent positions and pos_now
 // ---------------------------------------------------------------------------
 
-template <int D>
-__global__ void rope_table_kernel(const int32_t* __restrict__ recent_pos, const int32_t* __restrict__ pos_now,
-                                  int R, double theta, float2* __restrict__ tab) {
-  const int n = blockIdx.x;
-  constexpr int H = D / 2;
-  float2* out = tab + (size_t)n * (R + 1) * H;
-  for (int e = threadIdx.x; e < (R + 1) * H; e += blockDim.x) {
-    const int r = e / H, i = e % H;
-    const int pos = r < R ? recent_pos[(size_t)n * R + r] : pos_now[n];
-    float2 cs = make_float2(1.0f, 0.0f);
-    if (pos >= 0) {
-      // inverse frequency theta^(-2i/d) held in binary32; the angle pos * freq
-      // is exact in binary64; cos and sin are evaluated in binary64 and held
-      // in binary32
-      const double freq = (double)(float)pow(theta, -(2.0 * i) / (double)D);
-      const double a = (double)pos * freq;
-      cs = make_float2((float)cos(a), (float)sin(a));
-    }
-    out[e] = cs;
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Observation rows: beacons (FPS over the buffer, rotated to pos_now) and
-// recent queries (rotated to their own positions)
+// Beacon selection: FPS over the live buffer of each query head
 // ---------------------------------------------------------------------------
 
-// Rotates `nrows` rows into dst rows [0, nrows): row r comes from row_of(r)
-// (always a readable row) and is present when ok_of(r) (absent rows are
-// written as zeros); its (cos, sin) pairs start at cs_of(r).  A lane takes
-// one 16-byte chunk of the first half of a row and the matching chunk of the
-// second half; all loads of a pass go out before its stores.
-template <int DT, int D, typename RowF, typename OkF, typename CsF>
-__device__ inline void rotate_rows(int nrows, RowF row_of, OkF ok_of, CsF cs_of, typename Elem<DT>::T* dst) {
-  using ET = typename Elem<DT>::T;
-  using E = Elem<DT>;
-  constexpr int H = D / 2;
-  constexpr int kPer = 16 / E::kBytes;      // elements per chunk
-  constexpr int kLanes = H / kPer;          // lanes per row
-  constexpr int kRows = 64 / kLanes;        // rows per pass
-  const int lane = fps_lane();
-  const int q = lane % kLanes;
-  for (int r0 = 0; r0 < nrows; r0 += kRows) {
-    const int r = min(r0 + lane / kLanes, nrows - 1);
-    const ET* x = row_of(r);
-    const float2* cs = cs_of(r) + q * kPer;
-    const uint4 lo = *reinterpret_cast<const uint4*>(x + q * kPer);
-    const uint4 hi = *reinterpret_cast<const uint4*>(x + H + q * kPer);
-    float4 c4[kPer / 2];
-#pragma unroll
-    for (int k = 0; k < kPer / 2; ++k) c4[k] = reinterpret_cast<const float4*>(cs)[k];
-    const bool ok = ok_of(r);
-    uint4 ylo = make_uint4(0u, 0u, 0u, 0u), yhi = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) {
-      const ET* a = reinterpret_cast<const ET*>(&lo);
-      const ET* b = reinterpret_cast<const ET*>(&hi);
-      ET* ya = reinterpret_cast<ET*>(&ylo);
-      ET* yb = reinterpret_cast<ET*>(&yhi);
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) {
-        // binary64 products of a storage value and a binary32 cos/sin are
-        // exact, so each output is the correctly rounded binary64 value of
-        // the exact rotation, rounded once more to the storage type
-        const float4 cc = c4[e >> 1];
-        const double c = (double)((e & 1) ? cc.z : cc.x), sn = (double)((e & 1) ? cc.w : cc.y);
-        const double xa = E::to_f64(a[e]), xb = E::to_f64(b[e]);
-        ya[e] = E::from_f64(xa * c - xb * sn);
-        yb[e] = E::from_f64(xb * c + xa * sn);
-      }
-    }
-    if (r0 + lane / kLanes < nrows) {
-      ET* y = dst + (size_t)r * D;
-      *reinterpret_cast<uint4*>(y + q * kPer) = ylo;
-      *reinterpret_cast<uint4*>(y + H + q * kPer) = yhi;
-    }
-  }
-}
-
+// One wavefront per query head.  Writes beacons[head][0] = the pick count
+// min(nb, count) and beacons[head][1 + b] = buffer row of pick b, in pick
+// order.  The rows themselves are rotated by the score kernel.
 template <int DT, int D, int NTMAX>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void obs_build_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void beacon_pick_kernel(
     const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
-    const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
-    const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid,
-    int Hq, int Hkv, int RP, int32_t* __restrict__ ws_words) {
-  using ET = typename Elem<DT>::T;
-  constexpr int H = D / 2;
+    int32_t* __restrict__ beacons, int32_t* __restrict__ ws_words) {
   constexpr int cap = 32 * NTMAX;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
   const int lane = fps_lane();
-  const int n = head / Hq;
-  const int gq = head % Hq;
-  const int G = Hq / Hkv;
-  const int h = gq / G;
-  const int gl = gq % G;
-  const size_t unit = (size_t)n * Hkv + h;
-  const int rowbase = gl * (R + nb);
-  ET* obs_u = obs + unit * RP * D;
-  int32_t* val_u = obs_valid + unit * RP;
-  const float2* tab_n = tab + (size_t)n * (R + 1) * H;
-
-  // recent queries at their own positions
-  const int32_t* rpos_n = recent_pos + (size_t)n * R;
-  rotate_rows<DT, D>(
-      R, [&](int r) -> const ET* { return recent + ((size_t)head * R + r) * D; },
-      [&](int r) { return rpos_n[r] >= 0; }, [&](int r) { return tab_n + r * H; }, obs_u + (size_t)rowbase * D);
-  for (int r = lane; r < R; r += 64) val_u[rowbase + r] = recent_pos[(size_t)n * R + r] >= 0 ? 1 : 0;
-
-  // beacons: FPS over the live buffer
   int c = qcount[head];
   if (c < 0 || c >= C) {
     if (lane == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
@@ -812,17 +717,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     __builtin_amdgcn_wave_barrier();
     kk = fps_dispatch<DT, D, NTMAX>(src, s, c, want);
   }
-  rotate_rows<DT, D>(
-      nb, [&](int b) -> const ET* { return b < kk ? src.row(s.picks[b]) : src.buf; },
-      [&](int b) { return b < kk; }, [&](int) { return tab_n + R * H; }, obs_u + (size_t)(rowbase + R) * D);
-  for (int b = lane; b < nb; b += 64) val_u[rowbase + R + b] = b < kk ? 1 : 0;
-
-  // padding rows of the unit (written once, by the last query head of the group)
-  if (gl == G - 1) {
-    const int first = G * (R + nb);
-    for (int e = lane; e < (RP - first) * D; e += 64) obs_u[(size_t)first * D + e] = ET(0);
-    for (int r = first + lane; r < RP; r += 64) val_u[r] = 0;
-  }
+  int32_t* out = beacons + (size_t)head * (nb + 1);
+  for (int b = lane; b < kk; b += 64) out[1 + b] = s.picks[b];
+  if (lane == 0) out[0] = kk;
 }
 
 // ---------------------------------------------------------------------------
@@ -857,35 +754,23 @@ hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcou
 }
 
 template <int DT, int D, int NTMAX>
-static hipError_t launch_obs_nt(const void* qbuf, const int32_t* qcount, int C, int nb, const void* recent,
-                                const int32_t* recent_pos, int R, float2* tab, void* obs, int32_t* obs_valid, int N,
-                                int Hq, int Hkv, int RP, int32_t* ws_words, hipStream_t st) {
+static hipError_t launch_picks_nt(const void* qbuf, const int32_t* qcount, int C, int nb, int heads,
+                                  int32_t* beacons, int32_t* ws_words, hipStream_t st) {
   using ET = typename Elem<DT>::T;
   const size_t smem = fps_lds_bytes<DT, D>(32 * NTMAX, 0);
-  auto kern = obs_build_kernel<DT, D, NTMAX>;
+  auto kern = beacon_pick_kernel<DT, D, NTMAX>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(N * Hq), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, (const ET*)recent,
-                     recent_pos, R, (const float2*)tab, (ET*)obs, obs_valid, Hq, Hkv, RP, ws_words);
+  hipLaunchKernelGGL(kern, dim3(heads), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, beacons, ws_words);
   return hipGetLastError();
 }
 
 template <int DT, int D>
-hipError_t launch_obs_build(const void* qbuf, const int32_t* qcount, int C, int nb, const void* recent,
-                            const int32_t* recent_pos, int R, const int32_t* pos_now, double theta, float2* tab,
-                            void* obs, int32_t* obs_valid, int N, int Hq, int Hkv, int RP, int32_t* ws_words,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(rope_table_kernel<D>, dim3(N), dim3(256), 0, st, recent_pos, pos_now, R, theta, tab);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (C <= 64)
-    return launch_obs_nt<DT, D, 2>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
-                                   ws_words, st);
-  if (C <= 128)
-    return launch_obs_nt<DT, D, 4>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
-                                   ws_words, st);
-  return launch_obs_nt<DT, D, 8>(qbuf, qcount, C, nb, recent, recent_pos, R, tab, obs, obs_valid, N, Hq, Hkv, RP,
-                                 ws_words, st);
+hipError_t launch_beacon_picks(const void* qbuf, const int32_t* qcount, int C, int nb, int heads, int32_t* beacons,
+                               int32_t* ws_words, hipStream_t st) {
+  if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, ws_words, st);
+  if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, ws_words, st);
+  return launch_picks_nt<DT, D, 8>(qbuf, qcount, C, nb, heads, beacons, ws_words, st);
 }
 
 template hipError_t launch_fps_update<BKV_F32, 64>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
@@ -896,13 +781,12 @@ template hipError_t launch_fps_update<BKV_BF16, 64>(const void*, int, void*, int
                                                     hipStream_t);
 template hipError_t launch_fps_update<BKV_BF16, 128>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
                                                      hipStream_t);
-#define BKV_INST_OBS(DT, D)                                                                                    \
-  template hipError_t launch_obs_build<DT, D>(const void*, const int32_t*, int, int, const void*,              \
-                                              const int32_t*, int, const int32_t*, double, float2*, void*,     \
-                                              int32_t*, int, int, int, int, int32_t*, hipStream_t);
-BKV_INST_OBS(BKV_F32, 64)
-BKV_INST_OBS(BKV_F32, 128)
-BKV_INST_OBS(BKV_BF16, 64)
-BKV_INST_OBS(BKV_BF16, 128)
+#define BKV_INST_PICKS(DT, D)                                                                                  \
+  template hipError_t launch_beacon_picks<DT, D>(const void*, const int32_t*, int, int, int, int32_t*, int32_t*,   \
+                                                 hipStream_t);
+BKV_INST_PICKS(BKV_F32, 64)
+BKV_INST_PICKS(BKV_F32, 128)
+BKV_INST_PICKS(BKV_BF16, 64)
+BKV_INST_PICKS(BKV_BF16, 128)
 
 }  // namespace bkv

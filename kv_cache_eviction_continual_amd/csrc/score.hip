@@ -1,19 +1,27 @@
 // score.hip -- beacon-guided importance scores on gfx950 matrix cores.
 //
 // For one (slot, KV head) the observation rows are the recent queries and
-// beacons of the G query heads of the group (already rotated and rounded by
-// obs_build_kernel).  Each row r attends to every cached key:
+// beacons of the G query heads of the group.  Each row r attends to every
+// cached key:
 //   p_r(j) = softmax_j(q_r . k_j / sqrt(d)),  score_j = max_r p_r(j)
 // (inkeast.github.io MessageDaily paper-reading post on BeaconKV, sections 三
 // and 4.4: scoring by the attention of recent queries together with the
 // beacon set; wzjinhao.cn news article 56682, section 信标查询怎么用:
+// beacons placed at the current position, recent queries at their own, and
 // aggregation by maximum).
 //
-// One workgroup per (slot, KV head), one wave per 32-row tile of
-// observation rows, so the wave keeps its query fragment in registers for
-// the whole kernel.  K streams through LDS in tiles of kTile keys (coalesced
-// 16-byte loads, the next tile prefetched into registers while the current
-// one is multiplied).  Two passes over K:
+// rope_table_kernel: per slot, (cos, sin) of every recent position and of
+// the current position, one entry per rotated pair.
+//
+// score_kernel: one workgroup per (slot, KV head), one wave per 32-row tile
+// of observation rows.  The wave loads its rows (recent queries, or the
+// buffer rows the beacon FPS picked) straight into matrix-core fragments and
+// rotates them there: a lane holds dims i and i + d/2 of its row in the same
+// element of two fragments.  The rotated rows are written to the workspace
+// (a debug copy) and stay in registers for the whole kernel.  K streams
+// through LDS in tiles of kTile keys (coalesced 16-byte loads, the next tile
+// prefetched into registers while the current one is multiplied).  Two
+// passes over K:
 //   pass 1: S^T = K Q^T on MFMA (lane = row, 16 keys per lane), online
 //           row max and sum of exp2 -> per-row log2-sum-exp;
 //   pass 2: S = Q K^T on MFMA (lane = key, 16 rows per lane), per-key max of
@@ -43,7 +51,16 @@ struct Mfma;
 template <int D>
 struct Mfma<BKV_BF16, D> {
   using Frag = bf16x8_t;
+  using Raw = uint4;  // the same 8 elements as storage bits
   static constexpr int kSteps = D / 16;
+  __device__ static inline Raw load_raw(const unsigned char* row, int s, int lane) {
+    return *reinterpret_cast<const uint4*>(row + (size_t)(16 * s + 8 * (lane >> 5)) * 2);
+  }
+  __device__ static inline void store_raw(unsigned char* row, int s, int lane, Raw v) {
+    *reinterpret_cast<uint4*>(row + (size_t)(16 * s + 8 * (lane >> 5)) * 2) = v;
+  }
+  __device__ static inline Raw zero_raw() { return make_uint4(0u, 0u, 0u, 0u); }
+  __device__ static inline Frag frag(Raw v) { return __builtin_bit_cast(Frag, v); }
   // dims of lane `lane` at k-step s: 16 s + 8 (lane / 32) + [0, 8)
   __device__ static inline Frag load(const unsigned char* row, int s, int lane) {
     uint4 w = *reinterpret_cast<const uint4*>(row + (size_t)(16 * s + 8 * (lane >> 5)) * 2);
@@ -57,7 +74,16 @@ struct Mfma<BKV_BF16, D> {
 template <int D>
 struct Mfma<BKV_F32, D> {
   using Frag = float;
+  using Raw = float;
   static constexpr int kSteps = D / 2;
+  __device__ static inline Raw load_raw(const unsigned char* row, int s, int lane) {
+    return *reinterpret_cast<const float*>(row + (size_t)(2 * s + (lane >> 5)) * 4);
+  }
+  __device__ static inline void store_raw(unsigned char* row, int s, int lane, Raw v) {
+    *reinterpret_cast<float*>(row + (size_t)(2 * s + (lane >> 5)) * 4) = v;
+  }
+  __device__ static inline Raw zero_raw() { return 0.0f; }
+  __device__ static inline Frag frag(Raw v) { return v; }
   // dim of lane `lane` at k-step s: 2 s + lane / 32
   __device__ static inline Frag load(const unsigned char* row, int s, int lane) {
     return *reinterpret_cast<const float*>(row + (size_t)(2 * s + (lane >> 5)) * 4);
@@ -71,6 +97,97 @@ struct Mfma<BKV_F32, D> {
 // r % 4 and output column l % 32 (32x32 MFMA family, checked on gfx950).
 __device__ inline int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// ---------------------------------------------------------------------------
+// RoPE (rotate-half: dim i pairs with dim i + d/2, i < d/2)
+// ---------------------------------------------------------------------------
+
+// tab[n][r][i] = (cos, sin) of the angle of pair i at recent position r
+// (r < R) or at pos_now (r = R); positions below zero give (1, 0).
+template <int D>
+__global__ void rope_table_kernel(const int32_t* __restrict__ recent_pos, const int32_t* __restrict__ pos_now,
+                                  int R, double theta, float2* __restrict__ tab) {
+  const int n = blockIdx.x;
+  constexpr int H = D / 2;
+  float2* out = tab + (size_t)n * (R + 1) * H;
+  for (int e = threadIdx.x; e < (R + 1) * H; e += blockDim.x) {
+    const int r = e / H, i = e % H;
+    const int pos = r < R ? recent_pos[(size_t)n * R + r] : pos_now[n];
+    float2 cs = make_float2(1.0f, 0.0f);
+    if (pos >= 0) {
+      // inverse frequency theta^(-2i/d) held in binary32; the angle pos * freq
+      // is exact in binary64; cos and sin are evaluated in binary64 and held
+      // in binary32
+      const double freq = (double)(float)pow(theta, -(2.0 * i) / (double)D);
+      const double a = (double)pos * freq;
+      cs = make_float2((float)cos(a), (float)sin(a));
+    }
+    out[e] = cs;
+  }
+}
+
+// One rotated pair: binary64 products of a storage value and a binary32
+// cos/sin are exact, so each output is the correctly rounded binary64 value
+// of the exact rotation, rounded once more to the storage type.
+template <int DT>
+__device__ inline void rope_pair(double xa, double xb, float2 cs, typename Elem<DT>::T* ya,
+                                 typename Elem<DT>::T* yb) {
+  const double c = (double)cs.x, sn = (double)cs.y;
+  *ya = Elem<DT>::from_f64(xa * c - xb * sn);
+  *yb = Elem<DT>::from_f64(xb * c + xa * sn);
+}
+
+// Rotates the fragments of one lane in place.  Fragment s and fragment
+// s + kSteps/2 hold the same dims of the two halves of the row.
+template <int DT, int D>
+struct RopeFrag;
+
+template <int D>
+struct RopeFrag<BKV_BF16, D> {
+  static constexpr int KS = D / 16;
+  // dims of fragment s: 16 s + 8 h + [0, 8), h = lane / 32
+  __device__ static inline void rotate(uint4 (&x)[KS], const float2* cs_row, int h) {
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s) {
+      const float4* c4 = reinterpret_cast<const float4*>(cs_row + 16 * s + 8 * h);
+      const float4 c01 = c4[0], c23 = c4[1], c45 = c4[2], c67 = c4[3];
+      const float2 cs[8] = {make_float2(c01.x, c01.y), make_float2(c01.z, c01.w), make_float2(c23.x, c23.y),
+                            make_float2(c23.z, c23.w), make_float2(c45.x, c45.y), make_float2(c45.z, c45.w),
+                            make_float2(c67.x, c67.y), make_float2(c67.z, c67.w)};
+      const uint32_t lo[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+      const uint32_t hi[4] = {x[s + KS / 2].x, x[s + KS / 2].y, x[s + KS / 2].z, x[s + KS / 2].w};
+      uint32_t ylo[4], yhi[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint16_t a0, a1, b0, b1;
+        rope_pair<BKV_BF16>(Elem<BKV_BF16>::to_f64((uint16_t)(lo[w] & 0xFFFF)),
+                            Elem<BKV_BF16>::to_f64((uint16_t)(hi[w] & 0xFFFF)), cs[2 * w], &a0, &b0);
+        rope_pair<BKV_BF16>(Elem<BKV_BF16>::to_f64((uint16_t)(lo[w] >> 16)),
+                            Elem<BKV_BF16>::to_f64((uint16_t)(hi[w] >> 16)), cs[2 * w + 1], &a1, &b1);
+        ylo[w] = (uint32_t)a0 | ((uint32_t)a1 << 16);
+        yhi[w] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      }
+      x[s] = make_uint4(ylo[0], ylo[1], ylo[2], ylo[3]);
+      x[s + KS / 2] = make_uint4(yhi[0], yhi[1], yhi[2], yhi[3]);
+      __builtin_amdgcn_sched_barrier(0);  // one fragment pair at a time (register pressure)
+    }
+  }
+};
+
+template <int D>
+struct RopeFrag<BKV_F32, D> {
+  static constexpr int KS = D / 2;
+  // dim of fragment s: 2 s + h
+  __device__ static inline void rotate(float (&x)[KS], const float2* cs_row, int h) {
+#pragma unroll
+    for (int s = 0; s < KS / 2; ++s) {
+      float a, b;
+      rope_pair<BKV_F32>((double)x[s], (double)x[s + KS / 2], cs_row[2 * s + h], &a, &b);
+      x[s] = a;
+      x[s + KS / 2] = b;
+    }
+  }
+};
+
 template <int DT, int D>
 struct ScoreLayout {
   static constexpr int kRowBytes = D * Elem<DT>::kBytes;
@@ -79,19 +196,24 @@ struct ScoreLayout {
 };
 
 // NW waves per block; the first RP / 32 of them own a row tile each, the
-// others only help to stage K.
+// others only help to stage K.  Observation row r of the unit is, for
+// g = r / (R + nb) and k = r % (R + nb): recent query k of query head
+// h G + g (present if its position is >= 0), or for k >= R its beacon k - R
+// (present if below the pick count); rows from G (R + nb) to RP are padding.
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(64 * NW) void score_kernel(const typename Elem<DT>::T* __restrict__ K,
-                                                        const int32_t* __restrict__ len, int Hkv, int Lmax,
-                                                        const typename Elem<DT>::T* __restrict__ obs,
-                                                        const int32_t* __restrict__ obs_valid, int RP,
-                                                        float* __restrict__ scores, float* __restrict__ lse_out,
-                                                        int32_t* __restrict__ ws_words) {
+__global__ __launch_bounds__(64 * NW) void score_kernel(
+    const typename Elem<DT>::T* __restrict__ K, const int32_t* __restrict__ len, int Hkv, int Hq, int Lmax,
+    const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
+    const typename Elem<DT>::T* __restrict__ qbuf, int C, const int32_t* __restrict__ beacons, int nb,
+    const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid, int RP,
+    float* __restrict__ scores, float* __restrict__ lse_out, int32_t* __restrict__ ws_words) {
   using Lay = ScoreLayout<DT, D>;
   using MF = Mfma<DT, D>;
   using Frag = typename MF::Frag;
+  using Raw = typename MF::Raw;
   constexpr int KS = MF::kSteps;
   constexpr int kU = Lay::kU;
+  constexpr int H = D / 2;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* ktile = smem;                                                    // [kTile][kRowStride]
@@ -101,6 +223,7 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(const typename Elem<DT>:
 
   const size_t unit = blockIdx.x;
   const int n = (int)(unit / Hkv);
+  const int hkv = (int)(unit % Hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -110,23 +233,50 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(const typename Elem<DT>:
     if (tid == 0) set_status(ws_words, BKV_DEV_BAD_LEN);
     return;
   }
-  if (L == 0) return;
 
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(K + unit * (size_t)Lmax * D);
-  const float scale2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
-  const float ninf = -__builtin_huge_valf();
-
-  // query fragment of this wave's 32 rows (lane's row = 32 wave + lane % 32)
+  // this lane's observation row (two lanes per row, h = lane / 32): load it
+  // into fragments, rotate it, keep it, and write the debug copy
   const int myrow = 32 * wave + (lane & 31);
   Frag qf[KS];
   bool row_valid = false;
   if (has_rows) {
-    const unsigned char* qrow =
-        reinterpret_cast<const unsigned char*>(obs + (unit * RP + myrow) * (size_t)D);
+    const int G = Hq / Hkv;
+    const int per = R + nb;  // > 0 whenever RP > 0
+    const int g = min(myrow / per, G - 1);
+    const int k = myrow - (myrow / per) * per;
+    const size_t head = (size_t)n * Hq + (size_t)hkv * G + g;
+    const int32_t* bk = beacons + head * (nb + 1);
+    const unsigned char* src;
+    if (k < R) {
+      row_valid = recent_pos[(size_t)n * R + k] >= 0;
+      src = reinterpret_cast<const unsigned char*>(recent + (head * R + k) * D);
+    } else {
+      row_valid = k - R < bk[0];
+      const int pick = row_valid ? bk[1 + k - R] : 0;
+      src = reinterpret_cast<const unsigned char*>(qbuf + (head * C + pick) * D);
+    }
+    row_valid = row_valid && myrow < G * per;
+    Raw x[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = MF::load(qrow, s, lane);
-    row_valid = obs_valid[unit * RP + myrow] != 0;
+    for (int s2 = 0; s2 < KS; ++s2) x[s2] = MF::load_raw(src, s2, lane);
+    RopeFrag<DT, D>::rotate(x, tab + ((size_t)n * (R + 1) + (k < R ? k : R)) * H, lane >> 5);
+    unsigned char* orow = reinterpret_cast<unsigned char*>(obs + (unit * RP + myrow) * (size_t)D);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      if (!row_valid) x[s2] = MF::zero_raw();
+      MF::store_raw(orow, s2, lane, x[s2]);
+      qf[s2] = MF::frag(x[s2]);
+    }
+    if (lane < 32) obs_valid[unit * RP + myrow] = row_valid ? 1 : 0;
   }
+  if (L == 0) {
+    if (has_rows && lane < 32) lse_out[unit * RP + myrow] = __builtin_huge_valf();
+    return;
+  }
+
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(K + unit * (size_t)Lmax * D);
+  const float scale2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
+  const float ninf = -__builtin_huge_valf();
 
   const int ntiles = (L + kTile - 1) / kTile;
   constexpr int nthreads = 64 * NW;
@@ -251,34 +401,47 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(const typename Elem<DT>:
 }
 
 template <int DT, int D, int NW>
-static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int Hkv, int Lmax, const void* obs,
-                                  const int32_t* obs_valid, int RP, float* scores, float* lse, int32_t* ws_words,
-                                  hipStream_t st) {
+static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax,
+                                  const void* recent, const int32_t* recent_pos, int R, const void* qbuf, int C,
+                                  const int32_t* beacons, int nb, const float2* tab, void* obs, int32_t* obs_valid,
+                                  int RP, float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
   using Lay = ScoreLayout<DT, D>;
   using ET = typename Elem<DT>::T;
   const size_t smem = (size_t)kTile * Lay::kRowStride + (size_t)NW * kTile * sizeof(float) + RP * sizeof(float);
   auto kern = score_kernel<DT, D, NW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(N * Hkv), dim3(64 * NW), smem, st, (const ET*)K, len, Hkv, Lmax, (const ET*)obs,
-                     obs_valid, RP, scores, lse, ws_words);
+  hipLaunchKernelGGL(kern, dim3(N * Hkv), dim3(64 * NW), smem, st, (const ET*)K, len, Hkv, Hq, Lmax,
+                     (const ET*)recent, recent_pos, R, (const ET*)qbuf, C, beacons, nb, tab, (ET*)obs, obs_valid, RP,
+                     scores, lse, ws_words);
   return hipGetLastError();
 }
 
-// RP (observation rows rounded up to 32) is at most 256: 1..8 row tiles.
+// The RoPE table, then the scores.  RP (observation rows rounded up to 32)
+// is at most 256: 1..8 row tiles.
 template <int DT, int D>
-hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int Lmax, const void* obs,
-                        const int32_t* obs_valid, int RP, float* scores, float* lse, int32_t* ws_words,
-                        hipStream_t st) {
+hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax, const void* recent,
+                        const int32_t* recent_pos, int R, const void* qbuf, int C, const int32_t* beacons, int nb,
+                        const int32_t* pos_now, double theta, float2* tab, void* obs, int32_t* obs_valid, int RP,
+                        float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
+  hipLaunchKernelGGL(rope_table_kernel<D>, dim3(N), dim3(256), 0, st, recent_pos, pos_now, R, theta, tab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int tiles = RP / 32;
-  if (tiles <= 2) return launch_score_nw<DT, D, 2>(K, len, N, Hkv, Lmax, obs, obs_valid, RP, scores, lse, ws_words, st);
-  if (tiles <= 4) return launch_score_nw<DT, D, 4>(K, len, N, Hkv, Lmax, obs, obs_valid, RP, scores, lse, ws_words, st);
-  return launch_score_nw<DT, D, 8>(K, len, N, Hkv, Lmax, obs, obs_valid, RP, scores, lse, ws_words, st);
+#define BKV_SCORE_NW(NW)                                                                                      \
+  return launch_score_nw<DT, D, NW>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, qbuf, C, beacons, nb, tab, \
+                                    obs, obs_valid, RP, scores, lse, ws_words, st)
+  if (tiles <= 2) BKV_SCORE_NW(2);
+  if (tiles <= 4) BKV_SCORE_NW(4);
+  BKV_SCORE_NW(8);
+#undef BKV_SCORE_NW
 }
 
-#define BKV_INST_SCORE(DT, D)                                                                                   \
-  template hipError_t launch_score<DT, D>(const void*, const int32_t*, int, int, int, const void*,             \
-                                          const int32_t*, int, float*, float*, int32_t*, hipStream_t);
+#define BKV_INST_SCORE(DT, D)                                                                                  \
+  template hipError_t launch_score<DT, D>(const void*, const int32_t*, int, int, int, int, const void*,       \
+                                          const int32_t*, int, const void*, int, const int32_t*, int,         \
+                                          const int32_t*, double, float2*, void*, int32_t*, int, float*,      \
+                                          float*, int32_t*, hipStream_t);
 BKV_INST_SCORE(BKV_F32, 64)
 BKV_INST_SCORE(BKV_F32, 128)
 BKV_INST_SCORE(BKV_BF16, 64)

@@ -60,7 +60,8 @@ def test_workspace_size_and_layout(lib):
     assert offs[bkv.WS_VALID] - offs[bkv.WS_OBS] >= units * RP * 128 * 2
     assert offs[bkv.WS_LSE] - offs[bkv.WS_VALID] >= units * RP * 4
     assert offs[bkv.WS_ROPE] - offs[bkv.WS_LSE] >= units * RP * 4
-    assert n - offs[bkv.WS_ROPE] >= 2 * 17 * 64 * 8
+    assert offs[bkv.WS_BEACONS] - offs[bkv.WS_ROPE] >= 2 * 17 * 64 * 8
+    assert n - offs[bkv.WS_BEACONS] >= 2 * 32 * 17 * 4
     # rows above 256 and bad shapes give size 0
     assert bkv.bkv_workspace_size(s, 40, 40) == 0
     assert bkv.bkv_workspace_size(shape(head_dim=96), 16, 16) == 0
