@@ -16,38 +16,23 @@ constexpr size_t kHeaderBytes = 256;  // status + statistics block at the front 
 // Storage element types
 // ---------------------------------------------------------------------------
 
-// Round a binary64 value once to bfloat16 (round to nearest, ties to even),
-// working on the binary64 bit pattern: keep the top 8 significant bits of a
-// normal bf16 result, or the bits above 2^-133 for a subnormal one.
+// Round a binary64 value once to bfloat16 (round to nearest, ties to even).
+// Every bfloat16 value, and every midpoint between two neighbours, is a
+// binary32 number.  Rounding to binary32 first (to nearest) therefore never
+// moves the value across such a midpoint: it either lands strictly inside the
+// same half-interval, where the integer round-to-nearest-even of the binary32
+// bits gives the right result, or exactly on a midpoint, where the binary64
+// value decides the direction (ties to even only if it is the midpoint).
 __device__ inline uint16_t bf16_from_f64(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t sign = (uint32_t)(u >> 63) << 15;
-  const int ef = (int)((u >> 52) & 0x7FF);
-  const uint64_t frac = u & ((1ull << 52) - 1);
-  if (ef == 0x7FF) return frac ? (uint16_t)0x7FC0 : (uint16_t)(sign | 0x7F80);
-  if (ef == 0) return (uint16_t)sign;  // |v| < 2^-1022: far below half the smallest bf16
-  int e = ef - 1023;
-  const uint64_t sig = frac | (1ull << 52);  // 53-bit significand, v = sig * 2^(e-52)
-  if (e >= -126) {
-    uint64_t keep = sig >> 45;  // 8 significant bits
-    const uint64_t rem = sig & ((1ull << 45) - 1);
-    const uint64_t half = 1ull << 44;
-    if (rem > half || (rem == half && (keep & 1))) keep += 1;
-    if (keep == 256) {
-      keep = 128;
-      e += 1;
-    }
-    if (e > 127) return (uint16_t)(sign | 0x7F80);
-    return (uint16_t)(sign | ((uint32_t)(e + 127) << 7) | (uint32_t)(keep & 0x7F));
+  const float f = (float)v;
+  if (f != f) return (uint16_t)0x7FC0;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t hi = u >> 16;
+  if ((u & 0xFFFFu) == 0x8000u) {
+    const double a = fabs(v), af = fabs((double)f);
+    return (uint16_t)(a > af ? hi + 1 : (a < af ? hi : hi + (hi & 1)));
   }
-  // subnormal result: count of 2^-133 units, sig * 2^(e-52+133) = sig >> (-81-e)
-  const int sh = -81 - e;  // >= 46
-  if (sh >= 54) return (uint16_t)sign;  // below a quarter unit: rounds to zero
-  uint64_t keep = sig >> sh;
-  const uint64_t rem = sig & ((1ull << sh) - 1);
-  const uint64_t half = 1ull << (sh - 1);
-  if (rem > half || (rem == half && (keep & 1))) keep += 1;
-  return (uint16_t)(sign | (uint32_t)keep);  // keep == 128 encodes 2^-126 exactly
+  return (uint16_t)((u + 0x7FFFu + (hi & 1)) >> 16);
 }
 
 template <int DT>

@@ -234,6 +234,46 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
     return;
   }
 
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(K + unit * (size_t)Lmax * D);
+  const float scale2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
+  const float ninf = -__builtin_huge_valf();
+
+  const int ntiles = (L + kTile - 1) / kTile;
+  constexpr int nthreads = 64 * NW;
+  constexpr int units_per_tile = kTile * kU;
+  constexpr int kPerThreadMax = (units_per_tile + nthreads - 1) / nthreads;
+
+  // register prefetch of one tile: thread handles units tid, tid + nthreads, ...
+  uint4 pre[kPerThreadMax];
+  auto prefetch = [&](int tile) {
+    const int key0 = tile * kTile;
+#pragma unroll
+    for (int k = 0; k < kPerThreadMax; ++k) {
+      const int u = tid + k * nthreads;
+      if (u < units_per_tile) {
+        const int r = u / kU, q = u % kU;
+        if (key0 + r < L) {
+          pre[k] = reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + r) * Lay::kRowBytes)[q];
+        } else {
+          pre[k] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int k = 0; k < kPerThreadMax; ++k) {
+      const int u = tid + k * nthreads;
+      if (u < units_per_tile) {
+        const int r = u / kU, q = u % kU;
+        reinterpret_cast<uint4*>(ktile + (size_t)r * Lay::kRowStride)[q] = pre[k];
+      }
+    }
+  };
+
+  // the first K tile is in flight while the rows are built
+  if (L > 0) prefetch(0);
+
   // this lane's observation row (two lanes per row, h = lane / 32): load it
   // into fragments, rotate it, keep it, and write the debug copy
   const int myrow = 32 * wave + (lane & 31);
@@ -274,46 +314,8 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
     return;
   }
 
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(K + unit * (size_t)Lmax * D);
-  const float scale2 = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(d)
-  const float ninf = -__builtin_huge_valf();
-
-  const int ntiles = (L + kTile - 1) / kTile;
-  constexpr int nthreads = 64 * NW;
-  constexpr int units_per_tile = kTile * kU;
-  constexpr int kPerThreadMax = (units_per_tile + nthreads - 1) / nthreads;
-
-  // register prefetch of one tile: thread handles units tid, tid + nthreads, ...
-  uint4 pre[kPerThreadMax];
-  auto prefetch = [&](int tile) {
-    const int key0 = tile * kTile;
-#pragma unroll
-    for (int k = 0; k < kPerThreadMax; ++k) {
-      const int u = tid + k * nthreads;
-      if (u < units_per_tile) {
-        const int r = u / kU, q = u % kU;
-        if (key0 + r < L) {
-          pre[k] = reinterpret_cast<const uint4*>(kbase + (size_t)(key0 + r) * Lay::kRowBytes)[q];
-        } else {
-          pre[k] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int k = 0; k < kPerThreadMax; ++k) {
-      const int u = tid + k * nthreads;
-      if (u < units_per_tile) {
-        const int r = u / kU, q = u % kU;
-        reinterpret_cast<uint4*>(ktile + (size_t)r * Lay::kRowStride)[q] = pre[k];
-      }
-    }
-  };
-
   // ---------------- pass 1: per-row log2-sum-exp ----------------
   float run_m = ninf, run_s = 0.0f;
-  prefetch(0);
   for (int tile = 0; tile < ntiles; ++tile) {
     __syncthreads();  // previous tile fully consumed
     commit();
