@@ -28,7 +28,46 @@
 namespace bkv {
 
 constexpr int kSelThreads = 256;
+// Units of at most kStageMax entries read their scores (and positions) once
+// into LDS; longer ones read them from global memory on every pass.
+constexpr int kStageMax = 4096;
 
+// Copies n 32-bit words to LDS (16-byte loads where aligned), then syncs.
+__device__ inline void stage_words(uint32_t* dst, const uint32_t* src, int n) {
+  const int tid = threadIdx.x;
+  if ((((uintptr_t)src) & 15) == 0) {
+    const int n4 = n >> 2;
+    for (int i = tid; i < n4; i += kSelThreads)
+      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+    for (int i = 4 * n4 + tid; i < n; i += kSelThreads) dst[i] = src[i];
+  } else {
+    for (int i = tid; i < n; i += kSelThreads) dst[i] = src[i];
+  }
+}
+
+// hist[b] += 1 for every lane with `active`.  The radix digits of one wave
+// are often all equal (scores share their exponent, positions their high
+// bytes), and same-address LDS atomics serialise, so lanes holding the most
+// common digits are first combined into one atomic each (a few ballot
+// rounds); the remaining lanes add individually.  Every lane of the wave must
+// call it.
+__device__ inline void hist_add(int* hist, uint32_t b, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t pending = __ballot(active);
+#pragma unroll
+  for (int round = 0; round < 3; ++round) {
+    if (pending == 0) break;
+    const int leader = __ffsll((long long)pending) - 1;
+    const uint32_t lb = __shfl(b, leader, 64);
+    const uint64_t same = __ballot(active && b == lb) & pending;
+    if (lane == leader) atomicAdd(&hist[lb], __popcll(same));
+    if ((same >> lane) & 1) active = false;
+    pending &= ~same;
+  }
+  if (active) atomicAdd(&hist[b], 1);
+}
+
+template <bool kStaged>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores,
                                                              const int32_t* __restrict__ len, int Hkv, int Lmax,
                                                              int B, int W, int32_t* __restrict__ kept,
@@ -58,7 +97,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
     }
     return;
   }
+  extern __shared__ uint32_t stage[];
   const uint32_t* u = reinterpret_cast<const uint32_t*>(scores + unit * (size_t)Lmax);
+  if constexpr (kStaged) {
+    stage_words(stage, u, L);
+    __syncthreads();
+    u = stage;
+  }
   const int ncand = L - W;  // candidates [0, L - W)
   const int want = B - W;   // how many candidates survive
 
@@ -70,9 +115,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
       const int shift = 24 - 8 * pass;
       for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
       __syncthreads();
-      for (int j = tid; j < ncand; j += kSelThreads) {
-        const uint32_t x = u[j];
-        if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255], 1);
+      for (int j0 = 0; j0 < ncand; j0 += kSelThreads) {
+        const int j = j0 + tid;
+        const uint32_t x = j < ncand ? u[j] : 0u;
+        hist_add(hist, (x >> shift) & 255, j < ncand && (x & mask) == prefix);
       }
       __syncthreads();
       // suffix sums from the top bucket: thread t owns bucket 255 - t
@@ -241,9 +287,11 @@ __device__ inline uint32_t radix_cut(KeyFn key, int n, int want, int* hist, int*
     const int shift = 24 - 8 * pass;
     for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kSelThreads) {
-      uint32_t k;
-      if (key(j, k) && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1);
+    for (int j0 = 0; j0 < n; j0 += kSelThreads) {
+      const int j = j0 + tid;
+      uint32_t k = 0;
+      const bool act = j < n && key(j, k) && (k & mask) == prefix;
+      hist_add(hist, (k >> shift) & 255, act);
     }
     __syncthreads();
     const int b = 255 - tid;  // thread t owns bucket 255 - t (kSelThreads == 256)
@@ -267,6 +315,7 @@ __device__ inline uint32_t radix_cut(KeyFn key, int n, int want, int* hist, int*
   return prefix;
 }
 
+template <bool kStaged>
 __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* __restrict__ scores,
                                                                   const int32_t* __restrict__ pos,
                                                                   const int32_t* __restrict__ len, int Hkv, int Lmax,
@@ -299,15 +348,53 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
     }
     return;
   }
+  extern __shared__ uint32_t stage[];
   const uint32_t* u = reinterpret_cast<const uint32_t*>(scores + unit * (size_t)Lmax);
   const int32_t* pp = pos + unit * (size_t)Lmax;
+  if constexpr (kStaged) {
+    stage_words(stage, u, L);
+    const int ls = (Lmax + 3) & ~3;  // positions follow the scores, 16-byte aligned
+    stage_words(stage + ls, reinterpret_cast<const uint32_t*>(pp), L);
+    __syncthreads();
+    u = stage;
+    pp = reinterpret_cast<const int32_t*>(stage + ls);
+  }
   // signed positions -> unsigned keys in the same order
   auto pkey = [pp](int j) { return (uint32_t)pp[j] ^ 0x80000000u; };
 
-  // the window: the W largest position keys, ties to the lower row
+  // the window: the W largest position keys, ties to the lower row.  When the
+  // last W rows hold positions above every other row's (tokens appended in
+  // order since the last eviction), they are that window; otherwise radix
+  // selections find it.
   uint32_t wt = 0;
   int wrow = 0x7fffffff;
+  bool tail_window = false;
   if (W > 0) {
+    uint32_t head_max = 0u, tail_min = 0xFFFFFFFFu;
+    for (int j = tid; j < L; j += kSelThreads) {
+      const uint32_t k = pkey(j);
+      if (j < L - W) head_max = k > head_max ? k : head_max;
+      else tail_min = k < tail_min ? k : tail_min;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint32_t a = __shfl_xor(head_max, off, 64), b = __shfl_xor(tail_min, off, 64);
+      head_max = a > head_max ? a : head_max;
+      tail_min = b < tail_min ? b : tail_min;
+    }
+    if ((tid & 63) == 0) {
+      scan_tmp[tid >> 6] = (int)head_max;
+      scan_tmp[8 + (tid >> 6)] = (int)tail_min;
+    }
+    __syncthreads();
+    for (int w = 0; w < kSelThreads / 64; ++w) {
+      head_max = (uint32_t)scan_tmp[w] > head_max ? (uint32_t)scan_tmp[w] : head_max;
+      tail_min = (uint32_t)scan_tmp[8 + w] < tail_min ? (uint32_t)scan_tmp[8 + w] : tail_min;
+    }
+    __syncthreads();
+    // with no row before the tail (L == W) the tail is trivially the window
+    tail_window = L == W || tail_min > head_max;
+  }
+  if (W > 0 && !tail_window) {
     int take, neq;
     wt = radix_cut([&](int j, uint32_t& k) { k = pkey(j); return true; }, L, W, hist, scan_tmp, bcast, &take, &neq);
     if (take < neq) {  // equal positions straddle the cut: the lowest `take` rows of them
@@ -318,6 +405,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
   }
   auto in_win = [&](int j) -> bool {
     if (W == 0) return false;
+    if (tail_window) return j >= L - W;
     const uint32_t k = pkey(j);
     return k > wt || (k == wt && j <= wrow);
   };
@@ -488,8 +576,12 @@ __global__ __launch_bounds__(kCompactThreads) void compact_fill_kernel(unsigned 
 
 hipError_t launch_select(const float* scores, const int32_t* len, int N, int Hkv, int Lmax, int B, int W,
                          int32_t* kept, int32_t* sel, int32_t* ws_words, hipStream_t st) {
-  hipLaunchKernelGGL(select_kernel, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, len, Hkv, Lmax, B, W, kept, sel,
-                     ws_words);
+  if (Lmax <= kStageMax)
+    hipLaunchKernelGGL(select_kernel<true>, dim3(N * Hkv), dim3(kSelThreads), Lmax * sizeof(uint32_t), st, scores,
+                       len, Hkv, Lmax, B, W, kept, sel, ws_words);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, len, Hkv, Lmax, B, W,
+                       kept, sel, ws_words);
   return hipGetLastError();
 }
 
@@ -502,8 +594,13 @@ hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* 
 
 hipError_t launch_select_fill(const float* scores, const int32_t* pos, const int32_t* len, int N, int Hkv, int Lmax,
                               int B, int W, int32_t* kept, int32_t* sel, int32_t* ws_words, hipStream_t st) {
-  hipLaunchKernelGGL(select_fill_kernel, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, pos, len, Hkv, Lmax, B, W,
-                     kept, sel, ws_words);
+  if (Lmax <= kStageMax)
+    hipLaunchKernelGGL(select_fill_kernel<true>, dim3(N * Hkv), dim3(kSelThreads),
+                       2 * ((Lmax + 3) & ~3) * sizeof(uint32_t), st, scores, pos, len, Hkv, Lmax, B, W, kept, sel,
+                       ws_words);
+  else
+    hipLaunchKernelGGL(select_fill_kernel<false>, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, pos, len, Hkv,
+                       Lmax, B, W, kept, sel, ws_words);
   return hipGetLastError();
 }
 
