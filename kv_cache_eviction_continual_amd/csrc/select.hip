@@ -1,18 +1,21 @@
 // select.hip -- top-B_KV selection with an always-kept window, and in-place
-// order-preserving compaction of K and V, on gfx950.
+// compaction of K and V (order-preserving, or hole-filling with positions),
+// on gfx950.
 //
 // Selection (inkeast.github.io MessageDaily paper-reading post on BeaconKV,
 // section 三: I = TopK(score(K,V), B_KV); aimodeling.com "BeaconKV: Beacon
 // Queries Fix KV Eviction for Long Reasoning", section "Beacon queries
 // anticipate what will be revisited": the recent sliding window is always
 // kept).  B_KV counts the window; the other B_KV - W entries are the highest
-// scores of [0, L - W), ties at the cut going to the lower index.
+// scores of the rest, ties at the cut going to the lower index (the older
+// position in the hole-filling layout).
 //
-// select_kernel: one workgroup per (slot, KV head).  Scores are non-negative
-// floats, so their bit patterns order like the values; an MSB-first radix
-// select (4 passes of 8 bits, LDS histograms) finds the cut value tau and
-// how many entries equal to tau are taken.  One more pass marks the kept
-// entries in index order (block prefix sums) and writes them ascending.
+// select_kernel / select_fill_kernel: one workgroup per (slot, KV head).
+// Scores are non-negative floats, so their bit patterns order like the
+// values; MSB-first radix selections (4 passes of 8 bits, LDS histograms)
+// find each cut value and how many entries equal to it are taken.  A final
+// pass gives every thread a contiguous run of entries, so one block scan
+// ranks all kept (or evicted) entries in index order.
 //
 // compact_kernel: one workgroup per (slot, KV head, tensor).  Row i <- row
 // kept[i] for i from the first evicted index up to the kept count.  Because
@@ -32,7 +35,8 @@ constexpr int kSelThreads = 256;
 // into LDS; longer ones read them from global memory on every pass.
 constexpr int kStageMax = 4096;
 
-// Copies n 32-bit words to LDS (16-byte loads where aligned), then syncs.
+// Copies n 32-bit words to LDS (16-byte loads where aligned); the caller
+// synchronises.
 __device__ inline void stage_words(uint32_t* dst, const uint32_t* src, int n) {
   const int tid = threadIdx.x;
   if ((((uintptr_t)src) & 15) == 0) {
@@ -67,12 +71,114 @@ __device__ inline void hist_add(int* hist, uint32_t b, bool active) {
   if (active) atomicAdd(&hist[b], 1);
 }
 
+// Largest-first radix cut over the entries j in [0, n) for which key(j, k)
+// returns true (and sets their key k).  Finds the want-th largest key, for
+// 1 <= want <= the number of such entries; *take receives how many entries
+// equal to it the first `want` include, *n_eq how many entries equal it.
+// Every thread of the block must call it with the same arguments.
+template <class KeyFn>
+__device__ inline uint32_t radix_cut(KeyFn key, int n, int want, int* hist, int* scan_tmp, int* bcast, int* take,
+                                     int* n_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = want, eq = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
+    for (int j0 = 0; j0 < n; j0 += kSelThreads) {
+      const int j = j0 + tid;
+      uint32_t k = 0;
+      const bool act = j < n && key(j, k) && (k & mask) == prefix;
+      hist_add(hist, (k >> shift) & 255, act);
+    }
+    __syncthreads();
+    const int b = 255 - tid;  // thread t owns bucket 255 - t (kSelThreads == 256)
+    const int cnt = hist[b];
+    int total;
+    const int above = block_exclusive_scan(cnt, scan_tmp, &total);
+    if (above < remaining && remaining <= above + cnt) {
+      bcast[0] = b;
+      bcast[1] = remaining - above;
+      bcast[2] = cnt;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bcast[0] << shift;
+    mask |= 255u << shift;
+    remaining = bcast[1];
+    eq = bcast[2];
+    __syncthreads();
+  }
+  *take = remaining;
+  *n_eq = eq;
+  return prefix;
+}
+
+// Thread t's contiguous run [*a, *b) of [lo, hi).  The run length is odd, so
+// the lanes of a wave reading the k-th entry of their runs from LDS hit
+// distinct banks.
+__device__ inline void thread_run(int lo, int hi, int* a, int* b) {
+  const int per = ((hi - lo + kSelThreads - 1) / kSelThreads) | 1;
+  *a = min(hi, lo + (int)threadIdx.x * per);
+  *b = min(hi, *a + per);
+}
+
+// Index of the last of the first `take` entries of [lo, hi) with pred(j),
+// in index order (take >= 1 and at most their number).
+template <class Pred>
+__device__ inline int nth_in_order(int lo, int hi, int take, Pred pred, int* scan_tmp, int* slot) {
+  int a, b;
+  thread_run(lo, hi, &a, &b);
+  int cnt = 0;
+  for (int j = a; j < b; ++j) cnt += pred(j) ? 1 : 0;
+  int total;
+  int r = block_exclusive_scan(cnt, scan_tmp, &total);
+  for (int j = a; j < b; ++j)
+    if (pred(j)) {
+      if (r == take - 1) *slot = j;
+      ++r;
+    }
+  __syncthreads();
+  const int v = *slot;
+  __syncthreads();
+  return v;
+}
+
+// Block minimum of one unsigned int per thread.
+__device__ inline uint32_t block_min_u32(uint32_t v, int* scan_tmp) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, 64);
+    v = o < v ? o : v;
+  }
+  if ((threadIdx.x & 63) == 0) scan_tmp[threadIdx.x >> 6] = (int)v;
+  __syncthreads();
+  uint32_t m = (uint32_t)scan_tmp[0];
+  for (int w = 1; w < kSelThreads / 64; ++w) m = (uint32_t)scan_tmp[w] < m ? (uint32_t)scan_tmp[w] : m;
+  __syncthreads();
+  return m;
+}
+
+// Block minimum of one int per thread.
+__device__ inline int block_min(int v, int* scan_tmp) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const int o = __shfl_xor(v, off, 64);
+    v = o < v ? o : v;
+  }
+  if ((threadIdx.x & 63) == 0) scan_tmp[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int m = scan_tmp[0];
+  for (int w = 1; w < kSelThreads / 64; ++w) m = scan_tmp[w] < m ? scan_tmp[w] : m;
+  __syncthreads();
+  return m;
+}
+
 template <bool kStaged>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores,
                                                              const int32_t* __restrict__ len, int Hkv, int Lmax,
                                                              int B, int W, int32_t* __restrict__ kept,
                                                              int32_t* __restrict__ sel,
                                                              int32_t* __restrict__ ws_words) {
+  static_assert(kSelThreads == 256, "one radix bucket per thread");
   __shared__ int hist[256];
   __shared__ int scan_tmp[16];
   __shared__ int bcast[4];
@@ -107,76 +213,38 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __rest
   const int ncand = L - W;  // candidates [0, L - W)
   const int want = B - W;   // how many candidates survive
 
-  // radix select of the want-th largest bit pattern among the candidates
-  uint32_t prefix = 0, mask = 0;
-  int remaining = want;  // entries still to take at or below the current prefix
+  // the cut value among the candidates; when entries equal to it straddle
+  // the cut, the lowest indices of them are kept up to eq_last
+  uint32_t tau = 0;
+  int eq_last = 0x7fffffff;
   if (want > 0) {
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
-      __syncthreads();
-      for (int j0 = 0; j0 < ncand; j0 += kSelThreads) {
-        const int j = j0 + tid;
-        const uint32_t x = j < ncand ? u[j] : 0u;
-        hist_add(hist, (x >> shift) & 255, j < ncand && (x & mask) == prefix);
-      }
-      __syncthreads();
-      // suffix sums from the top bucket: thread t owns bucket 255 - t
-      const int b = 255 - tid;
-      int cnt = tid < 256 ? hist[b] : 0;
-      int total;
-      const int above = block_exclusive_scan(cnt, scan_tmp, &total);  // entries in buckets > b
-      if (tid < 256 && above < remaining && remaining <= above + cnt) {
-        bcast[0] = b;
-        bcast[1] = remaining - above;
-      }
-      __syncthreads();
-      prefix |= (uint32_t)bcast[0] << shift;
-      mask |= 255u << shift;
-      remaining = bcast[1];
-      __syncthreads();
-    }
+    int take, neq;
+    tau = radix_cut([&](int j, uint32_t& k) { k = u[j]; return true; }, ncand, want, hist, scan_tmp, bcast, &take,
+                    &neq);
+    if (take < neq) eq_last = nth_in_order(0, ncand, take, [&](int j) { return u[j] == tau; }, scan_tmp, &bcast[3]);
   }
-  const uint32_t tau = prefix;  // exact bit pattern of the cut value
-  const int take_eq = remaining; // entries equal to tau to keep, lowest index first
+  auto keep = [&](int j) -> bool {
+    if (j >= ncand) return true;  // the window
+    if (want <= 0) return false;
+    const uint32_t x = u[j];
+    return x > tau || (x == tau && j <= eq_last);
+  };
 
-  // mark and write: kept = (x > tau) or (x == tau and among the first take_eq
-  // equal entries) over the candidates, plus the window
-  int eq_base = 0, out_base = 0;
-  int first_hole = 0x7fffffff;
-  for (int j0 = 0; j0 < L; j0 += kSelThreads) {
-    const int j = j0 + tid;
-    bool gt = false, eq = false, win = false;
-    if (j < ncand) {
-      if (want > 0) {
-        const uint32_t x = u[j];
-        gt = x > tau;
-        eq = x == tau;
-      }
-    } else if (j < L) {
-      win = true;
-    }
-    int eq_total;
-    const int eq_rank = block_exclusive_scan(eq ? 1 : 0, scan_tmp, &eq_total);
-    const bool keep = gt || win || (eq && eq_base + eq_rank < take_eq);
-    int keep_total;
-    const int pos = block_exclusive_scan(keep ? 1 : 0, scan_tmp, &keep_total);
-    if (keep) kept_u[out_base + pos] = j;
-    if (j < L && !keep && j < first_hole) first_hole = j;
-    eq_base += eq_total;
-    out_base += keep_total;
+  // kept indices ascending, and the first evicted index
+  int a, b;
+  thread_run(0, L, &a, &b);
+  int cnt = 0, hole = 0x7fffffff;
+  for (int j = a; j < b; ++j) {
+    if (keep(j)) ++cnt;
+    else if (j < hole) hole = j;
   }
-  // block minimum of first_hole
-  for (int off = 32; off > 0; off >>= 1) {
-    int o = __shfl_xor(first_hole, off, 64);
-    first_hole = o < first_hole ? o : first_hole;
-  }
-  if ((tid & 63) == 0) scan_tmp[tid >> 6] = first_hole;
-  __syncthreads();
+  int total;
+  int r = block_exclusive_scan(cnt, scan_tmp, &total);
+  for (int j = a; j < b; ++j)
+    if (keep(j)) kept_u[r++] = j;
+  const int first_hole = block_min(hole, scan_tmp);
   if (tid == 0) {
-    int f = scan_tmp[0];
-    for (int w = 1; w < kSelThreads / 64; ++w) f = scan_tmp[w] < f ? scan_tmp[w] : f;
-    sel[2 * unit] = f < B ? f : B;
+    sel[2 * unit] = first_hole < B ? first_hole : B;
     sel[2 * unit + 1] = B;
   }
 }
@@ -263,57 +331,14 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(unsigned char*
 // stay in position order.  select_fill_kernel keeps the W newest positions
 // (ties: the lower row) and the B - W highest scores of the other rows (ties:
 // the older position, then the lower row).  Each of these orders is found by
-// MSB-first radix selections over 32-bit keys that order like the quantity;
-// a further selection runs only when entries tie at a cut.  The evicted rows
-// of [0, B) ("holes") are then paired, in ascending order, with the kept rows
-// of [B, L) ("fillers"): kept[i] = i for a kept row below B, else its filler.
+// radix cuts over 32-bit keys that order like the quantity; a further cut
+// runs only when entries tie at a cut.  The evicted rows of [0, B) ("holes")
+// are then paired, in ascending order, with the kept rows of [B, L)
+// ("fillers"): kept[i] = i for a kept row below B, else its filler.
 // compact_fill_kernel moves only the fillers.  Destinations lie below B and
 // sources at or beyond it, so no copy reads a row that another one writes.
 
 constexpr int kFillChunk = 1024;  // fillers paired per sweep (LDS list)
-
-// Largest-first radix cut over the entries j in [0, n) for which key(j, k)
-// returns true (and sets their key k).  Finds the want-th largest key, for
-// 1 <= want <= the number of such entries; *take receives how many entries
-// equal to it the first `want` include, *n_eq how many entries equal it.
-// Every thread of the block must call it with the same arguments.
-template <class KeyFn>
-__device__ inline uint32_t radix_cut(KeyFn key, int n, int want, int* hist, int* scan_tmp, int* bcast, int* take,
-                                     int* n_eq) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  int remaining = want, eq = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
-    __syncthreads();
-    for (int j0 = 0; j0 < n; j0 += kSelThreads) {
-      const int j = j0 + tid;
-      uint32_t k = 0;
-      const bool act = j < n && key(j, k) && (k & mask) == prefix;
-      hist_add(hist, (k >> shift) & 255, act);
-    }
-    __syncthreads();
-    const int b = 255 - tid;  // thread t owns bucket 255 - t (kSelThreads == 256)
-    const int cnt = hist[b];
-    int total;
-    const int above = block_exclusive_scan(cnt, scan_tmp, &total);
-    if (above < remaining && remaining <= above + cnt) {
-      bcast[0] = b;
-      bcast[1] = remaining - above;
-      bcast[2] = cnt;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)bcast[0] << shift;
-    mask |= 255u << shift;
-    remaining = bcast[1];
-    eq = bcast[2];
-    __syncthreads();
-  }
-  *take = remaining;
-  *n_eq = eq;
-  return prefix;
-}
 
 template <bool kStaged>
 __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* __restrict__ scores,
@@ -365,7 +390,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
   // the window: the W largest position keys, ties to the lower row.  When the
   // last W rows hold positions above every other row's (tokens appended in
   // order since the last eviction), they are that window; otherwise radix
-  // selections find it.
+  // cuts find it.
   uint32_t wt = 0;
   int wrow = 0x7fffffff;
   bool tail_window = false;
@@ -376,32 +401,15 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
       if (j < L - W) head_max = k > head_max ? k : head_max;
       else tail_min = k < tail_min ? k : tail_min;
     }
-    for (int off = 32; off > 0; off >>= 1) {
-      const uint32_t a = __shfl_xor(head_max, off, 64), b = __shfl_xor(tail_min, off, 64);
-      head_max = a > head_max ? a : head_max;
-      tail_min = b < tail_min ? b : tail_min;
-    }
-    if ((tid & 63) == 0) {
-      scan_tmp[tid >> 6] = (int)head_max;
-      scan_tmp[8 + (tid >> 6)] = (int)tail_min;
-    }
-    __syncthreads();
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      head_max = (uint32_t)scan_tmp[w] > head_max ? (uint32_t)scan_tmp[w] : head_max;
-      tail_min = (uint32_t)scan_tmp[8 + w] < tail_min ? (uint32_t)scan_tmp[8 + w] : tail_min;
-    }
-    __syncthreads();
-    // with no row before the tail (L == W) the tail is trivially the window
-    tail_window = L == W || tail_min > head_max;
+    head_max = ~block_min_u32(~head_max, scan_tmp);  // max(x) = ~min(~x)
+    tail_min = block_min_u32(tail_min, scan_tmp);
+    tail_window = tail_min > head_max;
   }
   if (W > 0 && !tail_window) {
     int take, neq;
     wt = radix_cut([&](int j, uint32_t& k) { k = pkey(j); return true; }, L, W, hist, scan_tmp, bcast, &take, &neq);
-    if (take < neq) {  // equal positions straddle the cut: the lowest `take` rows of them
-      int t2, n2;
-      wrow = (int)~radix_cut([&](int j, uint32_t& k) { k = ~(uint32_t)j; return pkey(j) == wt; }, L, take, hist,
-                             scan_tmp, bcast, &t2, &n2);
-    }
+    if (take < neq)  // equal positions straddle the cut: the lowest rows of them
+      wrow = nth_in_order(0, L, take, [&](int j) { return pkey(j) == wt; }, scan_tmp, &bcast[3]);
   }
   auto in_win = [&](int j) -> bool {
     if (W == 0) return false;
@@ -426,13 +434,8 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
                      scan_tmp, bcast, &t2, &n2);
       if (t2 < n2) {
         all_pt = false;
-        int t3, n3;
-        prow = (int)~radix_cut(
-            [&](int j, uint32_t& k) {
-              k = ~(uint32_t)j;
-              return u[j] == st && ~pkey(j) == pt && !in_win(j);
-            },
-            L, t2, hist, scan_tmp, bcast, &t3, &n3);
+        prow = nth_in_order(0, L, t2, [&](int j) { return u[j] == st && ~pkey(j) == pt && !in_win(j); }, scan_tmp,
+                            &bcast[3]);
       }
     }
   }
@@ -447,8 +450,10 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
     return all_pt || j <= prow;
   };
 
-  // pair the holes of [0, B) with the fillers of [B, L), kFillChunk at a time
-  int first_hole = B;
+  // pair the holes of [0, B) with the fillers of [B, L), kFillChunk at a
+  // time (one predicate evaluation per row and sweep: cheaper here than
+  // contiguous runs, which evaluate each row three times)
+  int hole = 0x7fffffff;
   for (int r0 = 0;; r0 += kFillChunk) {
     int base = 0;
     for (int j0 = B; j0 < L; j0 += kSelThreads) {
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
         if (!h) {
           if (r0 == 0) kept_u[i] = i;
         } else {
-          if (i < first_hole) first_hole = i;
+          if (i < hole) hole = i;
           // r < nfill always (as many holes as fillers); the guard keeps every
           // LDS read inside the filled part of the list
           if (r >= r0 && r < r0 + kFillChunk) kept_u[i] = r < nfill ? fillers[r - r0] : i;
@@ -482,16 +487,9 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
     __syncthreads();
     if (r0 + kFillChunk >= nfill) break;
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    const int o = __shfl_xor(first_hole, off, 64);
-    first_hole = o < first_hole ? o : first_hole;
-  }
-  if ((tid & 63) == 0) scan_tmp[tid >> 6] = first_hole;
-  __syncthreads();
+  const int first_hole = block_min(hole, scan_tmp);
   if (tid == 0) {
-    int f = scan_tmp[0];
-    for (int w = 1; w < kSelThreads / 64; ++w) f = scan_tmp[w] < f ? scan_tmp[w] : f;
-    sel[2 * unit] = f;
+    sel[2 * unit] = first_hole < B ? first_hole : B;
     sel[2 * unit + 1] = B;
   }
 }
