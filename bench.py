@@ -92,32 +92,135 @@ class State:
             bkv.bkv_fps_update(self.shape, blk, blk.shape[2], self.qbuf, self.qcount, w.capacity, w.shrink_to, self.ws)
         torch.cuda.synchronize()
 
-    def step(self, i, ev=None):
+    def block(self, i):
+        return (self.n_warm + i) % self.n_pool
+
+    def ingest(self, i, stream):
         w = self.w
-        p = (self.n_warm + i) % self.n_pool
-        e = i % N_EVENTS
-        if ev is not None:
-            ev[0].record()
-        self.length.copy_(self.len_full)
-        if ev is not None:
-            ev[1].record()
-        bkv.bkv_fps_update(self.shape, self.blocks[p], w.interval, self.qbuf, self.qcount, w.capacity, w.shrink_to,
-                           self.ws)
-        if ev is not None:
-            ev[2].record()
+        bkv.bkv_fps_update(self.shape, self.blocks[self.block(i)], w.interval, self.qbuf, self.qcount, w.capacity,
+                           w.shrink_to, self.ws, stream=stream)
+
+    def score(self, i, stream):
+        w = self.w
+        p, e = self.block(i), i % N_EVENTS
         bkv.bkv_score(self.shape, self.K, self.length, self.recent[p], self.recent_pos[e], w.n_recent, self.qbuf,
-                      self.qcount, w.capacity, w.n_beacons, self.pos_now[e], w.rope_theta, self.scores, self.ws)
-        if ev is not None:
-            ev[3].record()
-        bkv.bkv_select(self.shape, self.scores, self.length, w.budget, w.window, self.kept, self.ws)
-        if ev is not None:
-            ev[4].record()
-        bkv.bkv_compact(self.shape, self.K, self.V, self.length, w.budget, self.kept, self.ws)
-        if ev is not None:
-            ev[5].record()
+                      self.qcount, w.capacity, w.n_beacons, self.pos_now[e], w.rope_theta, self.scores, self.ws,
+                      stream=stream)
+
+    def picks(self, stream):
+        w = self.w
+        bkv.bkv_beacon_picks(self.shape, self.qbuf, self.qcount, w.capacity, w.n_recent, w.n_beacons, self.ws,
+                             stream=stream)
+
+    def score_picked(self, i, stream):
+        w = self.w
+        p, e = self.block(i), i % N_EVENTS
+        bkv.bkv_score_picked(self.shape, self.K, self.length, self.recent[p], self.recent_pos[e], w.n_recent,
+                             w.n_beacons, self.pos_now[e], w.rope_theta, self.scores, self.ws, stream=stream)
 
 
-def time_hole_fill(st, warmup, steps):
+STAGES = ("grow", "fps_update", "beacon_picks", "score", "select", "compact")
+
+
+class Schedule:
+    """Enqueues eviction passes i = 0, 1, ... in order.
+
+    grow(i) resets the cache length (and writes new positions), tail(i)
+    selects and compacts; both run on the main stream.  Serial: ingest and
+    scoring (beacon FPS included) of pass i also run there, in order.
+    Overlapped: a second stream (default priority) runs the ingest and then
+    the beacon FPS of pass i + 1 while the main stream scores, selects and
+    compacts pass i.  The ingest only follows pass i's beacon FPS (same
+    stream; scoring reads copies of the picked rows, not the buffers); the
+    beacon FPS of pass i + 1 waits for pass i's scoring (the reader of the
+    picks), and pass i + 1's scoring waits for it.  Every pass does the same
+    work either way.  `ev` is a dict of (start, end) event pairs per stage,
+    or None; in the serial schedule the score stage includes the beacon FPS."""
+
+    def __init__(self, st, grow, tail, overlap):
+        self.st, self.grow, self.tail, self.overlap = st, grow, tail, overlap
+        self.main = torch.cuda.current_stream()
+        self.side = torch.cuda.Stream() if overlap else None
+        self.ready = None  # beacon FPS of the next pass enqueued on the side stream
+        self.scored = None
+
+    def _side_work(self, i, ev):
+        side = self.side
+        if ev is not None:
+            ev["fps_update"][0].record(side)
+        self.st.ingest(i, side)
+        if ev is not None:
+            ev["fps_update"][1].record(side)
+        if self.scored is not None:
+            side.wait_event(self.scored)
+        if ev is not None:
+            ev["beacon_picks"][0].record(side)
+        self.st.picks(side)
+        if ev is not None:
+            ev["beacon_picks"][1].record(side)
+        self.ready = torch.cuda.Event()
+        self.ready.record(side)
+
+    def prime(self, i):
+        """Enqueues pass i's ingest and beacon FPS ahead of time (overlapped schedule)."""
+        if self.overlap and self.ready is None:
+            self.scored = torch.cuda.Event()
+            self.scored.record(self.main)
+            self._side_work(i, None)
+
+    def run(self, i, ev=None):
+        st, m = self.st, self.main
+        rec = (lambda name, k: ev[name][k].record(m)) if ev is not None else (lambda name, k: None)
+        if self.overlap:
+            self.prime(i)
+            m.wait_event(self.ready)
+        rec("grow", 0)
+        self.grow(i)
+        rec("grow", 1)
+        if not self.overlap:
+            rec("fps_update", 0)
+            st.ingest(i, m)
+            rec("fps_update", 1)
+        rec("score", 0)
+        if self.overlap:
+            st.score_picked(i, m)
+        else:
+            st.score(i, m)
+        rec("score", 1)
+        if self.overlap:
+            self.scored = torch.cuda.Event()
+            self.scored.record(m)
+            self._side_work(i + 1, ev)  # measured as this pass's ingest and beacon FPS stages
+        self.tail(i, rec)
+
+
+def new_events(overlap):
+    names = STAGES if overlap else tuple(n for n in STAGES if n != "beacon_picks")
+    return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+
+
+def timed_passes(sched, warmup, steps, ws):
+    """warmup untimed passes, then `steps` timed ones between two device
+    synchronisations; returns (seconds, per-stage mean ms)."""
+    for i in range(warmup):
+        sched.run(i)
+    sched.prime(warmup)  # the first timed pass's ingest stays outside the timed region
+    torch.cuda.synchronize()
+    bkv.bkv_reset_device_status(ws)
+    evs = [new_events(sched.overlap) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sched.run(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = bkv.bkv_read_device_status(ws)
+    assert status == 0, "device status %d" % status
+    stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in evs[0]}
+    return elapsed, stage_ms
+
+
+def time_hole_fill(st, warmup, steps, overlap):
     """The same eviction pass in the hole-filling layout (rows carry their
     positions; only kept rows beyond the budget move).  Runs on the state the
     order-preserving phase left; each pass first appends the positions of the
@@ -131,46 +234,20 @@ def time_hole_fill(st, warmup, steps):
     fresh = [torch.full((N, Hkv, new_rows), w.max_len + new_rows * i, dtype=torch.int32, device=dev)
              + torch.arange(new_rows, dtype=torch.int32, device=dev) for i in range(min(steps + warmup, 64))]
 
-    def step(i, ev=None):
-        p = (st.n_warm + i) % st.n_pool
-        e = i % N_EVENTS
-        if ev is not None:
-            ev[0].record()
+    def grow(i):
         st.length.copy_(st.len_full)
         pos[:, :, B:L].copy_(fresh[i % len(fresh)] + new_rows * len(fresh) * (i // len(fresh)))
-        if ev is not None:
-            ev[1].record()
-        bkv.bkv_fps_update(st.shape, st.blocks[p], w.interval, st.qbuf, st.qcount, w.capacity, w.shrink_to, st.ws)
-        if ev is not None:
-            ev[2].record()
-        bkv.bkv_score(st.shape, st.K, st.length, st.recent[p], st.recent_pos[e], w.n_recent, st.qbuf, st.qcount,
-                      w.capacity, w.n_beacons, st.pos_now[e], w.rope_theta, st.scores, st.ws)
-        if ev is not None:
-            ev[3].record()
-        bkv.bkv_select_fill(st.shape, st.scores, pos, st.length, B, w.window, st.kept, st.ws)
-        if ev is not None:
-            ev[4].record()
-        bkv.bkv_compact_fill(st.shape, st.K, st.V, pos, st.length, B, st.kept, st.ws)
-        if ev is not None:
-            ev[5].record()
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    bkv.bkv_reset_device_status(st.ws)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(warmup + i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    status = bkv.bkv_read_device_status(st.ws)
-    assert status == 0, "device status %d" % status
+    def tail(i, rec):
+        rec("select", 0)
+        bkv.bkv_select_fill(st.shape, st.scores, pos, st.length, B, w.window, st.kept, st.ws)
+        rec("select", 1)
+        rec("compact", 0)
+        bkv.bkv_compact_fill(st.shape, st.K, st.V, pos, st.length, B, st.kept, st.ws)
+        rec("compact", 1)
+
+    elapsed, stage_ms = timed_passes(Schedule(st, grow, tail, overlap), warmup, steps, st.ws)
     rows_moved = bkv.ws_rows_moved(st.ws)
-    names = ["grow", "fps_update", "score", "select", "compact"]
-    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
-                for j, n in enumerate(names)}
     row_bytes = w.head_dim * 2
     moved_per_pass = rows_moved / steps                       # K and V rows
     compact_bytes = moved_per_pass * row_bytes * 2 + moved_per_pass / 2 * 4 * 2  # rows + positions, read + write
@@ -280,6 +357,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-hole-fill", action="store_true", help="skip the hole-filling layout phase")
+    ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped-schedule measurement")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -300,27 +378,21 @@ def main():
     cp = copy_probe(dev)
     log("copy probe: %.0f GB/s" % cp["GBps"])
 
-    for i in range(args.warmup):
-        st.step(i)
-    torch.cuda.synchronize()
-    bkv.bkv_reset_device_status(st.ws)
-    torch.cuda.synchronize()
+    def grow(i):
+        st.length.copy_(st.len_full)
+
+    def tail(i, rec):
+        rec("select", 0)
+        bkv.bkv_select(st.shape, st.scores, st.length, w.budget, w.window, st.kept, st.ws)
+        rec("select", 1)
+        rec("compact", 0)
+        bkv.bkv_compact(st.shape, st.K, st.V, st.length, w.budget, st.kept, st.ws)
+        rec("compact", 1)
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        st.step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    status = bkv.bkv_read_device_status(st.ws)
-    assert status == 0, "device status %d" % status
+    elapsed, stage_ms = timed_passes(Schedule(st, grow, tail, False), args.warmup, K, st.ws)
     rows_moved = bkv.ws_rows_moved(st.ws)
 
-    stage_names = ["grow", "fps_update", "score", "select", "compact"]
-    stage_ms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(K)]))
-                for j, n in enumerate(stage_names)}
     ms_per_step = elapsed * 1e3 / K
     passes_per_s = K / elapsed
 
@@ -363,6 +435,7 @@ def main():
         "score_compact_GBps": score_compact_gbps,
         "score_compact_frac_of_peak": score_compact_gbps / HBM_PEAK_GBPS,
         "stage_ms": stage_ms,
+        "schedule": "serial: every stage on one stream (the overlapped schedule is reported under 'overlapped')",
         "algorithmic_bytes_per_step": {"score": score_bytes, "compact": compact_bytes},
         "copy_probe_GBps": cp["GBps"],
         "roofline": {
@@ -376,9 +449,23 @@ def main():
         },
         "kernel_source_hash": src_hash,
     }
+    if not args.no_overlap:
+        log("timing the overlapped schedule")
+        el, sm = timed_passes(Schedule(st, grow, tail, True), args.warmup, K, st.ws)
+        result["overlapped"] = {
+            "schedule": "the ingest and beacon FPS of pass i+1 run on a second stream (default priority) while pass i "
+                        "scores, selects and compacts; same work per pass",
+            "passes_per_s": K / el,
+            "ms_per_step": el * 1e3 / K,
+            "stage_ms": sm,
+        }
     if not args.no_hole_fill:
         log("timing the hole-filling layout on the same workload")
-        result["hole_fill"] = time_hole_fill(st, args.warmup, K)
+        result["hole_fill"] = time_hole_fill(st, args.warmup, K, False)
+        if not args.no_overlap:
+            ov = time_hole_fill(st, args.warmup, K, True)
+            result["hole_fill"]["overlapped"] = {"passes_per_s": ov["passes_per_s"], "ms_per_step": ov["ms_per_step"],
+                                                 "stage_ms": ov["stage_ms"]}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(st, budget_s=args.cpu_budget)

@@ -97,11 +97,13 @@ typedef struct bkv_shape {
  *   [3] select  : int32 [N][Hkv][2] = {first evicted index, kept count};
  *   [4] rope    : float2 [N][R+1][d/2] (cos, sin) tables;
  *   [5] beacons : int32 [N][Hq][nb+1]: the pick count, then the buffer rows
- *                 of the beacons in pick order.
+ *                 of the beacons in pick order;
+ *   [6] beacon rows : [N][Hq][nb][d], storage type: copies of the picked
+ *                 buffer rows (pre-RoPE), the first `count` of each head valid.
  * Zero the first 256 bytes once before first use (bkv_reset_device_status).
  */
 size_t bkv_workspace_size(const bkv_shape *shape, int32_t R, int32_t nb);
-int bkv_workspace_layout(const bkv_shape *shape, int32_t R, int32_t nb, size_t offsets[6]);
+int bkv_workspace_layout(const bkv_shape *shape, int32_t R, int32_t nb, size_t offsets[7]);
 
 /*
  * bkv_fps_update -- Continual FPS ingest ([WZ] 怎么挑出这几个信标: a bounded
@@ -154,6 +156,31 @@ int bkv_score(const bkv_shape *shape, const void *K, const int32_t *len, const v
               const int32_t *recent_pos, int32_t R, const void *qbuf, const int32_t *qcount,
               int32_t C, int32_t nb, const int32_t *pos_now, double rope_theta, float *scores,
               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bkv_score in two calls, so that the beacon FPS can run on another stream.
+ * After bkv_beacon_picks the buffers are free: the next ingest may run while
+ * bkv_score_picked still scores (for instance on a second stream, during the
+ * current eviction).
+ *
+ * bkv_beacon_picks -- the beacon FPS of every query head (the first half of
+ *   bkv_score): writes workspace regions [5] (pick count, then the buffer
+ *   rows of the picks) and [6] (copies of the picked rows).  qbuf, qcount,
+ *   C, nb as for bkv_score; R only locates the regions (the workspace of
+ *   shape, R, nb).
+ *
+ * bkv_score_picked -- the second half: rotation and scoring exactly as
+ *   bkv_score, with the beacons taken from regions [5] and [6] as the last
+ *   bkv_beacon_picks on this workspace left them.  Reads no buffer.
+ *
+ * bkv_score = bkv_beacon_picks followed by bkv_score_picked on one stream.
+ */
+int bkv_beacon_picks(const bkv_shape *shape, const void *qbuf, const int32_t *qcount, int32_t C,
+                     int32_t R, int32_t nb, void *ws, size_t ws_bytes, hipStream_t stream);
+int bkv_score_picked(const bkv_shape *shape, const void *K, const int32_t *len, const void *recent,
+                     const int32_t *recent_pos, int32_t R, int32_t nb, const int32_t *pos_now,
+                     double rope_theta, float *scores, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /*
  * bkv_select -- kept set ([IK] 三: I = TopK(score, B_KV); [AM]: the recent

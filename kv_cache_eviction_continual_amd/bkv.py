@@ -24,7 +24,7 @@ E_NULL, E_SHAPE, E_DTYPE, E_BUDGET, E_CAPACITY, E_WORKSPACE, E_HIP = range(1, 8)
 DEV_BAD_LEN = 0x1
 DEV_BAD_COUNT = 0x2
 
-WS_OBS, WS_VALID, WS_LSE, WS_SELECT, WS_ROPE, WS_BEACONS = range(6)
+WS_OBS, WS_VALID, WS_LSE, WS_SELECT, WS_ROPE, WS_BEACONS, WS_BEACON_ROWS = range(7)
 WS_HEADER_BYTES = 256
 
 EXPORTS = (
@@ -32,6 +32,8 @@ EXPORTS = (
     "bkv_workspace_layout",
     "bkv_fps_update",
     "bkv_score",
+    "bkv_beacon_picks",
+    "bkv_score_picked",
     "bkv_select",
     "bkv_compact",
     "bkv_select_compact",
@@ -85,6 +87,10 @@ def load() -> ctypes.CDLL:
     L.bkv_fps_update.restype = ctypes.c_int
     L.bkv_score.argtypes = [SP, P, P, P, P, I32, P, P, I32, I32, P, ctypes.c_double, P, P, SZ, P]
     L.bkv_score.restype = ctypes.c_int
+    L.bkv_beacon_picks.argtypes = [SP, P, P, I32, I32, I32, P, SZ, P]
+    L.bkv_beacon_picks.restype = ctypes.c_int
+    L.bkv_score_picked.argtypes = [SP, P, P, P, P, I32, I32, P, ctypes.c_double, P, P, SZ, P]
+    L.bkv_score_picked.restype = ctypes.c_int
     L.bkv_select.argtypes = [SP, P, P, I32, I32, P, P, SZ, P]
     L.bkv_select.restype = ctypes.c_int
     L.bkv_compact.argtypes = [SP, P, P, P, I32, P, P, SZ, P]
@@ -150,7 +156,7 @@ def bkv_workspace_size(shape: Shape, R: int, nb: int) -> int:
 
 
 def bkv_workspace_layout(shape: Shape, R: int, nb: int):
-    offs = (ctypes.c_size_t * 6)()
+    offs = (ctypes.c_size_t * 7)()
     _check(load().bkv_workspace_layout(ctypes.byref(shape), R, nb, offs))
     return [int(o) for o in offs]
 
@@ -165,6 +171,18 @@ def bkv_score(shape: Shape, K, length, recent, recent_pos, R: int, qbuf, qcount,
     _check(load().bkv_score(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos), R,
                             _ptr(qbuf), _ptr(qcount), C, nb, _ptr(pos_now), float(rope_theta), _ptr(scores),
                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_beacon_picks(shape: Shape, qbuf, qcount, C: int, R: int, nb: int, ws, stream=None) -> None:
+    _check(load().bkv_beacon_picks(ctypes.byref(shape), _ptr(qbuf), _ptr(qcount), C, R, nb, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_score_picked(shape: Shape, K, length, recent, recent_pos, R: int, nb: int, pos_now, rope_theta: float,
+                     scores, ws, stream=None) -> None:
+    _check(load().bkv_score_picked(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos), R,
+                                   nb, _ptr(pos_now), float(rope_theta), _ptr(scores), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bkv_select(shape: Shape, scores, length, budget: int, window: int, kept, ws, stream=None) -> None:
@@ -249,4 +267,9 @@ def ws_views(shape: Shape, R: int, nb: int, ws):
     nbk = shape.n_seq * shape.n_q_heads * (nb + 1)
     beacons = ws[offs[WS_BEACONS]:offs[WS_BEACONS] + nbk * 4].view(torch.int32).view(shape.n_seq, shape.n_q_heads,
                                                                                        nb + 1)
-    return {"obs": obs, "valid": valid, "lse": lse, "select": sel, "beacons": beacons, "rows": rows, "RP": RP}
+    st_bytes = es * d
+    nbr = shape.n_seq * shape.n_q_heads * nb
+    brows = ws[offs[WS_BEACON_ROWS]:offs[WS_BEACON_ROWS] + nbr * st_bytes].view(st).view(shape.n_seq, shape.n_q_heads,
+                                                                                      nb, d)
+    return {"obs": obs, "valid": valid, "lse": lse, "select": sel, "beacons": beacons, "beacon_rows": brows,
+            "rows": rows, "RP": RP}

@@ -11,10 +11,10 @@ namespace bkv {
 template <int DT, int D>
 hipError_t launch_fps_update(const void*, int, void*, int32_t*, int, int, int, int32_t*, hipStream_t);
 template <int DT, int D>
-hipError_t launch_beacon_picks(const void*, const int32_t*, int, int, int, int32_t*, int32_t*, hipStream_t);
+hipError_t launch_beacon_picks(const void*, const int32_t*, int, int, int, int32_t*, void*, int32_t*, hipStream_t);
 template <int DT, int D>
 hipError_t launch_score(const void*, const int32_t*, int, int, int, int, const void*, const int32_t*, int,
-                        const void*, int, const int32_t*, int, const int32_t*, double, float2*, void*, int32_t*, int,
+                        const int32_t*, const void*, int, const int32_t*, double, float2*, void*, int32_t*, int,
                         float*, float*, int32_t*, hipStream_t);
 hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
                          hipStream_t);
@@ -51,7 +51,7 @@ int check_shape(const bkv_shape* s) {
 }
 
 struct WsLayout {
-  size_t obs, valid, lse, select, rope, beacons, total;
+  size_t obs, valid, lse, select, rope, beacons, beacon_rows, total;
   int RP;
 };
 
@@ -80,6 +80,8 @@ bool layout(const bkv_shape* s, int R, int nb, WsLayout* out) {
   off = align256(off + (size_t)s->n_seq * (R + 1) * (s->head_dim / 2) * sizeof(float2));
   out->beacons = off;
   off = align256(off + (size_t)s->n_seq * s->n_q_heads * (nb + 1) * sizeof(int32_t));
+  out->beacon_rows = off;
+  off = align256(off + (size_t)s->n_seq * s->n_q_heads * nb * s->head_dim * elem_bytes(s->dtype));
   out->total = off;
   return true;
 }
@@ -93,7 +95,64 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_E_HIP; }
 
+// Argument checks of the scoring calls, in a fixed order (the first failing
+// check decides the status).  qbuf and qcount are only checked for non-null,
+// and only when the call runs the beacon FPS itself; C < 0 means the call
+// takes no capacity (nb is then only range-checked).
+int check_score_args(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
+                     const int32_t* recent_pos, int32_t R, const void* qbuf, const int32_t* qcount, bool need_qcount,
+                     int32_t C, int32_t nb, const int32_t* pos_now, double rope_theta, const float* scores,
+                     const void* ws, size_t ws_bytes, WsLayout* w) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (C >= 0 ? (C < 2 || C > kMaxCapacity || nb < 0 || nb > C) : (nb < 0 || nb > kMaxCapacity))
+    return BKV_E_CAPACITY;
+  if (R < 0 || R > kMaxRecent) return BKV_E_SHAPE;
+  if (!(rope_theta > 1.0)) return BKV_E_SHAPE;
+  if (!layout(shape, R, nb, w)) return BKV_E_SHAPE;
+  if (w->RP == 0) return BKV_E_SHAPE;  // no observation rows at all
+  if (!K || !len || !scores || !pos_now || (need_qcount && (!qbuf || !qcount))) return BKV_E_NULL;
+  if (R > 0 && (!recent || !recent_pos)) return BKV_E_NULL;
+  return check_ws(ws, ws_bytes, w->total);
+}
+
+
 }  // namespace
+
+// The RoPE tables and the score kernel, with the beacon picks already in ws.
+int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
+                  const int32_t* recent_pos, int32_t R, int32_t nb, const int32_t* pos_now, double rope_theta,
+                  float* scores, void* ws, const WsLayout& w, hipStream_t stream) {
+  const int N = shape->n_seq, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  unsigned char* base = (unsigned char*)ws;
+  int32_t* words = (int32_t*)ws;
+  float2* tab = (float2*)(base + w.rope);
+  void* obs = base + w.obs;
+  int32_t* valid = (int32_t*)(base + w.valid);
+  float* lse = (float*)(base + w.lse);
+  const int32_t* beacons = (const int32_t*)(base + w.beacons);
+  const void* brows = base + w.beacon_rows;
+  hipError_t e;
+#define BKV_SCORE_CASE(DT, D)                                                                                  \
+  e = launch_score<DT, D>(K, len, N, Hkv, Hq, shape->max_len, recent, recent_pos, R, beacons, brows, nb,       \
+                          pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, stream);
+  if (shape->dtype == BKV_BF16) {
+    if (shape->head_dim == 128) {
+      BKV_SCORE_CASE(BKV_BF16, 128)
+    } else {
+      BKV_SCORE_CASE(BKV_BF16, 64)
+    }
+  } else {
+    if (shape->head_dim == 128) {
+      BKV_SCORE_CASE(BKV_F32, 128)
+    } else {
+      BKV_SCORE_CASE(BKV_F32, 64)
+    }
+  }
+#undef BKV_SCORE_CASE
+  return hip_status(e);
+}
 }  // namespace bkv
 
 using namespace bkv;
@@ -107,7 +166,7 @@ size_t bkv_workspace_size(const bkv_shape* shape, int32_t R, int32_t nb) {
   return w.total;
 }
 
-int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t offsets[6]) {
+int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t offsets[7]) {
   int st = check_shape(shape);
   if (st != BKV_OK) return st;
   if (!offsets) return BKV_E_NULL;
@@ -119,6 +178,7 @@ int bkv_workspace_layout(const bkv_shape* shape, int32_t R, int32_t nb, size_t o
   offsets[3] = w.select;
   offsets[4] = w.rope;
   offsets[5] = w.beacons;
+  offsets[6] = w.beacon_rows;
   return BKV_OK;
 }
 
@@ -143,51 +203,52 @@ int bkv_fps_update(const bkv_shape* shape, const void* q_new, int32_t T, void* q
   return hip_status(e);
 }
 
-int bkv_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
-              const int32_t* recent_pos, int32_t R, const void* qbuf, const int32_t* qcount, int32_t C, int32_t nb,
-              const int32_t* pos_now, double rope_theta, float* scores, void* ws, size_t ws_bytes,
-              hipStream_t stream) {
+int bkv_beacon_picks(const bkv_shape* shape, const void* qbuf, const int32_t* qcount, int32_t C, int32_t R,
+                     int32_t nb, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != BKV_OK) return st;
   if (C < 2 || C > kMaxCapacity || nb < 0 || nb > C) return BKV_E_CAPACITY;
   if (R < 0 || R > kMaxRecent) return BKV_E_SHAPE;
-  if (!(rope_theta > 1.0)) return BKV_E_SHAPE;
   WsLayout w;
   if (!layout(shape, R, nb, &w)) return BKV_E_SHAPE;
-  if (w.RP == 0) return BKV_E_SHAPE;  // no observation rows at all
-  if (!K || !len || !scores || !pos_now || !qbuf || !qcount) return BKV_E_NULL;
-  if (R > 0 && (!recent || !recent_pos)) return BKV_E_NULL;
+  if (!qbuf || !qcount) return BKV_E_NULL;
   if ((st = check_ws(ws, ws_bytes, w.total)) != BKV_OK) return st;
-  const int N = shape->n_seq, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
-  if (N == 0) return BKV_OK;
-  unsigned char* base = (unsigned char*)ws;
+  const int heads = shape->n_seq * shape->n_q_heads;
+  if (heads == 0) return BKV_OK;
   int32_t* words = (int32_t*)ws;
-  float2* tab = (float2*)(base + w.rope);
-  void* obs = base + w.obs;
-  int32_t* valid = (int32_t*)(base + w.valid);
-  float* lse = (float*)(base + w.lse);
+  int32_t* beacons = (int32_t*)((unsigned char*)ws + w.beacons);
+  void* brows = (unsigned char*)ws + w.beacon_rows;
   hipError_t e;
-  int32_t* beacons = (int32_t*)(base + w.beacons);
-#define BKV_SCORE_CASE(DT, D)                                                                                  \
-  e = launch_beacon_picks<DT, D>(qbuf, qcount, C, nb, N * Hq, beacons, words, stream);                         \
-  if (e == hipSuccess)                                                                                         \
-    e = launch_score<DT, D>(K, len, N, Hkv, Hq, shape->max_len, recent, recent_pos, R, qbuf, C, beacons, nb,   \
-                            pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, stream);
-  if (shape->dtype == BKV_BF16) {
-    if (shape->head_dim == 128) {
-      BKV_SCORE_CASE(BKV_BF16, 128)
-    } else {
-      BKV_SCORE_CASE(BKV_BF16, 64)
-    }
-  } else {
-    if (shape->head_dim == 128) {
-      BKV_SCORE_CASE(BKV_F32, 128)
-    } else {
-      BKV_SCORE_CASE(BKV_F32, 64)
-    }
-  }
-#undef BKV_SCORE_CASE
+#define BKV_PICKS(DT, D) launch_beacon_picks<DT, D>(qbuf, qcount, C, nb, heads, beacons, brows, words, stream)
+  if (shape->dtype == BKV_BF16)
+    e = shape->head_dim == 128 ? BKV_PICKS(BKV_BF16, 128) : BKV_PICKS(BKV_BF16, 64);
+  else
+    e = shape->head_dim == 128 ? BKV_PICKS(BKV_F32, 128) : BKV_PICKS(BKV_F32, 64);
+#undef BKV_PICKS
   return hip_status(e);
+}
+
+int bkv_score_picked(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
+                     const int32_t* recent_pos, int32_t R, int32_t nb, const int32_t* pos_now, double rope_theta,
+                     float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  WsLayout w;
+  int st = check_score_args(shape, K, len, recent, recent_pos, R, nullptr, nullptr, false, -1, nb, pos_now,
+                            rope_theta, scores, ws, ws_bytes, &w);
+  if (st != BKV_OK) return st;
+  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w, stream);
+}
+
+int bkv_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
+              const int32_t* recent_pos, int32_t R, const void* qbuf, const int32_t* qcount, int32_t C, int32_t nb,
+              const int32_t* pos_now, double rope_theta, float* scores, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  WsLayout w;
+  int st = check_score_args(shape, K, len, recent, recent_pos, R, qbuf, qcount, true, C, nb, pos_now, rope_theta,
+                            scores, ws, ws_bytes, &w);
+  if (st != BKV_OK) return st;  // nothing enqueued
+  st = bkv_beacon_picks(shape, qbuf, qcount, C, R, nb, ws, ws_bytes, stream);
+  if (st != BKV_OK) return st;
+  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w, stream);
 }
 
 int bkv_select(const bkv_shape* shape, const float* scores, const int32_t* len, int32_t budget, int32_t window,

@@ -693,12 +693,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 // ---------------------------------------------------------------------------
 
 // One wavefront per query head.  Writes beacons[head][0] = the pick count
-// min(nb, count) and beacons[head][1 + b] = buffer row of pick b, in pick
-// order.  The rows themselves are rotated by the score kernel.
+// min(nb, count), beacons[head][1 + b] = buffer row of pick b, in pick
+// order, and a copy of the picked rows to rows[head][b] (so that scoring
+// does not read the buffer, which the next ingest may already be changing).
+// The score kernel rotates them.
 template <int DT, int D, int NTMAX>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void beacon_pick_kernel(
     const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
-    int32_t* __restrict__ beacons, int32_t* __restrict__ ws_words) {
+    int32_t* __restrict__ beacons, typename Elem<DT>::T* __restrict__ rows, int32_t* __restrict__ ws_words) {
   constexpr int cap = 32 * NTMAX;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
@@ -720,6 +722,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   int32_t* out = beacons + (size_t)head * (nb + 1);
   for (int b = lane; b < kk; b += 64) out[1 + b] = s.picks[b];
   if (lane == 0) out[0] = kk;
+  // the picked rows, 16 bytes per lane and load
+  constexpr int kU = D * Elem<DT>::kBytes / 16;
+  uint4* dst = reinterpret_cast<uint4*>(rows + (size_t)head * nb * D);
+  for (int u = lane; u < kk * kU; u += 64) {
+    const int b = u / kU, q = u - b * kU;
+    dst[u] = reinterpret_cast<const uint4*>(src.row(s.picks[b]))[q];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -755,22 +764,23 @@ hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcou
 
 template <int DT, int D, int NTMAX>
 static hipError_t launch_picks_nt(const void* qbuf, const int32_t* qcount, int C, int nb, int heads,
-                                  int32_t* beacons, int32_t* ws_words, hipStream_t st) {
+                                  int32_t* beacons, void* rows, int32_t* ws_words, hipStream_t st) {
   using ET = typename Elem<DT>::T;
   const size_t smem = fps_lds_bytes<DT, D>(32 * NTMAX, 0);
   auto kern = beacon_pick_kernel<DT, D, NTMAX>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(heads), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, beacons, ws_words);
+  hipLaunchKernelGGL(kern, dim3(heads), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, beacons, (ET*)rows,
+                     ws_words);
   return hipGetLastError();
 }
 
 template <int DT, int D>
 hipError_t launch_beacon_picks(const void* qbuf, const int32_t* qcount, int C, int nb, int heads, int32_t* beacons,
-                               int32_t* ws_words, hipStream_t st) {
-  if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, ws_words, st);
-  if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, ws_words, st);
-  return launch_picks_nt<DT, D, 8>(qbuf, qcount, C, nb, heads, beacons, ws_words, st);
+                               void* rows, int32_t* ws_words, hipStream_t st) {
+  if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  return launch_picks_nt<DT, D, 8>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
 }
 
 template hipError_t launch_fps_update<BKV_F32, 64>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
@@ -782,8 +792,8 @@ template hipError_t launch_fps_update<BKV_BF16, 64>(const void*, int, void*, int
 template hipError_t launch_fps_update<BKV_BF16, 128>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
                                                      hipStream_t);
 #define BKV_INST_PICKS(DT, D)                                                                                  \
-  template hipError_t launch_beacon_picks<DT, D>(const void*, const int32_t*, int, int, int, int32_t*, int32_t*,   \
-                                                 hipStream_t);
+  template hipError_t launch_beacon_picks<DT, D>(const void*, const int32_t*, int, int, int, int32_t*, void*,      \
+                                                 int32_t*, hipStream_t);
 BKV_INST_PICKS(BKV_F32, 64)
 BKV_INST_PICKS(BKV_F32, 128)
 BKV_INST_PICKS(BKV_BF16, 64)

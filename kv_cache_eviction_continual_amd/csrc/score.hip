@@ -199,12 +199,13 @@ struct ScoreLayout {
 // others only help to stage K.  Observation row r of the unit is, for
 // g = r / (R + nb) and k = r % (R + nb): recent query k of query head
 // h G + g (present if its position is >= 0), or for k >= R its beacon k - R
-// (present if below the pick count); rows from G (R + nb) to RP are padding.
+// (present if below the pick count; read from the picks kernel's row copy);
+// rows from G (R + nb) to RP are padding.
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void score_kernel(
     const typename Elem<DT>::T* __restrict__ K, const int32_t* __restrict__ len, int Hkv, int Hq, int Lmax,
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
-    const typename Elem<DT>::T* __restrict__ qbuf, int C, const int32_t* __restrict__ beacons, int nb,
+    const int32_t* __restrict__ beacons, const typename Elem<DT>::T* __restrict__ brows, int nb,
     const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid, int RP,
     float* __restrict__ scores, float* __restrict__ lse_out, int32_t* __restrict__ ws_words) {
   using Lay = ScoreLayout<DT, D>;
@@ -290,10 +291,9 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
     if (k < R) {
       row_valid = recent_pos[(size_t)n * R + k] >= 0;
       src = reinterpret_cast<const unsigned char*>(recent + (head * R + k) * D);
-    } else {
+    } else {  // beacon k - R: the picks kernel's copy of its buffer row
       row_valid = k - R < bk[0];
-      const int pick = row_valid ? bk[1 + k - R] : 0;
-      src = reinterpret_cast<const unsigned char*>(qbuf + (head * C + pick) * D);
+      src = reinterpret_cast<const unsigned char*>(brows + (head * nb + (row_valid ? k - R : 0)) * D);
     }
     row_valid = row_valid && myrow < G * per;
     Raw x[KS];
@@ -404,8 +404,8 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
 
 template <int DT, int D, int NW>
 static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax,
-                                  const void* recent, const int32_t* recent_pos, int R, const void* qbuf, int C,
-                                  const int32_t* beacons, int nb, const float2* tab, void* obs, int32_t* obs_valid,
+                                  const void* recent, const int32_t* recent_pos, int R, const int32_t* beacons,
+                                  const void* brows, int nb, const float2* tab, void* obs, int32_t* obs_valid,
                                   int RP, float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
   using Lay = ScoreLayout<DT, D>;
   using ET = typename Elem<DT>::T;
@@ -414,7 +414,7 @@ static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int 
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(N * Hkv), dim3(64 * NW), smem, st, (const ET*)K, len, Hkv, Hq, Lmax,
-                     (const ET*)recent, recent_pos, R, (const ET*)qbuf, C, beacons, nb, tab, (ET*)obs, obs_valid, RP,
+                     (const ET*)recent, recent_pos, R, beacons, (const ET*)brows, nb, tab, (ET*)obs, obs_valid, RP,
                      scores, lse, ws_words);
   return hipGetLastError();
 }
@@ -423,7 +423,7 @@ static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int 
 // is at most 256: 1..8 row tiles.
 template <int DT, int D>
 hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax, const void* recent,
-                        const int32_t* recent_pos, int R, const void* qbuf, int C, const int32_t* beacons, int nb,
+                        const int32_t* recent_pos, int R, const int32_t* beacons, const void* brows, int nb,
                         const int32_t* pos_now, double theta, float2* tab, void* obs, int32_t* obs_valid, int RP,
                         float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
   hipLaunchKernelGGL(rope_table_kernel<D>, dim3(N), dim3(256), 0, st, recent_pos, pos_now, R, theta, tab);
@@ -431,7 +431,7 @@ hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int H
   if (e != hipSuccess) return e;
   const int tiles = RP / 32;
 #define BKV_SCORE_NW(NW)                                                                                      \
-  return launch_score_nw<DT, D, NW>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, qbuf, C, beacons, nb, tab, \
+  return launch_score_nw<DT, D, NW>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, beacons, brows, nb, tab,  \
                                     obs, obs_valid, RP, scores, lse, ws_words, st)
   if (tiles <= 2) BKV_SCORE_NW(2);
   if (tiles <= 4) BKV_SCORE_NW(4);
@@ -441,7 +441,7 @@ hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int H
 
 #define BKV_INST_SCORE(DT, D)                                                                                  \
   template hipError_t launch_score<DT, D>(const void*, const int32_t*, int, int, int, int, const void*,       \
-                                          const int32_t*, int, const void*, int, const int32_t*, int,         \
+                                          const int32_t*, int, const int32_t*, const void*, int,              \
                                           const int32_t*, double, float2*, void*, int32_t*, int, float*,      \
                                           float*, int32_t*, hipStream_t);
 BKV_INST_SCORE(BKV_F32, 64)

@@ -61,7 +61,8 @@ def test_workspace_size_and_layout(lib):
     assert offs[bkv.WS_LSE] - offs[bkv.WS_VALID] >= units * RP * 4
     assert offs[bkv.WS_ROPE] - offs[bkv.WS_LSE] >= units * RP * 4
     assert offs[bkv.WS_BEACONS] - offs[bkv.WS_ROPE] >= 2 * 17 * 64 * 8
-    assert n - offs[bkv.WS_BEACONS] >= 2 * 32 * 17 * 4
+    assert offs[bkv.WS_BEACON_ROWS] - offs[bkv.WS_BEACONS] >= 2 * 32 * 17 * 4
+    assert n - offs[bkv.WS_BEACON_ROWS] >= 2 * 32 * 16 * 128 * 2
     # rows above 256 and bad shapes give size 0
     assert bkv.bkv_workspace_size(s, 40, 40) == 0
     assert bkv.bkv_workspace_size(shape(head_dim=96), 16, 16) == 0
@@ -106,6 +107,32 @@ def test_host_validation_rejects_before_launch(lib):
     assert sc(*a) == bkv.E_WORKSPACE
     a = list(ok_args); a[5] = 0; a[9] = 0
     assert sc(*a) == bkv.E_SHAPE  # no observation rows
+    # the two halves of score
+    bp = lib.bkv_beacon_picks
+    assert bp(ctypes.byref(s), fake, None, 128, 16, 16, fake, big, P) == bkv.E_NULL
+    assert bp(ctypes.byref(s), fake, fake, 128, 16, 200, fake, big, P) == bkv.E_CAPACITY
+    assert bp(ctypes.byref(s), fake, fake, 128, 70, 16, fake, big, P) == bkv.E_SHAPE
+    assert bp(ctypes.byref(s), fake, fake, 128, 16, 16, fake, 1024, P) == bkv.E_WORKSPACE
+    sp = lib.bkv_score_picked
+    ok_p = [ctypes.byref(s), fake, fake, fake, fake, 16, 16, fake, 1e6, fake, fake, big, P]
+    a = list(ok_p); a[1] = None
+    assert sp(*a) == bkv.E_NULL
+    a = list(ok_p); a[6] = 300
+    assert sp(*a) == bkv.E_CAPACITY
+    a = list(ok_p); a[8] = 0.5
+    assert sp(*a) == bkv.E_SHAPE
+    a = list(ok_p); a[11] = 1024
+    assert sp(*a) == bkv.E_WORKSPACE
+    # hole-filling layout
+    sf = lib.bkv_select_fill
+    assert sf(ctypes.byref(s), fake, None, fake, 2048, 32, fake, fake, big, P) == bkv.E_NULL
+    assert sf(ctypes.byref(s), fake, fake, fake, 16, 32, fake, fake, big, P) == bkv.E_BUDGET
+    assert sf(ctypes.byref(s), fake, fake, fake, 2048, 32, fake, fake, 100, P) == bkv.E_WORKSPACE
+    cf = lib.bkv_compact_fill
+    assert cf(ctypes.byref(s), fake, fake, None, fake, 2048, fake, fake, big, P) == bkv.E_NULL
+    assert cf(ctypes.byref(s), fake, fake, fake, fake, 0, fake, fake, big, P) == bkv.E_BUDGET
+    assert lib.bkv_select_compact_fill(ctypes.byref(s), fake, fake, fake, fake, fake, 2048, 4096, fake, fake, big,
+                                       P) == bkv.E_BUDGET
     # select / compact
     assert lib.bkv_select(ctypes.byref(s), fake, fake, 16, 32, fake, fake, big, P) == bkv.E_BUDGET
     assert lib.bkv_select(ctypes.byref(s), fake, fake, 4096, 32, fake, fake, big, P) == bkv.E_BUDGET

@@ -375,3 +375,57 @@ def test_fps_zero_rows_and_extreme_norms(cfg):
     stream = synth.to_storage(z, w.dtype)
     blocks = [stream[:, :, i:i + 50].contiguous() for i in range(0, stream.shape[2], 50)]
     _ingest_and_compare(w, blocks, N)
+
+
+def test_score_in_two_calls_equals_score():
+    """bkv_beacon_picks (on a second stream) + bkv_score_picked give bit for bit
+    what bkv_score gives; the picks are the oracle's FPS picks."""
+    w = configs.get(2)
+    N = 2
+    inp = make_inputs(w, N=N, steps=700)
+    g = GpuRun(inp)
+    for blk in inp.blocks:
+        g.ingest(blk)
+    g.score()
+    torch.cuda.synchronize()
+    ref_scores = g.scores.clone()
+    v = g.views()
+    ref = {k: v[k].clone() for k in ("obs", "valid", "lse", "beacons", "beacon_rows")}
+    # second workspace, picks on another stream
+    ws2 = bkv.alloc_workspace(g.shape, w.n_recent, w.n_beacons)
+    scores2 = torch.full_like(g.scores, float("nan"))
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    with torch.cuda.stream(side):
+        bkv.bkv_beacon_picks(g.shape, g.qbuf, g.qcount, w.capacity, w.n_recent, w.n_beacons, ws2, stream=side)
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    # the buffers are free once the picks are taken: scribble over them before scoring
+    qbuf_saved = g.qbuf.clone()
+    g.qbuf.fill_(0)
+    bkv.bkv_score_picked(g.shape, inp.K, g.length, inp.recent, g.recent_pos, w.n_recent, w.n_beacons, g.pos_now,
+                         w.rope_theta, scores2, ws2)
+    torch.cuda.synchronize()
+    g.qbuf.copy_(qbuf_saved)
+    torch.cuda.synchronize()
+    v2 = bkv.ws_views(g.shape, w.n_recent, w.n_beacons, ws2)
+    L = int(inp.length[0])
+    assert torch.equal(scores2[:, :, :L].view(torch.int32), ref_scores[:, :, :L].view(torch.int32))
+
+    def bits(t):
+        return t.view({torch.bfloat16: torch.int16, torch.float32: torch.int32}.get(t.dtype, t.dtype))
+
+    for k in ("obs", "valid", "lse", "beacons", "beacon_rows"):
+        assert torch.equal(bits(v2[k]), bits(ref[k])), k
+    # the picks against the oracle's FPS of the same buffers
+    bk = v2["beacons"].cpu().numpy()
+    qb = np_storage(g.qbuf)
+    qc = g.qcount.cpu().numpy()
+    for n in range(N):
+        for hq in (0, 5, w.n_q_heads - 1):
+            c = int(qc[n, hq])
+            picks = oracle.fps_stored(np.ascontiguousarray(qb[n, hq]), c, w.n_beacons)
+            assert bk[n, hq, 0] == len(picks)
+            assert np.array_equal(bk[n, hq, 1:1 + len(picks)], picks)
+            rows = np_storage(v2["beacon_rows"][n, hq, :len(picks)])
+            assert np.array_equal(rows, qb[n, hq][picks]), "beacon row copies differ from the buffer rows"
