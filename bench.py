@@ -119,7 +119,7 @@ class State:
                              w.n_beacons, self.pos_now[e], w.rope_theta, self.scores, self.ws, stream=stream)
 
 
-STAGES = ("grow", "fps_update", "beacon_picks", "score", "select", "compact")
+HEAD_STAGES = ("grow", "fps_update", "beacon_picks", "score")
 
 
 class Schedule:
@@ -137,8 +137,9 @@ class Schedule:
     work either way.  `ev` is a dict of (start, end) event pairs per stage,
     or None; in the serial schedule the score stage includes the beacon FPS."""
 
-    def __init__(self, st, grow, tail, overlap):
+    def __init__(self, st, grow, tail, overlap, tail_stages=("select", "compact")):
         self.st, self.grow, self.tail, self.overlap = st, grow, tail, overlap
+        self.tail_stages = tail_stages
         self.main = torch.cuda.current_stream()
         self.side = torch.cuda.Stream() if overlap else None
         self.ready = None  # beacon FPS of the next pass enqueued on the side stream
@@ -194,9 +195,10 @@ class Schedule:
         self.tail(i, rec)
 
 
-def new_events(overlap):
-    names = STAGES if overlap else tuple(n for n in STAGES if n != "beacon_picks")
-    return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+def new_events(sched):
+    names = HEAD_STAGES if sched.overlap else tuple(n for n in HEAD_STAGES if n != "beacon_picks")
+    return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for n in names + sched.tail_stages}
 
 
 def timed_passes(sched, warmup, steps, ws):
@@ -207,7 +209,7 @@ def timed_passes(sched, warmup, steps, ws):
     sched.prime(warmup)  # the first timed pass's ingest stays outside the timed region
     torch.cuda.synchronize()
     bkv.bkv_reset_device_status(ws)
-    evs = [new_events(sched.overlap) for _ in range(steps)]
+    evs = [new_events(sched) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -239,14 +241,11 @@ def time_hole_fill(st, warmup, steps, overlap):
         pos[:, :, B:L].copy_(fresh[i % len(fresh)] + new_rows * len(fresh) * (i // len(fresh)))
 
     def tail(i, rec):
-        rec("select", 0)
-        bkv.bkv_select_fill(st.shape, st.scores, pos, st.length, B, w.window, st.kept, st.ws)
-        rec("select", 1)
-        rec("compact", 0)
-        bkv.bkv_compact_fill(st.shape, st.K, st.V, pos, st.length, B, st.kept, st.ws)
-        rec("compact", 1)
+        rec("select_compact", 0)
+        bkv.bkv_select_compact_fill(st.shape, st.scores, st.K, st.V, pos, st.length, B, w.window, st.kept, st.ws)
+        rec("select_compact", 1)
 
-    elapsed, stage_ms = timed_passes(Schedule(st, grow, tail, overlap), warmup, steps, st.ws)
+    elapsed, stage_ms = timed_passes(Schedule(st, grow, tail, overlap, ("select_compact",)), warmup, steps, st.ws)
     rows_moved = bkv.ws_rows_moved(st.ws)
     row_bytes = w.head_dim * 2
     moved_per_pass = rows_moved / steps                       # K and V rows
@@ -258,7 +257,7 @@ def time_hole_fill(st, warmup, steps, overlap):
         "stage_ms": stage_ms,
         "rows_moved_per_pass": moved_per_pass,
         "compact_algorithmic_bytes": compact_bytes,
-        "compact_GBps": compact_bytes / (stage_ms["compact"] * 1e6),
+        "note": "select_compact is bkv_select_compact_fill: selection and hole filling in one kernel",
     }
 
 

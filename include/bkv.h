@@ -265,13 +265,18 @@ int bkv_select_fill(const bkv_shape *shape, const float *scores, const int32_t *
  *                           workspace
  *
  * Must follow bkv_select_fill on the same workspace, budget and stream.
- * Adds the number of moved K and V rows to the statistic rows_moved.
+ * Adds the number of moved K and V rows to the statistic rows_moved, and
+ * leaves the select table reading "no hole", so a repeated call moves
+ * nothing.
  */
 int bkv_compact_fill(const bkv_shape *shape, void *K, void *V, int32_t *pos, int32_t *len,
                      int32_t budget, const int32_t *kept, void *ws, size_t ws_bytes,
                      hipStream_t stream);
 
-/* bkv_select_fill followed by bkv_compact_fill. */
+/* bkv_select_fill followed by bkv_compact_fill, with the same results (also
+ * the select table reading "no hole").  Where max_len <= 4096 one kernel
+ * selects and fills: each (slot, KV head) moves its fillers as soon as it
+ * has paired them. */
 int bkv_select_compact_fill(const bkv_shape *shape, const float *scores, void *K, void *V,
                             int32_t *pos, int32_t *len, int32_t budget, int32_t window,
                             int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);

@@ -22,8 +22,10 @@ hipError_t launch_compact(void*, void*, const int32_t*, const int32_t*, int32_t*
                           unsigned long long*, hipStream_t);
 hipError_t launch_select_fill(const float*, const int32_t*, const int32_t*, int, int, int, int, int, int32_t*,
                               int32_t*, int32_t*, hipStream_t);
-hipError_t launch_compact_fill(void*, void*, int32_t*, const int32_t*, const int32_t*, int32_t*, int, int, int, int,
-                               int, unsigned long long*, hipStream_t);
+hipError_t launch_compact_fill(void*, void*, int32_t*, const int32_t*, int32_t*, int32_t*, int, int, int, int, int,
+                               unsigned long long*, hipStream_t);
+hipError_t launch_select_compact_fill(const float*, void*, void*, int32_t*, int32_t*, int, int, int, int, int,
+                                      int32_t*, int32_t*, int, unsigned long long*, int32_t*, hipStream_t);
 
 __global__ void zero_header_kernel(int32_t* w) {
   if (threadIdx.x < (int)(kHeaderBytes / 4)) w[threadIdx.x] = 0;
@@ -311,7 +313,7 @@ int bkv_compact_fill(const bkv_shape* shape, void* K, void* V, int32_t* pos, int
   if ((st = check_ws(ws, ws_bytes, select_end(shape))) != BKV_OK) return st;
   const int N = shape->n_seq, Hkv = shape->n_kv_heads;
   if (N == 0) return BKV_OK;
-  const int32_t* sel = (const int32_t*)((unsigned char*)ws + kHeaderBytes);
+  int32_t* sel = (int32_t*)((unsigned char*)ws + kHeaderBytes);
   unsigned long long* moved = (unsigned long long*)((unsigned char*)ws + 8);
   const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
   return hip_status(
@@ -321,9 +323,19 @@ int bkv_compact_fill(const bkv_shape* shape, void* K, void* V, int32_t* pos, int
 int bkv_select_compact_fill(const bkv_shape* shape, const float* scores, void* K, void* V, int32_t* pos,
                             int32_t* len, int32_t budget, int32_t window, int32_t* kept, void* ws, size_t ws_bytes,
                             hipStream_t stream) {
-  int st = bkv_select_fill(shape, scores, pos, len, budget, window, kept, ws, ws_bytes, stream);
+  int st = check_shape(shape);
   if (st != BKV_OK) return st;
-  return bkv_compact_fill(shape, K, V, pos, len, budget, kept, ws, ws_bytes, stream);
+  if (window < 0 || budget < window || budget < 1 || budget > shape->max_len) return BKV_E_BUDGET;
+  if (!scores || !K || !V || !pos || !len || !kept) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, select_end(shape))) != BKV_OK) return st;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  int32_t* words = (int32_t*)ws;
+  int32_t* sel = (int32_t*)((unsigned char*)ws + kHeaderBytes);
+  unsigned long long* moved = (unsigned long long*)((unsigned char*)ws + 8);
+  const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
+  return hip_status(launch_select_compact_fill(scores, K, V, pos, len, N, Hkv, shape->max_len, budget, window, kept,
+                                               sel, row_bytes, moved, words, stream));
 }
 
 const char* bkv_status_string(int status) {

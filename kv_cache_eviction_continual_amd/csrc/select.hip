@@ -339,19 +339,65 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(unsigned char*
 // sources at or beyond it, so no copy reads a row that another one writes.
 
 constexpr int kFillChunk = 1024;  // fillers paired per sweep (LDS list)
+constexpr int kFillBatch = 8;     // 16-byte pieces in flight per thread (named registers below)
 
-template <bool kStaged>
+// Copies K and V rows src[q] -> dst[q] (q < npairs, lists in LDS) of one unit
+// with all 256 threads, kFillBatch 16-byte loads per thread in flight before
+// the matching stores.  Sources and destinations must not overlap.
+__device__ __forceinline__ void copy_row_pairs(unsigned char* kb, unsigned char* vb, int row_bytes, const int* src,
+                                               const int* dst, int npairs) {
+  const int tid = threadIdx.x;
+  const int lpr = row_bytes / 16;  // 16-byte pieces per row
+  const int items = npairs * 2 * lpr;  // (row, tensor, piece)
+  // byte offset of piece `it` in the K (tensor 0) or V row of pair `mv`
+  auto piece = [&](int it, const int* rows, unsigned char** base) -> size_t {
+    const int mv = it / (2 * lpr), rem = it - mv * 2 * lpr;
+    *base = rem >= lpr ? vb : kb;
+    return (size_t)rows[mv] * row_bytes + (size_t)(rem >= lpr ? rem - lpr : rem) * 16;
+  };
+  for (int it0 = tid; it0 < items; it0 += 256 * kFillBatch) {
+    // past the end the last piece is loaded again and not stored
+    unsigned char* b;
+#define BKV_FILL_LD(k)                                                                     \
+  const int pc##k = min(it0 + (k) * 256, items - 1);                                       \
+  const size_t so##k = piece(pc##k, src, &b);                                              \
+  const uint4 v##k = *reinterpret_cast<const uint4*>(b + so##k);
+#define BKV_FILL_ST(k)                                                                     \
+  if (it0 + (k) * 256 < items) {                                                           \
+    const size_t d##k = piece(pc##k, dst, &b);                                             \
+    *reinterpret_cast<uint4*>(b + d##k) = v##k;                                            \
+  }
+    BKV_FILL_LD(0) BKV_FILL_LD(1) BKV_FILL_LD(2) BKV_FILL_LD(3)
+    BKV_FILL_LD(4) BKV_FILL_LD(5) BKV_FILL_LD(6) BKV_FILL_LD(7)
+    BKV_FILL_ST(0) BKV_FILL_ST(1) BKV_FILL_ST(2) BKV_FILL_ST(3)
+    BKV_FILL_ST(4) BKV_FILL_ST(5) BKV_FILL_ST(6) BKV_FILL_ST(7)
+#undef BKV_FILL_LD
+#undef BKV_FILL_ST
+  }
+}
+
+// kCompact: also moves the filler rows (K, V, positions) into their holes as
+// soon as a chunk of pairs is known, leaving nothing for compact_fill_kernel
+// (the select table then reads "no hole").  Needs the staged positions (the
+// selection keeps reading the old ones while holes are filled); the caller
+// updates len afterwards.
+template <bool kStaged, bool kCompact>
 __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* __restrict__ scores,
-                                                                  const int32_t* __restrict__ pos,
+                                                                  int32_t* __restrict__ pos,
                                                                   const int32_t* __restrict__ len, int Hkv, int Lmax,
                                                                   int B, int W, int32_t* __restrict__ kept,
                                                                   int32_t* __restrict__ sel,
-                                                                  int32_t* __restrict__ ws_words) {
+                                                                  int32_t* __restrict__ ws_words,
+                                                                  unsigned char* __restrict__ K,
+                                                                  unsigned char* __restrict__ V, int row_bytes,
+                                                                  unsigned long long* __restrict__ rows_moved) {
   static_assert(kSelThreads == 256, "one radix bucket per thread");
+  static_assert(kStaged || !kCompact, "filling in place needs the staged positions");
   __shared__ int hist[256];
   __shared__ int scan_tmp[16];
   __shared__ int bcast[4];
   __shared__ int fillers[kFillChunk];
+  __shared__ int holes[kCompact ? kFillChunk : 1];
   const size_t unit = blockIdx.x;
   const int n = (int)(unit / Hkv);
   const int tid = threadIdx.x;
@@ -479,22 +525,43 @@ __global__ __launch_bounds__(kSelThreads) void select_fill_kernel(const float* _
           if (i < hole) hole = i;
           // r < nfill always (as many holes as fillers); the guard keeps every
           // LDS read inside the filled part of the list
-          if (r >= r0 && r < r0 + kFillChunk) kept_u[i] = r < nfill ? fillers[r - r0] : i;
+          if (r >= r0 && r < r0 + kFillChunk) {
+            kept_u[i] = r < nfill ? fillers[r - r0] : i;
+            if constexpr (kCompact) {
+              if (r < nfill) holes[r - r0] = i;  // every rank below nfill has one hole
+            }
+          }
         }
       }
       hbase += tot;
     }
     __syncthreads();
+    if constexpr (kCompact) {
+      // this chunk's pairs: rows and positions (the selection reads the staged copies)
+      const int np = min(kFillChunk, nfill - r0);
+      const size_t ub = unit * (size_t)Lmax;
+      copy_row_pairs(K + ub * row_bytes, V + ub * row_bytes, row_bytes, fillers, holes, np);
+      for (int q = tid; q < np; q += kSelThreads) pos[ub + holes[q]] = pp[fillers[q]];
+      if (tid == 0 && np > 0) atomicAdd(rows_moved, 2ull * (unsigned long long)np);  // K and V rows
+      __syncthreads();  // the lists are rewritten by the next sweep
+    }
     if (r0 + kFillChunk >= nfill) break;
   }
   const int first_hole = block_min(hole, scan_tmp);
   if (tid == 0) {
-    sel[2 * unit] = first_hole < B ? first_hole : B;
+    sel[2 * unit] = kCompact ? B : (first_hole < B ? first_hole : B);
     sel[2 * unit + 1] = B;
   }
 }
 
-constexpr int kFillBatch = 8;  // 16-byte pieces in flight per thread (named registers below)
+// len[n] <- min(len[n], B) for valid lengths (after the fused selection and fill).
+__global__ void fill_len_kernel(int32_t* __restrict__ len, int N, int Lmax, int B) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n < N) {
+    const int L = len[n];
+    if (L > B && L <= Lmax) len[n] = B;
+  }
+}
 
 // One workgroup per (slot, KV head): K, V and the positions.  Rows from the
 // first hole to the kept count are scanned kCompactThreads at a time; the
@@ -505,7 +572,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_fill_kernel(unsigned 
                                                                        unsigned char* __restrict__ V,
                                                                        int32_t* __restrict__ pos,
                                                                        const int32_t* __restrict__ kept,
-                                                                       const int32_t* __restrict__ sel,
+                                                                       int32_t* __restrict__ sel,
                                                                        int32_t* __restrict__ len, int Hkv, int Lmax,
                                                                        int B, int row_bytes,
                                                                        unsigned long long* __restrict__ rows_moved) {
@@ -524,7 +591,6 @@ __global__ __launch_bounds__(kCompactThreads) void compact_fill_kernel(unsigned 
   unsigned char* kb = K + unit * (size_t)Lmax * row_bytes;
   unsigned char* vb = V + unit * (size_t)Lmax * row_bytes;
   int32_t* pu = pos + unit * (size_t)Lmax;
-  const int lpr = row_bytes / 16;  // 16-byte pieces per row
   int moved = 0;
   for (int i0 = f; i0 < cnt; i0 += kCompactThreads) {
     const int i = i0 + tid;
@@ -538,38 +604,15 @@ __global__ __launch_bounds__(kCompactThreads) void compact_fill_kernel(unsigned 
       mv_src[r] = src;
     }
     __syncthreads();
-    const int items = nm * 2 * lpr;  // (row, tensor, piece)
-    // byte offset of piece `it` in the K (tensor 0) or V row of mover `mv`
-    auto piece = [&](int it, const int* rows, unsigned char** base) -> size_t {
-      const int mv = it / (2 * lpr), rem = it - mv * 2 * lpr;
-      *base = rem >= lpr ? vb : kb;
-      return (size_t)rows[mv] * row_bytes + (size_t)(rem >= lpr ? rem - lpr : rem) * 16;
-    };
-    for (int it0 = tid; it0 < items; it0 += kCompactThreads * kFillBatch) {
-      // kFillBatch (8) loads in flight per thread, held in named registers;
-      // past the end the last piece is loaded again and not stored
-      unsigned char* b;
-#define BKV_FILL_LD(k)                                                                     \
-  const int pc##k = min(it0 + (k) * kCompactThreads, items - 1);                          \
-  const size_t so##k = piece(pc##k, mv_src, &b);                                          \
-  const uint4 v##k = *reinterpret_cast<const uint4*>(b + so##k);
-#define BKV_FILL_ST(k)                                                                     \
-  if (it0 + (k) * kCompactThreads < items) {                                              \
-    const size_t d##k = piece(pc##k, mv_dst, &b);                                         \
-    *reinterpret_cast<uint4*>(b + d##k) = v##k;                                            \
-  }
-      BKV_FILL_LD(0) BKV_FILL_LD(1) BKV_FILL_LD(2) BKV_FILL_LD(3)
-      BKV_FILL_LD(4) BKV_FILL_LD(5) BKV_FILL_LD(6) BKV_FILL_LD(7)
-      BKV_FILL_ST(0) BKV_FILL_ST(1) BKV_FILL_ST(2) BKV_FILL_ST(3)
-      BKV_FILL_ST(4) BKV_FILL_ST(5) BKV_FILL_ST(6) BKV_FILL_ST(7)
-#undef BKV_FILL_LD
-#undef BKV_FILL_ST
-    }
+    copy_row_pairs(kb, vb, row_bytes, mv_src, mv_dst, nm);
     if (tid < nm) pu[mv_dst[tid]] = pu[mv_src[tid]];
     moved += nm;
     __syncthreads();  // the lists are rewritten by the next sweep
   }
-  if (tid == 0 && moved > 0) atomicAdd(rows_moved, 2ull * (unsigned long long)moved);  // K and V rows
+  if (tid == 0) {
+    if (moved > 0) atomicAdd(rows_moved, 2ull * (unsigned long long)moved);  // K and V rows
+    sel[2 * unit] = cnt;  // no hole left: a repeated call moves nothing
+  }
 }
 
 hipError_t launch_select(const float* scores, const int32_t* len, int N, int Hkv, int Lmax, int B, int W,
@@ -592,21 +635,45 @@ hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* 
 
 hipError_t launch_select_fill(const float* scores, const int32_t* pos, const int32_t* len, int N, int Hkv, int Lmax,
                               int B, int W, int32_t* kept, int32_t* sel, int32_t* ws_words, hipStream_t st) {
+  int32_t* p = const_cast<int32_t*>(pos);  // read only without kCompact
   if (Lmax <= kStageMax)
-    hipLaunchKernelGGL(select_fill_kernel<true>, dim3(N * Hkv), dim3(kSelThreads),
-                       2 * ((Lmax + 3) & ~3) * sizeof(uint32_t), st, scores, pos, len, Hkv, Lmax, B, W, kept, sel,
-                       ws_words);
+    hipLaunchKernelGGL((select_fill_kernel<true, false>), dim3(N * Hkv), dim3(kSelThreads),
+                       2 * ((Lmax + 3) & ~3) * sizeof(uint32_t), st, scores, p, len, Hkv, Lmax, B, W, kept, sel,
+                       ws_words, nullptr, nullptr, 0, nullptr);
   else
-    hipLaunchKernelGGL(select_fill_kernel<false>, dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, pos, len, Hkv,
-                       Lmax, B, W, kept, sel, ws_words);
+    hipLaunchKernelGGL((select_fill_kernel<false, false>), dim3(N * Hkv), dim3(kSelThreads), 0, st, scores, p, len,
+                       Hkv, Lmax, B, W, kept, sel, ws_words, nullptr, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_compact_fill(void* K, void* V, int32_t* pos, const int32_t* kept, const int32_t* sel, int32_t* len,
+// Selection and hole filling in one kernel where the unit is staged in LDS,
+// else the two kernels.
+hipError_t launch_select_compact_fill(const float* scores, void* K, void* V, int32_t* pos, int32_t* len, int N,
+                                      int Hkv, int Lmax, int B, int W, int32_t* kept, int32_t* sel, int row_bytes,
+                                      unsigned long long* rows_moved, int32_t* ws_words, hipStream_t st);
+
+hipError_t launch_compact_fill(void* K, void* V, int32_t* pos, const int32_t* kept, int32_t* sel, int32_t* len,
                                int N, int Hkv, int Lmax, int B, int row_bytes, unsigned long long* rows_moved,
                                hipStream_t st) {
   hipLaunchKernelGGL(compact_fill_kernel, dim3(N * Hkv), dim3(kCompactThreads), 0, st, (unsigned char*)K,
                      (unsigned char*)V, pos, kept, sel, len, Hkv, Lmax, B, row_bytes, rows_moved);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_compact_fill(const float* scores, void* K, void* V, int32_t* pos, int32_t* len, int N,
+                                      int Hkv, int Lmax, int B, int W, int32_t* kept, int32_t* sel, int row_bytes,
+                                      unsigned long long* rows_moved, int32_t* ws_words, hipStream_t st) {
+  if (Lmax > kStageMax) {
+    hipError_t e = launch_select_fill(scores, pos, len, N, Hkv, Lmax, B, W, kept, sel, ws_words, st);
+    if (e != hipSuccess) return e;
+    return launch_compact_fill(K, V, pos, kept, sel, len, N, Hkv, Lmax, B, row_bytes, rows_moved, st);
+  }
+  hipLaunchKernelGGL((select_fill_kernel<true, true>), dim3(N * Hkv), dim3(kSelThreads),
+                     2 * ((Lmax + 3) & ~3) * sizeof(uint32_t), st, scores, pos, len, Hkv, Lmax, B, W, kept, sel,
+                     ws_words, (unsigned char*)K, (unsigned char*)V, row_bytes, rows_moved);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fill_len_kernel, dim3((N + 255) / 256), dim3(256), 0, st, len, N, Lmax, B);
   return hipGetLastError();
 }
 

@@ -322,3 +322,53 @@ def test_fill_full_size_qwen3_4b_36_layers_batch16():
         # 128 new tokens at rows [B, L): fresh positions
         pos[:, :, B:L] = torch.arange(L + ev * (L - B), L + (ev + 1) * (L - B), dtype=torch.int32, device="cuda")
         length.fill_(L)
+
+
+@pytest.mark.parametrize("Lmax", [2184, 4200])
+def test_fill_two_calls_equal_one_call(Lmax):
+    """bkv_select_fill + bkv_compact_fill and bkv_select_compact_fill (one
+    fused kernel up to 4096 rows, the two kernels above) leave bit-identical
+    maps, K, V, positions, lengths and moved-row counts, and agree with the
+    oracle."""
+    w = configs.get(2)
+    N, Hkv, B, W = 3, w.n_kv_heads, w.budget, w.window
+    syn = synth.Synth(w, n_slots=N, seed=61, device="cuda")
+    s = syn.scores(Lmax, tie_fraction=0.3)
+    pos = (torch.argsort(syn.randn((N, Hkv, Lmax)), dim=-1) + 5).to(torch.int32).contiguous()
+    lengths = [Lmax, B + 7, Lmax - 3]
+    K0 = syn.keys(max_len=Lmax)
+    V0 = syn.values(max_len=Lmax)
+    shape = bkv.make_shape(N, Hkv, w.n_q_heads, w.head_dim, Lmax, K0.dtype)
+    out = []
+    for fused in (False, True):
+        K, V, p = K0.clone(), V0.clone(), pos.clone()
+        ws = bkv.alloc_workspace(shape, w.n_recent, w.n_beacons)
+        length = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        kept = torch.full((N, Hkv, B), -7, dtype=torch.int32, device="cuda")
+        if fused:
+            bkv.bkv_select_compact_fill(shape, s, K, V, p, length, B, W, kept, ws)
+        else:
+            bkv.bkv_select_fill(shape, s, p, length, B, W, kept, ws)
+            bkv.bkv_compact_fill(shape, K, V, p, length, B, kept, ws)
+        torch.cuda.synchronize()
+        assert bkv.bkv_read_device_status(ws) == 0
+        out.append((kept, K, V, p, length, bkv.ws_rows_moved(ws), ws))
+    (k1, K1, V1, p1, l1, m1, _), (k2, K2, V2, p2, l2, m2, ws2) = out
+    assert torch.equal(k1, k2) and torch.equal(p1, p2) and torch.equal(l1, l2) and m1 == m2
+    assert torch.equal(_bits(K1), _bits(K2)) and torch.equal(_bits(V1), _bits(V2))
+    # a compaction after the one-call form moves nothing more
+    bkv.bkv_compact_fill(shape, K2, V2, p2, l2, B, k2, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(K1), _bits(K2)) and torch.equal(p1, p2) and bkv.ws_rows_moved(ws2) == m2
+    # against the oracle
+    sn, pn, kg = s.cpu().numpy(), pos.cpu().numpy(), k2.cpu().numpy()
+    K0n, Kn, Pn = np_storage(K0), np_storage(K2), p2.cpu().numpy()
+    for n in range(N):
+        for h in range(Hkv):
+            o_map = _check_unit_exact(sn[n, h], pn[n, h], lengths[n], B, W, kg[n, h])
+            ref = np.ascontiguousarray(K0n[n, h])
+            oracle.compact(ref, o_map)
+            assert np.array_equal(Kn[n, h], ref)
+            refp = np.ascontiguousarray(pn[n, h])
+            oracle.compact(refp, o_map)
+            assert np.array_equal(Pn[n, h], refp)
