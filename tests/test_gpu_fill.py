@@ -52,9 +52,10 @@ def _check_unit_exact(s, pos, L, B, W, g_map):
     return o_map
 
 
-def _given_scores_case(w, N, s, pos, lengths, B, W, Lmax):
-    """Runs select_fill + compact_fill on given scores and positions and
-    checks every unit against the oracle, bit for bit."""
+def _given_scores_case(w, N, s, pos, lengths, B, W, Lmax, fused=True):
+    """Runs the selection and hole filling (one call, or select_fill then
+    compact_fill) on given scores and positions and checks every unit against
+    the oracle, bit for bit."""
     Hkv = w.n_kv_heads
     syn = synth.Synth(w, n_slots=N, seed=11, device="cuda")
     K = syn.keys(max_len=Lmax)
@@ -65,7 +66,11 @@ def _given_scores_case(w, N, s, pos, lengths, B, W, Lmax):
     kept = torch.full((N, Hkv, B), -7, dtype=torch.int32, device="cuda")
     posd = pos.clone()
     K_old, V_old, P_old = np_storage(K), np_storage(V), pos.cpu().numpy()
-    bkv.bkv_select_compact_fill(shape, s, K, V, posd, length, B, W, kept, ws)
+    if fused:
+        bkv.bkv_select_compact_fill(shape, s, K, V, posd, length, B, W, kept, ws)
+    else:
+        bkv.bkv_select_fill(shape, s, posd, length, B, W, kept, ws)
+        bkv.bkv_compact_fill(shape, K, V, posd, length, B, kept, ws)
     torch.cuda.synchronize()
     assert bkv.bkv_read_device_status(ws) == 0
     sn, kg = s.cpu().numpy(), kept.cpu().numpy()
@@ -113,6 +118,19 @@ def test_fill_window_zero_window_budget_and_ragged_lengths():
     for W in (0, 32, B):
         log("case: fill, window %d, lengths %s" % (W, lengths))
         _given_scores_case(w, N, s, pos, lengths, B, W, Lmax)
+
+
+@pytest.mark.parametrize("dtype,head_dim", [("f32", 64), ("bf16", 64), ("f32", 128)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_fill_storage_types_and_head_dims(dtype, head_dim, fused):
+    """Rows of 128, 256 and 512 bytes, through both entry-point forms."""
+    w = configs.get(2, dtype=dtype, head_dim=head_dim)
+    N, L, Hkv = 2, w.length, w.n_kv_heads
+    log("case: fill %s d=%d %s" % (dtype, head_dim, "one call" if fused else "two calls"))
+    syn = synth.Synth(w, n_slots=N, seed=71, device="cuda")
+    s = syn.scores(L, tie_fraction=0.2)
+    pos = torch.argsort(syn.randn((N, Hkv, L)), dim=-1).to(torch.int32).contiguous()
+    _given_scores_case(w, N, s, pos, [L, L - 100], w.budget, w.window, L, fused=fused)
 
 
 def test_fill_pairs_more_holes_than_one_lds_sweep():
@@ -259,12 +277,28 @@ def test_fill_full_path_over_evictions(interval):
 
 
 def test_fill_full_size_qwen3_4b_36_layers_batch16():
-    """The benchmark's workload (576 slots x 8 KV heads) in the hole-filling
-    layout: a first eviction with positions in row order (kept set equal to
-    the order-preserving selection's on every unit), 128 new tokens, then a
-    second eviction with permuted rows; every unit checked on the device,
-    sampled units against the oracle on the GPU's scores."""
-    w = configs.get(3)
+    """The benchmark's workload (576 slots x 8 KV heads)."""
+    _fill_full_size(3)
+
+
+def test_fill_full_size_qwen3_4b_batch320_budget1024():
+    """11,520 slots x 8 KV heads (54 GB of K and V)."""
+    _fill_full_size(4)
+
+
+def test_fill_full_size_qwen3_14b_batch32_budget4096():
+    """1,280 slots x 8 KV heads at 4,224 rows: above the LDS staging limit, so
+    the one-call form runs the two kernels."""
+    _fill_full_size(5)
+
+
+def _fill_full_size(cfg):
+    """A full-size workload in the hole-filling layout: a first eviction with
+    positions in row order (kept set equal to the order-preserving
+    selection's on every unit), new tokens, then a second eviction with
+    permuted rows; every unit checked on the device, sampled units against
+    the oracle on the same scores."""
+    w = configs.get(cfg)
     N, Hkv, L, B, W = w.n_slots, w.n_kv_heads, w.length, w.budget, w.window
     log("case: fill full size %s" % w.name)
     syn = synth.Synth(w, seed=0, device="cuda")
