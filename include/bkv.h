@@ -36,7 +36,14 @@
  *     (a length above Lmax, a buffer count outside [0, C)) set bits of the
  *     device status word in the workspace and the affected unit is left
  *     untouched; read it with bkv_read_device_status.
- *   - Calls that share a workspace must not run concurrently.
+ *   - Calls that share a workspace must not run concurrently, with two
+ *     exceptions.  bkv_fps_update only ORs bits into the status word, so it
+ *     may overlap any call that does not use its buffers (bkv_score_picked
+ *     and the selection and compaction calls do not).  bkv_beacon_picks
+ *     writes only workspace regions [5] and [6] and the status word, so it
+ *     may overlap bkv_select* and bkv_compact*; it must still come after the
+ *     bkv_score_picked that reads the previous picks (an event, as for any
+ *     cross-stream dependency).
  */
 #ifndef BKV_H
 #define BKV_H
