@@ -219,7 +219,19 @@ def timed_passes(sched, warmup, steps, ws):
     status = bkv.bkv_read_device_status(ws)
     assert status == 0, "device status %d" % status
     stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in evs[0]}
-    return elapsed, stage_ms
+    return elapsed, stage_ms, spread(evs, sched)
+
+
+def spread(evs, sched):
+    """p10 / median / p90 (ms) of every stage over the timed passes, and of
+    the main stream's span of a pass (grow start to the last tail stage's end)."""
+    def pct(xs):
+        return [float(v) for v in np.percentile(xs, [10, 50, 90])]
+
+    out = {n: pct([e[n][0].elapsed_time(e[n][1]) for e in evs]) for n in evs[0]}
+    last = sched.tail_stages[-1]
+    out["pass_main_stream"] = pct([e["grow"][0].elapsed_time(e[last][1]) for e in evs])
+    return out
 
 
 def time_hole_fill(st, warmup, steps, overlap):
@@ -245,7 +257,8 @@ def time_hole_fill(st, warmup, steps, overlap):
         bkv.bkv_select_compact_fill(st.shape, st.scores, st.K, st.V, pos, st.length, B, w.window, st.kept, st.ws)
         rec("select_compact", 1)
 
-    elapsed, stage_ms = timed_passes(Schedule(st, grow, tail, overlap, ("select_compact",)), warmup, steps, st.ws)
+    elapsed, stage_ms, stage_spread = timed_passes(Schedule(st, grow, tail, overlap, ("select_compact",)), warmup,
+                                                   steps, st.ws)
     rows_moved = bkv.ws_rows_moved(st.ws)
     row_bytes = w.head_dim * 2
     moved_per_pass = rows_moved / steps                       # K and V rows
@@ -255,6 +268,7 @@ def time_hole_fill(st, warmup, steps, overlap):
         "passes_per_s": steps / elapsed,
         "ms_per_step": elapsed * 1e3 / steps,
         "stage_ms": stage_ms,
+        "stage_ms_p10_p50_p90": stage_spread,
         "rows_moved_per_pass": moved_per_pass,
         "compact_algorithmic_bytes": compact_bytes,
         "note": "select_compact is bkv_select_compact_fill: selection and hole filling in one kernel",
@@ -278,47 +292,74 @@ def copy_probe(dev, nbytes=1 << 30, reps=10):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GBps": 2 * nbytes / ms / 1e6}
 
 
-def cpu_baseline(st: State, budget_s: float = 10.0, min_units: int = 4, max_units: int = 1024, warm_blocks: int = 3):
-    """The CPU oracle (single-threaded C, binary64) on a bounded sample of
-    (slot, KV head) units of the same workload: one period's ingest for the
-    unit's query heads, scoring, selection and compaction."""
-    import oracle
+class OracleSample:
+    """Inputs of randomly sampled (slot, KV head) units of the workload, as
+    numpy storage arrays, for timing the CPU oracle.  Each unit's query heads
+    get an untimed warm-up ingest of three periods (48 live rows, so the timed
+    period ends at 64, the mean live count of the steady state)."""
 
-    w = st.w
-    G = w.group
-    rng = np.random.default_rng(1234)
-    units_all = [(int(n), int(h)) for n, h in zip(rng.integers(0, st.N, max_units), rng.integers(0, w.n_kv_heads, max_units))]
-    blocks_np = {}
-    done = 0
-    t_total = 0.0
-    e = 0
-    p = warm_blocks
-    for (n, h) in units_all:
+    def __init__(self, st: State, warm_blocks: int = 3, seed: int = 1234):
+        self.st, self.w = st, st.w
+        self.warm_blocks = warm_blocks
+        self.rng = np.random.default_rng(seed)
+        self.units = []
+        self._blocks = {}
+
+    def _block(self, b, n, g0):
+        key = (b, n, g0)
+        if key not in self._blocks:
+            self._blocks[key] = synth.to_numpy_storage(self.st.blocks[b][n:n + 1, g0:g0 + self.w.group])
+        return self._blocks[key]
+
+    def add(self):
+        import oracle
+
+        st, w = self.st, self.w
+        G = w.group
+        n, h = int(self.rng.integers(0, st.N)), int(self.rng.integers(0, w.n_kv_heads))
         g0 = h * G
-        K_u = synth.to_numpy_storage(st.K_pristine[n, h])
-        V_u = synth.to_numpy_storage(st.V_pristine[n, h])
-        # untimed: the oracle's own warm-up ingest of the unit's query heads
-        # (three periods leave 48 live rows, so the timed period ends at 64,
-        # the mean live count of the steady state)
         qbuf = np.zeros((1, G, w.capacity, w.head_dim), dtype=np.uint16)
         qcount = np.zeros((1, G), dtype=np.int32)
-        for b in range(warm_blocks):
-            key = (b, n, h)
-            if key not in blocks_np:
-                blocks_np[key] = synth.to_numpy_storage(st.blocks[b][n:n + 1, g0:g0 + G])
-            oracle.fps_update(blocks_np[key], qbuf, qcount, w.shrink_to)
-        blk = blocks_np.setdefault((p, n, h), synth.to_numpy_storage(st.blocks[p][n:n + 1, g0:g0 + G]))
-        recent = synth.to_numpy_storage(st.recent[p][n, g0:g0 + G])
-        rpos = st.recent_pos[e, n].cpu().numpy()
-        pos_now = int(st.pos_now[e, n])
+        for b in range(self.warm_blocks):
+            oracle.fps_update(self._block(b, n, g0), qbuf, qcount, w.shrink_to)
+        p, e = self.warm_blocks, 0
+        u = {"K": synth.to_numpy_storage(st.K_pristine[n, h]), "V": synth.to_numpy_storage(st.V_pristine[n, h]),
+             "qbuf": qbuf, "qcount": qcount, "blk": self._block(p, n, g0),
+             "recent": synth.to_numpy_storage(st.recent[p][n, g0:g0 + G]),
+             "rpos": st.recent_pos[e, n].cpu().numpy(), "pos_now": int(st.pos_now[e, n])}
+        self.units.append(u)
+        return u
+
+    def run(self, u, fresh: bool):
+        """One unit: ingest of the period's block, beacon FPS and scoring at
+        L, selection, compaction of K and V.  fresh=True works on copies (the
+        unit can be run again); the copies are inside the returned time."""
+        import oracle
+
+        w = self.w
         t0 = time.perf_counter()
-        oracle.fps_update(blk, qbuf, qcount, w.shrink_to)
-        s, _, _, _ = oracle.score_unit(K_u, w.length, recent, rpos, qbuf[0], qcount[0], w.n_beacons, pos_now,
-                                       w.rope_theta)
+        if fresh:
+            K, V, qbuf, qcount = u["K"].copy(), u["V"].copy(), u["qbuf"].copy(), u["qcount"].copy()
+        else:
+            K, V, qbuf, qcount = u["K"], u["V"], u["qbuf"], u["qcount"]
+        oracle.fps_update(u["blk"], qbuf, qcount, w.shrink_to)
+        s, _, _, _ = oracle.score_unit(K, w.length, u["recent"], u["rpos"], qbuf[0], qcount[0], w.n_beacons,
+                                       u["pos_now"], w.rope_theta)
         kept = oracle.select(s, w.length, w.budget, w.window)
-        oracle.compact(K_u, kept)
-        oracle.compact(V_u, kept)
-        t_total += time.perf_counter() - t0
+        oracle.compact(K, kept)
+        oracle.compact(V, kept)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(sample: OracleSample, budget_s: float = 10.0, min_units: int = 4, max_units: int = 1024):
+    """The CPU oracle (single-threaded C, binary64) on a bounded sample of
+    units: each is run once, on its own inputs (prepared untimed)."""
+    st, w = sample.st, sample.w
+    done, t_total = 0, 0.0
+    while done < max_units:
+        u = sample.add()
+        fresh = dict(u, K=u["K"].copy(), V=u["V"].copy(), qbuf=u["qbuf"].copy(), qcount=u["qcount"].copy())
+        t_total += sample.run(fresh, fresh=False)
         done += 1
         if done >= min_units and t_total >= budget_s:
             break
@@ -331,8 +372,58 @@ def cpu_baseline(st: State, budget_s: float = 10.0, min_units: int = 4, max_unit
         "kind": "oracle",
         "sample": "%d (slot, KV head) units of the workload, each: ingest of one 128-query block for its %d query "
                   "heads, beacon FPS, scoring at L=%d, selection and compaction; %.1f s of oracle time "
-                  "(%.3f s per unit), extrapolated to %d units per pass" % (done, G, w.length, t_total, per_unit,
-                                                                           units_per_pass),
+                  "(%.3f s per unit), extrapolated to %d units per pass" % (done, w.group, w.length, t_total,
+                                                                           per_unit, units_per_pass),
+    }
+
+
+def host_threads(cap: int = 16) -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def cpu_baseline_all_cores(sample: OracleSample, budget_s: float = 10.0, threads: int = 0):
+    """The same oracle on every host thread at once: the units are
+    independent, so T threads each run sampled units (on fresh copies of
+    their inputs; the oracle's C calls release the interpreter lock) until
+    the time budget is spent.  Rate = units finished / wall time."""
+    import threading
+
+    st, w = sample.st, sample.w
+    T = threads or host_threads()
+    units = sample.units
+    assert units, "run cpu_baseline first: it prepares the sampled units"
+    counter = [0]
+    lock = threading.Lock()
+    t_start = time.perf_counter()
+    deadline = t_start + budget_s
+
+    def worker():
+        while time.perf_counter() < deadline:
+            with lock:
+                k = counter[0]
+                counter[0] += 1
+            sample.run(units[k % len(units)], fresh=True)
+
+    pool = [threading.Thread(target=worker) for _ in range(T)]
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    wall = time.perf_counter() - t_start
+    done = counter[0]
+    units_per_pass = st.N * w.n_kv_heads
+    return {
+        "value": done / wall / units_per_pass,
+        "unit": "passes/s",
+        "cores": T,
+        "kind": "oracle",
+        "sample": "%d unit runs over %d threads in %.1f s of wall time, cycling over the %d sampled units of the "
+                  "single-core baseline (fresh copies of their inputs, copies included), extrapolated to %d units "
+                  "per pass" % (done, T, wall, len(units), units_per_pass),
     }
 
 
@@ -358,6 +449,7 @@ def main():
     ap.add_argument("--no-hole-fill", action="store_true", help="skip the hole-filling layout phase")
     ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped-schedule measurement")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
+    ap.add_argument("--no-all-cores", action="store_true", help="skip the all-host-threads oracle timing")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -389,7 +481,7 @@ def main():
         rec("compact", 1)
 
     K = args.steps
-    elapsed, stage_ms = timed_passes(Schedule(st, grow, tail, False), args.warmup, K, st.ws)
+    elapsed, stage_ms, stage_spread = timed_passes(Schedule(st, grow, tail, False), args.warmup, K, st.ws)
     rows_moved = bkv.ws_rows_moved(st.ws)
 
     ms_per_step = elapsed * 1e3 / K
@@ -434,6 +526,7 @@ def main():
         "score_compact_GBps": score_compact_gbps,
         "score_compact_frac_of_peak": score_compact_gbps / HBM_PEAK_GBPS,
         "stage_ms": stage_ms,
+        "stage_ms_p10_p50_p90": stage_spread,
         "schedule": "serial: every stage on one stream (the overlapped schedule is reported under 'overlapped')",
         "algorithmic_bytes_per_step": {"score": score_bytes, "compact": compact_bytes},
         "copy_probe_GBps": cp["GBps"],
@@ -450,13 +543,14 @@ def main():
     }
     if not args.no_overlap:
         log("timing the overlapped schedule")
-        el, sm = timed_passes(Schedule(st, grow, tail, True), args.warmup, K, st.ws)
+        el, sm, sp = timed_passes(Schedule(st, grow, tail, True), args.warmup, K, st.ws)
         result["overlapped"] = {
             "schedule": "the ingest and beacon FPS of pass i+1 run on a second stream (default priority) while pass i "
                         "scores, selects and compacts; same work per pass",
             "passes_per_s": K / el,
             "ms_per_step": el * 1e3 / K,
             "stage_ms": sm,
+            "stage_ms_p10_p50_p90": sp,
         }
     if not args.no_hole_fill:
         log("timing the hole-filling layout on the same workload")
@@ -464,10 +558,15 @@ def main():
         if not args.no_overlap:
             ov = time_hole_fill(st, args.warmup, K, True)
             result["hole_fill"]["overlapped"] = {"passes_per_s": ov["passes_per_s"], "ms_per_step": ov["ms_per_step"],
-                                                 "stage_ms": ov["stage_ms"]}
+                                                 "stage_ms": ov["stage_ms"],
+                                                 "stage_ms_p10_p50_p90": ov["stage_ms_p10_p50_p90"]}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(st, budget_s=args.cpu_budget)
+        sample = OracleSample(st)
+        result["cpu_baseline"] = cpu_baseline(sample, budget_s=args.cpu_budget)
+        if not args.no_all_cores:
+            log("timing the CPU oracle on %d host threads" % host_threads())
+            result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(sample, budget_s=args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
