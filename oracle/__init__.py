@@ -57,6 +57,10 @@ def lib():
         L.orc_fps_objectives.restype = None
         L.orc_fps_stored.argtypes = [P, I, I, I, I, P]
         L.orc_fps_stored.restype = I
+        L.orc_fps_full.argtypes = [P, I, I, I, I, P]
+        L.orc_fps_full.restype = I
+        L.orc_fps_full_objectives.argtypes = [P, I, I, I, P, I, P]
+        L.orc_fps_full_objectives.restype = None
         L.orc_fps_ingest.argtypes = [P, I, I, I, I, P, P, I]
         L.orc_fps_ingest.restype = I
         L.orc_rope.argtypes = [P, I, LONG, D, P]
@@ -134,14 +138,16 @@ def fps_objectives(X: np.ndarray, prefix) -> np.ndarray:
     return out[:c].copy()
 
 
-def check_fps_sequence(X: np.ndarray, picks, tol: float):
+def check_fps_sequence(X: np.ndarray, picks, tol: float, objectives=None):
     """Checks that ``picks`` is a valid FPS run over the rows of X: every pick
     is an unpicked row whose objective is within ``tol`` of the round's
-    minimum.  Returns the largest excess over the minimum."""
+    minimum.  Returns the largest excess over the minimum.  ``objectives``
+    (default fps_objectives) maps (X, prefix) to the per-row objective."""
+    objectives = objectives or fps_objectives
     picked = np.zeros(X.shape[0], dtype=bool)
     worst = 0.0
     for t, p in enumerate(picks):
-        obj = fps_objectives(X, list(picks[:t]))
+        obj = objectives(X, list(picks[:t]))
         assert not picked[p], "row %d picked twice" % p
         best = np.min(obj[~picked])
         excess = obj[p] - best
@@ -158,6 +164,28 @@ def fps_stored(buf: np.ndarray, count: int, k: int) -> np.ndarray:
     picks = np.empty(max(k, 1), dtype=np.int32)
     n = lib().orc_fps_stored(_ptr(buf), dtype_code(buf), count, d, k, _ptr(picks))
     return picks[:n].copy()
+
+
+def fps_full(X: np.ndarray, k: int) -> np.ndarray:
+    """Naive FPS picks (pick order) of up to k rows of a head's whole stored
+    query history X [c, d] (storage dtype)."""
+    X = np.ascontiguousarray(X)
+    c, d = X.shape
+    picks = np.empty(max(k, 1), dtype=np.int32)
+    n = lib().orc_fps_full(_ptr(X), dtype_code(X), c, d, k, _ptr(picks))
+    return picks[:n].copy()
+
+
+def fps_full_objectives(X: np.ndarray, prefix) -> np.ndarray:
+    """fps_objectives for a stored history X [c, d], with the start rule's mean
+    similarity taken through the summed normalised row (as fps_full does)."""
+    X = np.ascontiguousarray(X)
+    c, d = X.shape
+    pre = np.ascontiguousarray(np.asarray(prefix, dtype=np.int32).reshape(-1))
+    out = np.empty(max(c, 1), dtype=np.float64)
+    lib().orc_fps_full_objectives(_ptr(X), dtype_code(X), c, d, _ptr(pre) if pre.size else None, int(pre.size),
+                                  _ptr(out))
+    return out[:c].copy()
 
 
 def fps_ingest(buf: np.ndarray, count: int, q_new: np.ndarray, M: int) -> int:

@@ -208,6 +208,103 @@ int orc_fps_stored(const void *buf, int dtype, int c, int d, int k, int *picks) 
 }
 
 /*
+ * orc_fps_full: FPS over a head's whole stored query history buf[c][d], the
+ * naive alternative that Continual FPS replaces.
+ * [WZ, 怎么挑出这几个信标]: running FPS over every query seen so far would mean
+ * keeping the full history of each head; the bounded, repeatedly compressed
+ * buffer exists to avoid exactly that.  The picking rule and its readings are
+ * orc_fps's: start at the lowest mean cosine similarity (self included), then
+ * take the unpicked row with the lowest maximum cosine to the picked ones,
+ * ties to the lowest index, norms clamped at 1e-12.
+ *
+ * The start rule's mean similarity of row i is evaluated as
+ * x^_i . (sum_j x^_j) / c.  By linearity of the dot product this is the
+ * pairwise mean of orc_fps (rounding order aside), in O(c*d) instead of
+ * O(c^2*d) operations, which keeps histories of tens of thousands of queries
+ * tractable.  Rows are widened exactly to binary64 first.
+ *
+ * Returns min(k, c) picks, written to picks[] in pick order.
+ */
+static double *normalised_rows(const void *buf, int dtype, int c, int d) {
+  double *xh = (double *)malloc(sizeof(double) * (size_t)(c > 0 ? c : 1) * d);
+  for (int i = 0; i < c; ++i) {
+    double *r = xh + (size_t)i * d;
+    for (int t = 0; t < d; ++t) r[t] = orc_load(buf, dtype, (long)i * d + t);
+    double n = sqrt(dot(r, r, d));
+    if (n < 1e-12) n = 1e-12;
+    for (int t = 0; t < d; ++t) r[t] /= n;
+  }
+  return xh;
+}
+
+/* Mean cosine similarity of every row to all c rows, via the summed row. */
+static void mean_similarity(const double *xh, int c, int d, double *mu) {
+  double *sum = (double *)calloc((size_t)d, sizeof(double));
+  for (int j = 0; j < c; ++j)
+    for (int t = 0; t < d; ++t) sum[t] += xh[(size_t)j * d + t];
+  for (int i = 0; i < c; ++i) mu[i] = dot(xh + (size_t)i * d, sum, d) / c;
+  free(sum);
+}
+
+int orc_fps_full(const void *buf, int dtype, int c, int d, int k, int *picks) {
+  int kk = k < c ? k : c;
+  if (kk <= 0) return 0;
+  double *xh = normalised_rows(buf, dtype, c, d);
+  double *m = (double *)malloc(sizeof(double) * c);
+  char *picked = (char *)calloc(c, 1);
+
+  mean_similarity(xh, c, d, m);
+  int start = 0;
+  for (int i = 1; i < c; ++i)
+    if (m[i] < m[start]) start = i;
+  picks[0] = start;
+  picked[start] = 1;
+  for (int i = 0; i < c; ++i) m[i] = dot(xh + (size_t)i * d, xh + (size_t)start * d, d);
+
+  for (int t = 1; t < kk; ++t) {
+    int best = -1;
+    for (int i = 0; i < c; ++i) {
+      if (picked[i]) continue;
+      if (best < 0 || m[i] < m[best]) best = i;
+    }
+    if (best < 0) best = 0; /* unreachable: kk <= c leaves an unpicked row */
+    picks[t] = best;
+    picked[best] = 1;
+    for (int i = 0; i < c; ++i) {
+      double s = dot(xh + (size_t)i * d, xh + (size_t)best * d, d);
+      if (s > m[i]) m[i] = s;
+    }
+  }
+  free(xh);
+  free(m);
+  free(picked);
+  return kk;
+}
+
+/*
+ * orc_fps_full_objectives: orc_fps_objectives for a stored history, with the
+ * start rule's mean similarity evaluated as in orc_fps_full.  out[i] is the
+ * mean cosine of row i to all c rows for an empty prefix, else its maximum
+ * cosine to the picked rows prefix[0..np).
+ */
+void orc_fps_full_objectives(const void *buf, int dtype, int c, int d, const int *prefix, int np, double *out) {
+  double *xh = normalised_rows(buf, dtype, c, d);
+  if (np == 0) {
+    mean_similarity(xh, c, d, out);
+  } else {
+    for (int i = 0; i < c; ++i) {
+      double m = -INFINITY;
+      for (int q = 0; q < np; ++q) {
+        double s = dot(xh + (size_t)i * d, xh + (size_t)prefix[q] * d, d);
+        if (s > m) m = s;
+      }
+      out[i] = m;
+    }
+  }
+  free(xh);
+}
+
+/*
  * orc_fps_ingest: Continual FPS for one attention head.
  * [WZ, 怎么挑出这几个信标]: each attention head keeps only a small buffer with
  * an upper bound on its size; once the buffer is full an FPS pass compresses
