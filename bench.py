@@ -42,7 +42,7 @@ N_EVENTS = 240      # evictions in a 32K-token generation (first at L = 2176)
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("fps.hip", "score.hip", "select.hip", "bkv_api.hip", "bkv_device.hpp"):
+    for name in ("fps.hip", "score.hip", "select.hip", "bkv_api.hip", "bkv_device.hpp", "fps_full.hip"):
         with open(os.path.join(ROOT, "kv_cache_eviction_continual_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -427,6 +427,118 @@ def cpu_baseline_all_cores(sample: OracleSample, budget_s: float = 10.0, threads
     }
 
 
+def covering_radius_deg(hist, beacons, heads_per_batch=8):
+    """Per head: the largest angle (degrees) from any row of the history to
+    its nearest beacon (the k-centre objective FPS greedily minimises).
+    hist [N, Hq, n, d] and beacons [N, Hq, k, d] storage tensors; returns a
+    float64 array [N, Hq].  A reported statistic, evaluated in fp32 with torch."""
+    N, Hq, n, d = hist.shape
+    out = np.empty((N, Hq))
+    for s in range(N):
+        for g0 in range(0, Hq, heads_per_batch):
+            X = hist[s, g0:g0 + heads_per_batch].float()
+            X = X / X.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+            B = beacons[s, g0:g0 + heads_per_batch].float()
+            B = B / B.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+            cos = torch.bmm(X, B.transpose(1, 2).contiguous()).amax(dim=-1)      # nearest beacon per row
+            worst = cos.amin(dim=-1).clamp(-1.0, 1.0)                            # farthest row per head
+            out[s, g0:g0 + heads_per_batch] = torch.rad2deg(torch.arccos(worst)).double().cpu().numpy()
+    return out
+
+
+def fps_compare(reps: int = 3):
+    """Naive full-history FPS against Continual FPS on one layer of the
+    Qwen3-14B workload (batch 32, 40 query heads: 1,280 heads) over a
+    32,768-query generation with an eviction every 128 steps: time per
+    eviction and over the generation, memory, and the beacons' covering
+    radius at the end.  Prints its own JSON line."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bkv.load()
+    w = configs.get(5)
+    N, Hq, d, n = w.batch, w.n_q_heads, w.head_dim, 32768
+    k, C, M, T = w.n_beacons, w.capacity, w.shrink_to, w.interval
+    heads = N * Hq
+    events = n // T
+    log("generating the %d-query history of %d heads" % (n, heads))
+    syn = synth.Synth(w, n_slots=N, seed=0, device=dev)
+    blocks = [syn.query_block(b) for b in range(events)]
+    hist = torch.cat(blocks, dim=2).contiguous()
+    es = hist.element_size()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, r):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(r):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / r
+
+    # naive: FPS over the whole history so far, at several history lengths
+    naive = {}
+    picks = torch.empty(N, Hq, k, dtype=torch.int32, device=dev)
+    ws_full = torch.empty(bkv.bkv_fps_full_workspace_size(bkv.make_shape(N, 1, Hq, d, n, hist.dtype), n),
+                          dtype=torch.uint8, device=dev)
+    for m in (4096, 8192, 16384, n):
+        h = hist if m == n else hist[:, :, :m].contiguous()
+        shape = bkv.make_shape(N, 1, Hq, d, m, hist.dtype)
+        ms = timed(lambda: bkv.bkv_fps_full(shape, h, m, k, picks, ws_full), reps)
+        # the start and every pick stream the history once; norms and running maxima add 24 B per row per pick
+        nbytes = (k + 1) * heads * m * d * es + k * heads * m * 24
+        naive[m] = {"ms": ms, "algorithmic_bytes": nbytes, "GBps": nbytes / (ms * 1e6)}
+        del h
+    naive_beacons = torch.gather(hist, 2, picks.long().unsqueeze(-1).expand(N, Hq, k, d))
+    xs = np.array(sorted(naive), dtype=np.float64)
+    ys = np.array([naive[m]["ms"] for m in sorted(naive)])
+    slope, icpt = np.polyfit(xs, ys, 1)
+    naive_total = float(sum(icpt + slope * T * e for e in range(1, events + 1)))
+
+    # continual: each period's queries go through the C-row buffer, then the beacon FPS, at every eviction
+    eshape = bkv.make_shape(N, w.n_kv_heads, Hq, d, 1, hist.dtype)
+    ws = bkv.alloc_workspace(eshape, w.n_recent, k, device=dev)
+    qbuf = torch.empty(N, Hq, C, d, dtype=hist.dtype, device=dev)
+    qcount = torch.zeros(N, Hq, dtype=torch.int32, device=dev)
+
+    def continual():
+        qcount.zero_()
+        for blk in blocks:
+            bkv.bkv_fps_update(eshape, blk, T, qbuf, qcount, C, M, ws)
+            bkv.bkv_beacon_picks(eshape, qbuf, qcount, C, w.n_recent, k, ws)
+
+    cont_total = timed(continual, reps)
+    assert bkv.bkv_read_device_status(ws) == 0
+    cont_beacons = bkv.ws_views(eshape, w.n_recent, k, ws)["beacon_rows"].clone()
+
+    r_naive = covering_radius_deg(hist, naive_beacons)
+    r_cont = covering_radius_deg(hist, cont_beacons)
+    result = {
+        "metric": "full-history FPS vs Continual FPS: time, memory, covering radius",
+        "workload": "one layer of qwen3-14b-40layers-b32: %d query heads, a %d-step generation with an eviction every "
+                    "%d steps, %d beacons; Continual FPS buffer %d -> %d" % (heads, n, T, k, C, M),
+        "data": "synthetic",
+        "dtype": "bf16 storage; FPS cosines in binary64 (full history) / fp32 with binary64 decisions (buffer)",
+        "naive_per_eviction": {str(m): v for m, v in naive.items()},
+        "naive_fit_ms": {"intercept": float(icpt), "per_query": float(slope)},
+        "naive_generation_ms": naive_total,
+        "naive_memory_bytes_per_head_at_end": n * d * es,
+        "continual_generation_ms": cont_total,
+        "continual_per_eviction_ms": cont_total / events,
+        "continual_memory_bytes_per_head": C * d * es,
+        "memory_ratio_at_end": (n * d * es) / (C * d * es),
+        "generation_time_ratio": naive_total / cont_total,
+        "covering_radius_deg_at_end": {
+            "naive_mean": float(r_naive.mean()), "naive_max": float(r_naive.max()),
+            "continual_mean": float(r_cont.mean()), "continual_max": float(r_cont.max()),
+            "continual_over_naive_mean": float((r_cont / r_naive).mean()),
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def load_traffic(src_hash):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -450,12 +562,17 @@ def main():
     ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped-schedule measurement")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-all-cores", action="store_true", help="skip the all-host-threads oracle timing")
+    ap.add_argument("--fps-compare", action="store_true",
+                    help="instead of the eviction pass: full-history FPS vs Continual FPS on one Qwen3-14B layer")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.fps_compare:
+        fps_compare()
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = configs.get(CFG)

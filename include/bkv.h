@@ -288,6 +288,36 @@ int bkv_select_compact_fill(const bkv_shape *shape, const float *scores, void *K
                             int32_t *pos, int32_t *len, int32_t budget, int32_t window,
                             int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * bkv_fps_full -- FPS over each query head's WHOLE stored history: the naive
+ * alternative that Continual FPS replaces ([WZ] 怎么挑出这几个信标: FPS over
+ * every past query would keep the full history of each head, which the
+ * bounded buffer avoids).  For comparing the two; not a step of the
+ * eviction pass.
+ *
+ *   hist   [N][Hq][n][d]  the first n pre-RoPE queries of every query head,
+ *                         16-byte aligned (read only)
+ *   n      >= 0, <= 1 << 24
+ *   k      0 <= k <= 4096 picks per head
+ *   picks  [N][Hq][k]     int32 out: row indices in pick order; entries from
+ *                         min(k, n) on are -1
+ *   ws     its own workspace, 256-byte aligned, at least
+ *          bkv_fps_full_workspace_size(shape, n) bytes (row norms, running
+ *          maximum cosines, per-chunk partial results); no status word
+ *
+ * The picking rule is bkv_fps_update's (lowest mean cosine start, then the
+ * row with the lowest maximum cosine to the picked set, ties to the lower
+ * row, norms clamped at 1e-12), evaluated in binary64; the mean cosine of a
+ * row is its dot product with the sum of the normalised rows, divided by its
+ * norm and n.  Every pick reads the whole history once: min(k, n) + 1
+ * passes over hist.  Rows must be finite (with non-finite rows the picks
+ * are unspecified, though still inside [0, n)).  Only shape->n_seq,
+ * n_q_heads, head_dim and dtype are used.
+ */
+size_t bkv_fps_full_workspace_size(const bkv_shape *shape, int32_t n);
+int bkv_fps_full(const bkv_shape *shape, const void *hist, int32_t n, int32_t k, int32_t *picks,
+                 void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Text for a bkv_status value (static string). */
 const char *bkv_status_string(int status);
 

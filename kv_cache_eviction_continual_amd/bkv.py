@@ -40,6 +40,8 @@ EXPORTS = (
     "bkv_select_fill",
     "bkv_compact_fill",
     "bkv_select_compact_fill",
+    "bkv_fps_full_workspace_size",
+    "bkv_fps_full",
     "bkv_status_string",
     "bkv_read_device_status",
     "bkv_reset_device_status",
@@ -103,6 +105,10 @@ def load() -> ctypes.CDLL:
     L.bkv_compact_fill.restype = ctypes.c_int
     L.bkv_select_compact_fill.argtypes = [SP, P, P, P, P, P, I32, I32, P, P, SZ, P]
     L.bkv_select_compact_fill.restype = ctypes.c_int
+    L.bkv_fps_full_workspace_size.argtypes = [SP, I32]
+    L.bkv_fps_full_workspace_size.restype = SZ
+    L.bkv_fps_full.argtypes = [SP, P, I32, I32, P, P, SZ, P]
+    L.bkv_fps_full.restype = ctypes.c_int
     L.bkv_status_string.argtypes = [ctypes.c_int]
     L.bkv_status_string.restype = ctypes.c_char_p
     L.bkv_read_device_status.argtypes = [P, ctypes.POINTER(I32), P]
@@ -215,6 +221,15 @@ def bkv_select_compact_fill(shape: Shape, scores, K, V, pos, length, budget: int
     _check(load().bkv_select_compact_fill(ctypes.byref(shape), _ptr(scores), _ptr(K), _ptr(V), _ptr(pos),
                                           _ptr(length), budget, window, _ptr(kept), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_fps_full_workspace_size(shape: Shape, n: int) -> int:
+    return int(load().bkv_fps_full_workspace_size(ctypes.byref(shape), n))
+
+
+def bkv_fps_full(shape: Shape, hist, n: int, k: int, picks, ws, stream=None) -> None:
+    _check(load().bkv_fps_full(ctypes.byref(shape), _ptr(hist), n, k, _ptr(picks), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bkv_status_string(status: int) -> str:

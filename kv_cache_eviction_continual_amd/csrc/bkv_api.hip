@@ -27,6 +27,10 @@ hipError_t launch_compact_fill(void*, void*, int32_t*, const int32_t*, int32_t*,
 hipError_t launch_select_compact_fill(const float*, void*, void*, int32_t*, int32_t*, int, int, int, int, int,
                                       int32_t*, int32_t*, int, unsigned long long*, int32_t*, hipStream_t);
 
+template <int DT, int D>
+hipError_t launch_fps_full(const void*, long, long, int, int32_t*, void*, hipStream_t);
+size_t fps_full_workspace_bytes(long, long, int);
+
 __global__ void zero_header_kernel(int32_t* w) {
   if (threadIdx.x < (int)(kHeaderBytes / 4)) w[threadIdx.x] = 0;
 }
@@ -37,6 +41,8 @@ constexpr int kMaxCapacity = 256;
 constexpr int kMaxRows = 256;
 constexpr int kMaxRecent = 64;
 constexpr int kMaxLen = 1 << 24;
+constexpr int kMaxHistory = 1 << 24;
+constexpr int kMaxFullPicks = 4096;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -202,6 +208,32 @@ int bkv_fps_update(const bkv_shape* shape, const void* q_new, int32_t T, void* q
   else
     e = shape->head_dim == 128 ? launch_fps_update<BKV_F32, 128>(q_new, T, qbuf, qcount, C, M, heads, w, stream)
                                : launch_fps_update<BKV_F32, 64>(q_new, T, qbuf, qcount, C, M, heads, w, stream);
+  return hip_status(e);
+}
+
+size_t bkv_fps_full_workspace_size(const bkv_shape* shape, int32_t n) {
+  if (check_shape(shape) != BKV_OK || n < 0 || n > kMaxHistory) return 0;
+  return fps_full_workspace_bytes((long)shape->n_seq * shape->n_q_heads, n, shape->head_dim);
+}
+
+int bkv_fps_full(const bkv_shape* shape, const void* hist, int32_t n, int32_t k, int32_t* picks, void* ws,
+                 size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (n < 0 || n > kMaxHistory || k < 0 || k > kMaxFullPicks) return BKV_E_SHAPE;
+  const long heads = (long)shape->n_seq * shape->n_q_heads;
+  if (heads == 0 || k == 0) return BKV_OK;
+  if (!picks || (n > 0 && !hist)) return BKV_E_NULL;
+  if (n > 0 && ((uintptr_t)hist & 15u) != 0) return BKV_E_SHAPE;
+  if (heads * (((long)n + 1023) / 1024) > INT32_MAX || heads > INT32_MAX) return BKV_E_SHAPE;  // grid size
+  if ((st = check_ws(ws, ws_bytes, bkv_fps_full_workspace_size(shape, n))) != BKV_OK) return st;
+  hipError_t e;
+  if (shape->dtype == BKV_BF16)
+    e = shape->head_dim == 128 ? launch_fps_full<BKV_BF16, 128>(hist, heads, n, k, picks, ws, stream)
+                               : launch_fps_full<BKV_BF16, 64>(hist, heads, n, k, picks, ws, stream);
+  else
+    e = shape->head_dim == 128 ? launch_fps_full<BKV_F32, 128>(hist, heads, n, k, picks, ws, stream)
+                               : launch_fps_full<BKV_F32, 64>(hist, heads, n, k, picks, ws, stream);
   return hip_status(e);
 }
 

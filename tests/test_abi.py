@@ -154,3 +154,30 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.bkv_fps_update(ctypes.byref(s), fake, 4, fake, fake, 128, 16, fake, 1 << 20, None) == bkv.OK
     assert lib.bkv_select(ctypes.byref(s), fake, fake, 2048, 32, fake, fake, 1 << 20, None) == bkv.OK
     assert lib.bkv_compact(ctypes.byref(s), fake, fake, fake, 2048, fake, fake, 1 << 20, None) == bkv.OK
+
+
+def test_fps_full_validation_and_workspace_size(lib):
+    s = shape(n_seq=32, n_kv_heads=8, n_q_heads=40)
+    heads, n = 32 * 40, 32768
+    need = bkv.bkv_fps_full_workspace_size(s, n)
+    # row norms and running maxima (binary64 per row), per-chunk sums (d binary64 per 1024 rows), two candidate sets
+    assert need >= heads * n * 8 * 2 + heads * (n // 1024) * 128 * 8 + 2 * heads * (n // 1024) * 16
+    assert need < heads * n * 8 * 2 + (8 << 20) + heads * (n // 1024) * 128 * 8 * 2
+    assert bkv.bkv_fps_full_workspace_size(s, -1) == 0
+    assert bkv.bkv_fps_full_workspace_size(shape(head_dim=96), 100) == 0
+    fake, big, P = 256, 1 << 40, None
+    f = lib.bkv_fps_full
+    assert f(None, fake, n, 32, fake, fake, big, P) == bkv.E_NULL
+    assert f(ctypes.byref(s), fake, -1, 32, fake, fake, big, P) == bkv.E_SHAPE
+    assert f(ctypes.byref(s), fake, (1 << 24) + 1, 32, fake, fake, big, P) == bkv.E_SHAPE
+    assert f(ctypes.byref(s), fake, n, -1, fake, fake, big, P) == bkv.E_SHAPE
+    assert f(ctypes.byref(s), fake, n, 5000, fake, fake, big, P) == bkv.E_SHAPE
+    assert f(ctypes.byref(s), None, n, 32, fake, fake, big, P) == bkv.E_NULL
+    assert f(ctypes.byref(s), fake, n, 32, None, fake, big, P) == bkv.E_NULL
+    assert f(ctypes.byref(s), fake + 8, n, 32, fake, fake, big, P) == bkv.E_SHAPE  # history not 16-byte aligned
+    assert f(ctypes.byref(s), fake, n, 32, fake, fake + 8, big, P) == bkv.E_WORKSPACE
+    assert f(ctypes.byref(s), fake, n, 32, fake, fake, need - 1, P) == bkv.E_WORKSPACE
+    assert f(ctypes.byref(shape(dtype=3)), fake, n, 32, fake, fake, big, P) == bkv.E_DTYPE
+    # nothing to do
+    assert f(ctypes.byref(shape(n_seq=0)), fake, n, 32, fake, fake, big, P) == bkv.OK
+    assert f(ctypes.byref(s), fake, n, 0, fake, fake, big, P) == bkv.OK
