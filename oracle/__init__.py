@@ -67,6 +67,8 @@ def lib():
         L.orc_rope.restype = None
         L.orc_score_unit.argtypes = [I, I, I, P, I, P, P, I, P, P, I, I, LONG, D, P, P, P, P]
         L.orc_score_unit.restype = I
+        L.orc_score_given.argtypes = [I, I, I, P, I, P, P, I, P, P, I, LONG, D, I, P, P, P, P]
+        L.orc_score_given.restype = I
         L.orc_select.argtypes = [P, I, I, I, P]
         L.orc_select.restype = I
         L.orc_compact.argtypes = [P, LONG, P, I]
@@ -253,6 +255,40 @@ def score_unit(K: np.ndarray, L: int, recent: np.ndarray, recent_pos: np.ndarray
                               C, nb, int(pos_now), float(theta), _ptr(scores), _ptr(obs), _ptr(valid), _ptr(lse))
     if rc != 0:
         raise ValueError("oracle score rejected a query count")
+    return scores[:L].copy(), obs[:rows].copy(), valid[:rows].copy(), lse[:rows].copy()
+
+
+AGG_MAX = 0
+AGG_MEAN = 1
+
+
+def score_given(K: np.ndarray, L: int, recent: np.ndarray, recent_pos: np.ndarray, brows: np.ndarray,
+                bcount: np.ndarray, pos_now: int, theta: float, agg: int = AGG_MAX):
+    """Scores of one (slot, KV head) with given beacon rows and a choice of
+    aggregation (AGG_MAX or AGG_MEAN over the present rows).
+
+    K [>=L, d] storage; recent [G, R, d]; recent_pos [R]; brows [G, nb, d]
+    storage; bcount [G] (rows [0, bcount[g]) of head g are its beacons).
+    Returns (scores float64 [L], obs rows [G*(R+nb), d], valid [rows], lse [rows]).
+    """
+    K = np.ascontiguousarray(K)
+    recent = np.ascontiguousarray(recent)
+    brows = np.ascontiguousarray(brows)
+    rp = np.ascontiguousarray(recent_pos, dtype=np.int32)
+    bc = np.ascontiguousarray(bcount, dtype=np.int32)
+    G, R, d = recent.shape
+    nb = brows.shape[1]
+    dt = dtype_code(K)
+    assert dtype_code(recent) == dt and dtype_code(brows) == dt
+    rows = G * (R + nb)
+    scores = np.zeros(max(L, 1), dtype=np.float64)
+    obs = np.zeros((max(rows, 1), d), dtype=K.dtype)
+    valid = np.zeros(max(rows, 1), dtype=np.int32)
+    lse = np.zeros(max(rows, 1), dtype=np.float64)
+    rc = lib().orc_score_given(dt, d, G, _ptr(K), L, _ptr(recent), _ptr(rp), R, _ptr(brows), _ptr(bc), nb,
+                               int(pos_now), float(theta), int(agg), _ptr(scores), _ptr(obs), _ptr(valid), _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle score_given rejected a beacon count")
     return scores[:L].copy(), obs[:rows].copy(), valid[:rows].copy(), lse[:rows].copy()
 
 

@@ -375,6 +375,69 @@ void orc_rope(const double *x, int d, long pos, double theta, double *y) {
 /* Beacon-guided scoring of one (sequence slot, KV head)                      */
 /* ------------------------------------------------------------------------ */
 
+/* One observation row: a stored pre-RoPE query rotated to position pos and
+ * rounded once to the storage type (reading R8), widened back to binary64. */
+static void rotated_row(const char *src, int dtype, int d, long pos, double theta, double *x, double *yr,
+                        double *out) {
+  for (int t = 0; t < d; ++t) x[t] = orc_load(src, dtype, t);
+  orc_rope(x, d, pos, theta, yr);
+  for (int t = 0; t < d; ++t) {
+    char cell[4];
+    orc_store(cell, dtype, 0, yr[t]);
+    out[t] = orc_load(cell, dtype, 0);
+  }
+}
+
+#define ORC_AGG_MAX 0
+#define ORC_AGG_MEAN 1
+
+/*
+ * score_rows: logits of the present observation rows y[rows][d] against the L
+ * stored keys (q.k / sqrt(d), binary64), each row's log-sum-exp over all L
+ * keys, and the aggregate over rows of every key's softmax probability:
+ * the maximum (ORC_AGG_MAX) or the mean over the present rows
+ * (ORC_AGG_MEAN).  No present row gives scores 0; absent rows get lse +inf.
+ */
+static void score_rows(int dtype, int d, int rows, const double *y, const int *valid, const void *K, int L,
+                       int agg, double *scores, double *lse_r) {
+  double *s = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * (L > 0 ? L : 1));
+  double *kj = (double *)malloc(sizeof(double) * d);
+  double inv_sqrt_d = 1.0 / sqrt((double)d);
+  for (int j = 0; j < L; ++j) {
+    for (int t = 0; t < d; ++t) kj[t] = orc_load(K, dtype, (long)j * d + t);
+    for (int r = 0; r < rows; ++r) {
+      if (!valid[r]) continue;
+      s[(size_t)r * L + j] = dot(y + (size_t)r * d, kj, d) * inv_sqrt_d;
+    }
+  }
+  int present = 0;
+  for (int r = 0; r < rows; ++r) {
+    if (!valid[r] || L == 0) {
+      lse_r[r] = INFINITY;
+      continue;
+    }
+    present += 1;
+    double mx = -INFINITY;
+    for (int j = 0; j < L; ++j)
+      if (s[(size_t)r * L + j] > mx) mx = s[(size_t)r * L + j];
+    double sum = 0.0;
+    for (int j = 0; j < L; ++j) sum += exp(s[(size_t)r * L + j] - mx);
+    lse_r[r] = mx + log(sum);
+  }
+  for (int j = 0; j < L; ++j) {
+    double best = 0.0, total = 0.0;
+    for (int r = 0; r < rows; ++r) {
+      if (!valid[r]) continue;
+      double p = exp(s[(size_t)r * L + j] - lse_r[r]);
+      if (p > best) best = p;
+      total += p;
+    }
+    scores[j] = agg == ORC_AGG_MEAN ? (present > 0 ? total / present : 0.0) : best;
+  }
+  free(s);
+  free(kj);
+}
+
 /*
  * orc_score_unit: importance scores of the L cached keys of one KV head.
  *
@@ -413,6 +476,7 @@ int orc_score_unit(int dtype, int d, int G, const void *K, int L,
   double *x = (double *)malloc(sizeof(double) * d);
   double *yr = (double *)malloc(sizeof(double) * d);
   int *picks = (int *)malloc(sizeof(int) * (nb > 0 ? nb : 1));
+  double *lse_r = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
   int status = 0;
 
   for (int g = 0; g < G; ++g) {
@@ -421,14 +485,7 @@ int orc_score_unit(int dtype, int d, int G, const void *K, int L,
       int row = g * (R + nb) + r;
       if (recent_pos[r] < 0) continue;
       const char *src = (const char *)recent + es * (size_t)d * ((size_t)g * R + r);
-      for (int t = 0; t < d; ++t) x[t] = orc_load(src, dtype, t);
-      orc_rope(x, d, recent_pos[r], theta, yr);
-      for (int t = 0; t < d; ++t) {
-        /* single rounding to the storage type */
-        char cell[4];
-        orc_store(cell, dtype, 0, yr[t]);
-        y[(size_t)row * d + t] = orc_load(cell, dtype, 0);
-      }
+      rotated_row(src, dtype, d, recent_pos[r], theta, x, yr, y + (size_t)row * d);
       valid[row] = 1;
     }
     /* beacons: FPS over the buffer, rotated to the current decode position */
@@ -442,50 +499,12 @@ int orc_score_unit(int dtype, int d, int G, const void *K, int L,
     for (int b = 0; b < nsel; ++b) {
       int row = g * (R + nb) + R + b;
       const char *src = hb + es * (size_t)d * picks[b];
-      for (int t = 0; t < d; ++t) x[t] = orc_load(src, dtype, t);
-      orc_rope(x, d, pos_now, theta, yr);
-      for (int t = 0; t < d; ++t) {
-        char cell[4];
-        orc_store(cell, dtype, 0, yr[t]);
-        y[(size_t)row * d + t] = orc_load(cell, dtype, 0);
-      }
+      rotated_row(src, dtype, d, pos_now, theta, x, yr, y + (size_t)row * d);
       valid[row] = 1;
     }
   }
 
-  /* logits, per-row log-sum-exp, max over rows of the softmax probability */
-  double *s = (double *)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * (L > 0 ? L : 1));
-  double *kj = (double *)malloc(sizeof(double) * d);
-  double inv_sqrt_d = 1.0 / sqrt((double)d);
-  for (int j = 0; j < L; ++j) {
-    for (int t = 0; t < d; ++t) kj[t] = orc_load(K, dtype, (long)j * d + t);
-    for (int r = 0; r < rows; ++r) {
-      if (!valid[r]) continue;
-      s[(size_t)r * L + j] = dot(y + (size_t)r * d, kj, d) * inv_sqrt_d;
-    }
-  }
-  double *lse_r = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
-  for (int r = 0; r < rows; ++r) {
-    if (!valid[r] || L == 0) {
-      lse_r[r] = INFINITY;
-      continue;
-    }
-    double mx = -INFINITY;
-    for (int j = 0; j < L; ++j)
-      if (s[(size_t)r * L + j] > mx) mx = s[(size_t)r * L + j];
-    double sum = 0.0;
-    for (int j = 0; j < L; ++j) sum += exp(s[(size_t)r * L + j] - mx);
-    lse_r[r] = mx + log(sum);
-  }
-  for (int j = 0; j < L; ++j) {
-    double best = 0.0;
-    for (int r = 0; r < rows; ++r) {
-      if (!valid[r]) continue;
-      double p = exp(s[(size_t)r * L + j] - lse_r[r]);
-      if (p > best) best = p;
-    }
-    scores[j] = best;
-  }
+  score_rows(dtype, d, rows, y, valid, K, L, ORC_AGG_MAX, scores, lse_r);
 
   if (obs) {
     for (int r = 0; r < rows; ++r)
@@ -501,8 +520,71 @@ int orc_score_unit(int dtype, int d, int G, const void *K, int L,
   free(x);
   free(yr);
   free(picks);
-  free(s);
-  free(kj);
+  free(lse_r);
+  return status;
+}
+
+/*
+ * orc_score_given: orc_score_unit with the beacon rows given instead of
+ * chosen by FPS, and a choice of aggregation.  The policy variants the pages
+ * compare BeaconKV against run through it:
+ *   - [WZ, 效果到底怎么样]: InitialRecent keeps the earliest generated queries
+ *     together with the recent ones (the given rows are the first queries);
+ *   - representatives drawn at random from the buffer (the given rows are
+ *     those draws; the random numbers are the caller's);
+ *   - no beacons at all (bcount 0 everywhere, recent queries only);
+ *   - [IK, 4.4]: the per-key aggregate over the observation rows may be the
+ *     maximum or the mean; [WZ, 信标查询怎么用] takes the maximum.
+ * Same readings as orc_score_unit; the mean is over the present rows.
+ *
+ * Layouts: brows [G][nb][d] storage rows, bcount [G] with 0 <= bcount <= nb
+ * (rows [0, bcount[g]) of head g are its beacons).  agg: ORC_AGG_MAX or
+ * ORC_AGG_MEAN.  Outputs as orc_score_unit.  Returns 0, or -1 for a bcount
+ * outside [0, nb] (that head then has no beacons).
+ */
+int orc_score_given(int dtype, int d, int G, const void *K, int L, const void *recent, const int *recent_pos, int R,
+                    const void *brows, const int *bcount, int nb, long pos_now, double theta, int agg,
+                    double *scores, void *obs, int *obs_valid, double *lse) {
+  int rows = G * (R + nb);
+  size_t es = elem_size(dtype);
+  double *y = (double *)calloc((size_t)(rows > 0 ? rows : 1) * d, sizeof(double));
+  int *valid = (int *)calloc(rows > 0 ? rows : 1, sizeof(int));
+  double *x = (double *)malloc(sizeof(double) * d);
+  double *yr = (double *)malloc(sizeof(double) * d);
+  double *lse_r = (double *)malloc(sizeof(double) * (rows > 0 ? rows : 1));
+  int status = 0;
+  for (int g = 0; g < G; ++g) {
+    for (int r = 0; r < R; ++r) {
+      int row = g * (R + nb) + r;
+      if (recent_pos[r] < 0) continue;
+      rotated_row((const char *)recent + es * (size_t)d * ((size_t)g * R + r), dtype, d, recent_pos[r], theta, x,
+                  yr, y + (size_t)row * d);
+      valid[row] = 1;
+    }
+    int cnt = bcount[g];
+    if (cnt < 0 || cnt > nb) {
+      status = -1;
+      continue;
+    }
+    for (int b = 0; b < cnt; ++b) {
+      int row = g * (R + nb) + R + b;
+      rotated_row((const char *)brows + es * (size_t)d * ((size_t)g * nb + b), dtype, d, pos_now, theta, x, yr,
+                  y + (size_t)row * d);
+      valid[row] = 1;
+    }
+  }
+  score_rows(dtype, d, rows, y, valid, K, L, agg, scores, lse_r);
+  if (obs)
+    for (int r = 0; r < rows; ++r)
+      for (int t = 0; t < d; ++t) orc_store(obs, dtype, (long)r * d + t, y[(size_t)r * d + t]);
+  if (obs_valid)
+    for (int r = 0; r < rows; ++r) obs_valid[r] = valid[r];
+  if (lse)
+    for (int r = 0; r < rows; ++r) lse[r] = lse_r[r];
+  free(y);
+  free(valid);
+  free(x);
+  free(yr);
   free(lse_r);
   return status;
 }
