@@ -217,8 +217,9 @@ __global__ __launch_bounds__(kFullThreads) void fps_full_sum_kernel(const void* 
       const double r = fmax(sqrt(ss), 1e-12);
       if (i < n) {
         if (part == 0) nh[i] = r;
+        const double ir = 1.0 / r;  // one division per row; the sum's order differs from the oracle's anyway
 #pragma unroll
-        for (int k = 0; k < P::EL; ++k) acc[k] += x[k] / r;
+        for (int k = 0; k < P::EL; ++k) acc[k] = fma(x[k], ir, acc[k]);
       }
     }
   }
