@@ -49,10 +49,18 @@ N_EVENTS = 240      # evictions in a 32K-token generation (first at L = 2176)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the HIP sources with comments and blank lines removed, so that
+    recorded counter figures stay tied to the code they were measured on."""
+    import re
+
     h = hashlib.sha256()
     for name in ("fps.hip", "score.hip", "select.hip", "bkv_api.hip", "bkv_device.hpp", "fps_full.hip"):
-        with open(os.path.join(ROOT, "kv_cache_eviction_continual_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "kv_cache_eviction_continual_amd", "csrc", name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

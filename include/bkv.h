@@ -73,6 +73,10 @@ enum bkv_dtype { BKV_F32 = 0, BKV_BF16 = 1 };
 /* Device status bits (bkv_read_device_status). */
 #define BKV_DEV_BAD_LEN 0x1   /* len[n] < 0 or len[n] > max_len */
 #define BKV_DEV_BAD_COUNT 0x2 /* qcount[n][g] < 0 or >= C on entry */
+#define BKV_DEV_BAD_INDEX 0x4 /* bkv_beacon_rows: a row index >= S */
+
+/* Aggregation of the observation rows' probabilities into a key's score. */
+enum bkv_aggregation { BKV_AGG_MAX = 0, BKV_AGG_MEAN = 1 };
 
 /* Supported ranges (checked on the host):
  *   head_dim in {64, 128}; C (buffer capacity) <= 256; G * (R + nb) <= 256;
@@ -188,6 +192,39 @@ int bkv_score_picked(const bkv_shape *shape, const void *K, const int32_t *len, 
                      const int32_t *recent_pos, int32_t R, int32_t nb, const int32_t *pos_now,
                      double rope_theta, float *scores, void *ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/*
+ * Policy variants on the same kernels, for the comparisons the pages make
+ * ([WZ] 效果到底怎么样: InitialRecent keeps the earliest generated queries
+ * with the recent ones, and loses to the FPS beacons; [IK] 4.4: a key's score
+ * aggregates the rows' attention by maximum or mean, and [WZ] 信标查询怎么用
+ * uses the maximum).
+ *
+ * bkv_beacon_rows -- beacons given instead of chosen by FPS: writes regions
+ *   [5] and [6] as bkv_beacon_picks does, for bkv_score_picked(_agg) to use.
+ *     src  [N][Hq][S][d]  rows to take beacons from (read only): e.g. qbuf
+ *                         (S = C) for representatives drawn at random, or
+ *                         a caller-kept copy of each head's first queries
+ *                         for InitialRecent
+ *     idx  [N][Hq][nb]    int32 rows of src, in beacon order; the beacons of
+ *                         a head are its leading entries in [0, S): the first
+ *                         negative entry ends them, as does an entry >= S,
+ *                         which also sets BKV_DEV_BAD_INDEX
+ *   R and nb locate the regions (the workspace of shape, R, nb); 0 <= nb <=
+ *   256, S >= 0.  No beacons at all (recent queries only) is nb = 0, or idx
+ *   all -1.
+ *
+ * bkv_score_picked_agg -- bkv_score_picked with a choice of aggregation:
+ *   BKV_AGG_MAX (bkv_score_picked itself) or BKV_AGG_MEAN, the mean of the
+ *   rows' probabilities over the rows present in the (slot, KV head) (0 if
+ *   none).  Everything else as bkv_score_picked.
+ */
+int bkv_beacon_rows(const bkv_shape *shape, const void *src, int32_t S, const int32_t *idx, int32_t R,
+                    int32_t nb, void *ws, size_t ws_bytes, hipStream_t stream);
+int bkv_score_picked_agg(const bkv_shape *shape, const void *K, const int32_t *len, const void *recent,
+                         const int32_t *recent_pos, int32_t R, int32_t nb, const int32_t *pos_now,
+                         double rope_theta, int32_t aggregation, float *scores, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
  * bkv_select -- kept set ([IK] 三: I = TopK(score, B_KV); [AM]: the recent

@@ -23,6 +23,8 @@ OK = 0
 E_NULL, E_SHAPE, E_DTYPE, E_BUDGET, E_CAPACITY, E_WORKSPACE, E_HIP = range(1, 8)
 DEV_BAD_LEN = 0x1
 DEV_BAD_COUNT = 0x2
+DEV_BAD_INDEX = 0x4
+AGG_MAX, AGG_MEAN = 0, 1
 
 WS_OBS, WS_VALID, WS_LSE, WS_SELECT, WS_ROPE, WS_BEACONS, WS_BEACON_ROWS = range(7)
 WS_HEADER_BYTES = 256
@@ -34,6 +36,8 @@ EXPORTS = (
     "bkv_score",
     "bkv_beacon_picks",
     "bkv_score_picked",
+    "bkv_score_picked_agg",
+    "bkv_beacon_rows",
     "bkv_select",
     "bkv_compact",
     "bkv_select_compact",
@@ -105,6 +109,10 @@ def load() -> ctypes.CDLL:
     L.bkv_compact_fill.restype = ctypes.c_int
     L.bkv_select_compact_fill.argtypes = [SP, P, P, P, P, P, I32, I32, P, P, SZ, P]
     L.bkv_select_compact_fill.restype = ctypes.c_int
+    L.bkv_score_picked_agg.argtypes = [SP, P, P, P, P, I32, I32, P, ctypes.c_double, I32, P, P, SZ, P]
+    L.bkv_score_picked_agg.restype = ctypes.c_int
+    L.bkv_beacon_rows.argtypes = [SP, P, I32, P, I32, I32, P, SZ, P]
+    L.bkv_beacon_rows.restype = ctypes.c_int
     L.bkv_fps_full_workspace_size.argtypes = [SP, I32]
     L.bkv_fps_full_workspace_size.restype = SZ
     L.bkv_fps_full.argtypes = [SP, P, I32, I32, P, P, SZ, P]
@@ -189,6 +197,18 @@ def bkv_score_picked(shape: Shape, K, length, recent, recent_pos, R: int, nb: in
     _check(load().bkv_score_picked(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos), R,
                                    nb, _ptr(pos_now), float(rope_theta), _ptr(scores), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_score_picked_agg(shape: Shape, K, length, recent, recent_pos, R: int, nb: int, pos_now, rope_theta: float,
+                         aggregation: int, scores, ws, stream=None) -> None:
+    _check(load().bkv_score_picked_agg(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos),
+                                       R, nb, _ptr(pos_now), float(rope_theta), int(aggregation), _ptr(scores),
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_beacon_rows(shape: Shape, src, S: int, idx, R: int, nb: int, ws, stream=None) -> None:
+    _check(load().bkv_beacon_rows(ctypes.byref(shape), _ptr(src), S, _ptr(idx), R, nb, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bkv_select(shape: Shape, scores, length, budget: int, window: int, kept, ws, stream=None) -> None:

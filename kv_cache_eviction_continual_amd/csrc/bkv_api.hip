@@ -15,7 +15,9 @@ hipError_t launch_beacon_picks(const void*, const int32_t*, int, int, int, int32
 template <int DT, int D>
 hipError_t launch_score(const void*, const int32_t*, int, int, int, int, const void*, const int32_t*, int,
                         const int32_t*, const void*, int, const int32_t*, double, float2*, void*, int32_t*, int,
-                        float*, float*, int32_t*, hipStream_t);
+                        float*, float*, int32_t*, bool, hipStream_t);
+hipError_t launch_beacon_rows(const void*, int, const int32_t*, int, int, int, int32_t*, void*, int32_t*,
+                              hipStream_t);
 hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
                          hipStream_t);
 hipError_t launch_compact(void*, void*, const int32_t*, const int32_t*, int32_t*, int, int, int, int, int,
@@ -130,7 +132,7 @@ int check_score_args(const bkv_shape* shape, const void* K, const int32_t* len, 
 // The RoPE tables and the score kernel, with the beacon picks already in ws.
 int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
                   const int32_t* recent_pos, int32_t R, int32_t nb, const int32_t* pos_now, double rope_theta,
-                  float* scores, void* ws, const WsLayout& w, hipStream_t stream) {
+                  float* scores, void* ws, const WsLayout& w, bool mean, hipStream_t stream) {
   const int N = shape->n_seq, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
   if (N == 0) return BKV_OK;
   unsigned char* base = (unsigned char*)ws;
@@ -144,7 +146,7 @@ int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, con
   hipError_t e;
 #define BKV_SCORE_CASE(DT, D)                                                                                  \
   e = launch_score<DT, D>(K, len, N, Hkv, Hq, shape->max_len, recent, recent_pos, R, beacons, brows, nb,       \
-                          pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, stream);
+                          pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, mean, stream);
   if (shape->dtype == BKV_BF16) {
     if (shape->head_dim == 128) {
       BKV_SCORE_CASE(BKV_BF16, 128)
@@ -269,7 +271,36 @@ int bkv_score_picked(const bkv_shape* shape, const void* K, const int32_t* len, 
   int st = check_score_args(shape, K, len, recent, recent_pos, R, nullptr, nullptr, false, -1, nb, pos_now,
                             rope_theta, scores, ws, ws_bytes, &w);
   if (st != BKV_OK) return st;
-  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w, stream);
+  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w, false, stream);
+}
+
+int bkv_score_picked_agg(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
+                         const int32_t* recent_pos, int32_t R, int32_t nb, const int32_t* pos_now, double rope_theta,
+                         int32_t aggregation, float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (aggregation != BKV_AGG_MAX && aggregation != BKV_AGG_MEAN) return BKV_E_SHAPE;
+  WsLayout w;
+  int st = check_score_args(shape, K, len, recent, recent_pos, R, nullptr, nullptr, false, -1, nb, pos_now,
+                            rope_theta, scores, ws, ws_bytes, &w);
+  if (st != BKV_OK) return st;
+  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w,
+                       aggregation == BKV_AGG_MEAN, stream);
+}
+
+int bkv_beacon_rows(const bkv_shape* shape, const void* src, int32_t S, const int32_t* idx, int32_t R, int32_t nb,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (nb < 0 || nb > kMaxCapacity) return BKV_E_CAPACITY;
+  if (R < 0 || R > kMaxRecent || S < 0) return BKV_E_SHAPE;
+  WsLayout w;
+  if (!layout(shape, R, nb, &w)) return BKV_E_SHAPE;
+  if ((nb > 0 && !idx) || (S > 0 && nb > 0 && !src)) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, w.total)) != BKV_OK) return st;
+  const int heads = shape->n_seq * shape->n_q_heads;
+  if (heads == 0) return BKV_OK;
+  unsigned char* base = (unsigned char*)ws;
+  return hip_status(launch_beacon_rows(src, S, idx, nb, shape->head_dim * elem_bytes(shape->dtype), heads,
+                                       (int32_t*)(base + w.beacons), base + w.beacon_rows, (int32_t*)ws, stream));
 }
 
 int bkv_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
@@ -282,7 +313,7 @@ int bkv_score(const bkv_shape* shape, const void* K, const int32_t* len, const v
   if (st != BKV_OK) return st;  // nothing enqueued
   st = bkv_beacon_picks(shape, qbuf, qcount, C, R, nb, ws, ws_bytes, stream);
   if (st != BKV_OK) return st;
-  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w, stream);
+  return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w, false, stream);
 }
 
 int bkv_select(const bkv_shape* shape, const float* scores, const int32_t* len, int32_t budget, int32_t window,

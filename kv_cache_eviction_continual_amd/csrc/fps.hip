@@ -731,6 +731,45 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   }
 }
 
+// Beacons given by the caller instead of chosen by FPS (the policy variants
+// the pages compare against: the earliest queries of a head, or rows drawn at
+// random from its buffer).  Head h takes rows idx[h][0, cnt) of its source
+// src[h][S][row], where cnt is the length of the leading run of entries in
+// [0, S); a negative entry ends the list, an entry >= S ends it too and sets
+// BKV_DEV_BAD_INDEX.  Writes the same workspace regions as beacon_pick_kernel.
+__global__ __launch_bounds__(64) void beacon_rows_kernel(const unsigned char* __restrict__ src, int S,
+                                                         const int32_t* __restrict__ idx, int nb, int row_bytes,
+                                                         int32_t* __restrict__ beacons,
+                                                         unsigned char* __restrict__ rows,
+                                                         int32_t* __restrict__ ws_words) {
+  const size_t head = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int32_t* ih = idx + head * nb;
+  int stop = nb;  // first entry outside [0, S)
+  for (int b = lane; b < nb; b += 64)
+    if (ih[b] < 0 || ih[b] >= S) stop = min(stop, b);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) stop = min(stop, __shfl_xor(stop, off, 64));
+  if (lane == 0 && stop < nb && ih[stop] >= S) set_status(ws_words, BKV_DEV_BAD_INDEX);
+  int32_t* out = beacons + head * (nb + 1);
+  for (int b = lane; b < stop; b += 64) out[1 + b] = ih[b];
+  if (lane == 0) out[0] = stop;
+  const int ku = row_bytes / 16;
+  const unsigned char* sh = src + head * (size_t)S * row_bytes;
+  uint4* dst = reinterpret_cast<uint4*>(rows + head * (size_t)nb * row_bytes);
+  for (int u = lane; u < stop * ku; u += 64) {
+    const int b = u / ku, q = u - b * ku;
+    dst[u] = reinterpret_cast<const uint4*>(sh + (size_t)ih[b] * row_bytes)[q];
+  }
+}
+
+hipError_t launch_beacon_rows(const void* src, int S, const int32_t* idx, int nb, int row_bytes, int heads,
+                              int32_t* beacons, void* rows, int32_t* ws_words, hipStream_t st) {
+  hipLaunchKernelGGL(beacon_rows_kernel, dim3(heads), dim3(64), 0, st, (const unsigned char*)src, S, idx, nb,
+                     row_bytes, beacons, (unsigned char*)rows, ws_words);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (tile capacity from the buffer capacity)
 // ---------------------------------------------------------------------------

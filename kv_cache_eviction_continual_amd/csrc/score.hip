@@ -30,7 +30,9 @@
 //           most recently read tiles are still cached.
 // exp(max_r(s_r - lse_r)) = max_r exp(s_r - lse_r), so one exp per key
 // suffices.  Logits are accumulated in fp32 from exact bf16 (or fp32)
-// products.
+// products.  The mean-aggregation variant (the same post, section 4.4: max
+// or mean) sums exp2(s - lse) over the rows in pass 2 instead and divides by
+// the rows present.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -201,7 +203,7 @@ struct ScoreLayout {
 // h G + g (present if its position is >= 0), or for k >= R its beacon k - R
 // (present if below the pick count; read from the picks kernel's row copy);
 // rows from G (R + nb) to RP are padding.
-template <int DT, int D, int NW>
+template <int DT, int D, int NW, bool kMean>
 __global__ __launch_bounds__(64 * NW) void score_kernel(
     const typename Elem<DT>::T* __restrict__ K, const int32_t* __restrict__ len, int Hkv, int Hq, int Lmax,
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
@@ -220,6 +222,7 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
   unsigned char* ktile = smem;                                                    // [kTile][kRowStride]
   float* part = reinterpret_cast<float*>(smem + kTile * Lay::kRowStride);          // [NW][kTile]
   float* lse_lds = part + NW * kTile;                                              // [RP]
+  int* nvalid_lds = reinterpret_cast<int*>(lse_lds + RP);                          // [NW] present rows per wave
   const int nrow_waves = RP / 32;
 
   const size_t unit = blockIdx.x;
@@ -309,6 +312,10 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
     }
     if (lane < 32) obs_valid[unit * RP + myrow] = row_valid ? 1 : 0;
   }
+  if constexpr (kMean) {
+    const uint64_t present = __ballot(has_rows && lane < 32 && row_valid);
+    if (lane == 0) nvalid_lds[wave] = __builtin_popcountll(present);
+  }
   if (L == 0) {
     if (has_rows && lane < 32) lse_out[unit * RP + myrow] = __builtin_huge_valf();
     return;
@@ -367,6 +374,12 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
   float lse_r[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) lse_r[r] = has_rows ? lse_lds[32 * wave + acc_row(r, lane)] : 0.0f;
+  float inv_present = 0.0f;  // mean aggregation: 1 / (rows present in the unit), 0 if none
+  if constexpr (kMean) {
+    int present = 0;
+    for (int w = 0; w < nrow_waves; ++w) present += nvalid_lds[w];
+    inv_present = present > 0 ? 1.0f / (float)present : 0.0f;
+  }
 
   // ---------------- pass 2: per-key max of (s - lse) ----------------
   float* out = scores + unit * (size_t)Lmax;
@@ -384,10 +397,18 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
       floatx16_t acc = {};
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = MF::mma(qf[s], MF::load(krow, s, lane), acc);
-      float t = ninf;
+      float t;
+      if constexpr (kMean) {  // sum of the rows' probabilities (absent rows: lse +inf, probability 0)
+        t = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t = fmaxf(t, acc[r] * scale2 - lse_r[r]);
-      t = fmaxf(t, __shfl_xor(t, 32, 64));
+        for (int r = 0; r < 16; ++r) t += exp2f(acc[r] * scale2 - lse_r[r]);
+        t += __shfl_xor(t, 32, 64);
+      } else {  // maximum of the rows' log2-probabilities
+        t = ninf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t = fmaxf(t, acc[r] * scale2 - lse_r[r]);
+        t = fmaxf(t, __shfl_xor(t, 32, 64));
+      }
       if (lane < 32) part[wave * kTile + sub * kSub + lane] = t;
     }
     __syncthreads();
@@ -395,22 +416,28 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
       const int j = key0 + k;
       if (j < L) {
         float t = part[k];
-        for (int w = 1; w < nrow_waves; ++w) t = fmaxf(t, part[w * kTile + k]);
-        out[j] = exp2f(t);  // exp2(-inf) = 0 when no row is present
+        if constexpr (kMean) {
+          for (int w = 1; w < nrow_waves; ++w) t += part[w * kTile + k];
+          out[j] = t * inv_present;
+        } else {
+          for (int w = 1; w < nrow_waves; ++w) t = fmaxf(t, part[w * kTile + k]);
+          out[j] = exp2f(t);  // exp2(-inf) = 0 when no row is present
+        }
       }
     }
   }
 }
 
-template <int DT, int D, int NW>
+template <int DT, int D, int NW, bool kMean>
 static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax,
                                   const void* recent, const int32_t* recent_pos, int R, const int32_t* beacons,
                                   const void* brows, int nb, const float2* tab, void* obs, int32_t* obs_valid,
                                   int RP, float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
   using Lay = ScoreLayout<DT, D>;
   using ET = typename Elem<DT>::T;
-  const size_t smem = (size_t)kTile * Lay::kRowStride + (size_t)NW * kTile * sizeof(float) + RP * sizeof(float);
-  auto kern = score_kernel<DT, D, NW>;
+  const size_t smem = (size_t)kTile * Lay::kRowStride + (size_t)NW * kTile * sizeof(float) + RP * sizeof(float) +
+                      NW * sizeof(int);
+  auto kern = score_kernel<DT, D, NW, kMean>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(N * Hkv), dim3(64 * NW), smem, st, (const ET*)K, len, Hkv, Hq, Lmax,
@@ -425,14 +452,16 @@ template <int DT, int D>
 hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax, const void* recent,
                         const int32_t* recent_pos, int R, const int32_t* beacons, const void* brows, int nb,
                         const int32_t* pos_now, double theta, float2* tab, void* obs, int32_t* obs_valid, int RP,
-                        float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
+                        float* scores, float* lse, int32_t* ws_words, bool mean, hipStream_t st) {
   hipLaunchKernelGGL(rope_table_kernel<D>, dim3(N), dim3(256), 0, st, recent_pos, pos_now, R, theta, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int tiles = RP / 32;
-#define BKV_SCORE_NW(NW)                                                                                      \
-  return launch_score_nw<DT, D, NW>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, beacons, brows, nb, tab,  \
-                                    obs, obs_valid, RP, scores, lse, ws_words, st)
+#define BKV_SCORE_NW(NW)                                                                                       \
+  return mean ? launch_score_nw<DT, D, NW, true>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, beacons, brows, \
+                                                 nb, tab, obs, obs_valid, RP, scores, lse, ws_words, st)         \
+              : launch_score_nw<DT, D, NW, false>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, beacons,      \
+                                                  brows, nb, tab, obs, obs_valid, RP, scores, lse, ws_words, st)
   if (tiles <= 2) BKV_SCORE_NW(2);
   if (tiles <= 4) BKV_SCORE_NW(4);
   BKV_SCORE_NW(8);
@@ -443,7 +472,7 @@ hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int H
   template hipError_t launch_score<DT, D>(const void*, const int32_t*, int, int, int, int, const void*,       \
                                           const int32_t*, int, const int32_t*, const void*, int,              \
                                           const int32_t*, double, float2*, void*, int32_t*, int, float*,      \
-                                          float*, int32_t*, hipStream_t);
+                                          float*, int32_t*, bool, hipStream_t);
 BKV_INST_SCORE(BKV_F32, 64)
 BKV_INST_SCORE(BKV_F32, 128)
 BKV_INST_SCORE(BKV_BF16, 64)

@@ -181,3 +181,24 @@ def test_fps_full_validation_and_workspace_size(lib):
     # nothing to do
     assert f(ctypes.byref(shape(n_seq=0)), fake, n, 32, fake, fake, big, P) == bkv.OK
     assert f(ctypes.byref(s), fake, n, 0, fake, fake, big, P) == bkv.OK
+
+
+def test_policy_entry_points_validation(lib):
+    s = shape()
+    fake, big, P = 256, 1 << 40, None
+    br = lib.bkv_beacon_rows
+    assert br(ctypes.byref(s), fake, 128, fake, 16, 300, fake, big, P) == bkv.E_CAPACITY
+    assert br(ctypes.byref(s), fake, 128, fake, 70, 16, fake, big, P) == bkv.E_SHAPE
+    assert br(ctypes.byref(s), fake, -1, fake, 16, 16, fake, big, P) == bkv.E_SHAPE
+    assert br(ctypes.byref(s), fake, 128, None, 16, 16, fake, big, P) == bkv.E_NULL
+    assert br(ctypes.byref(s), None, 128, fake, 16, 16, fake, big, P) == bkv.E_NULL
+    assert br(ctypes.byref(s), fake, 128, fake, 16, 16, fake, 1024, P) == bkv.E_WORKSPACE
+    assert br(ctypes.byref(shape(n_seq=0)), fake, 128, fake, 16, 16, fake, big, P) == bkv.OK
+    sa = lib.bkv_score_picked_agg
+    ok = [ctypes.byref(s), fake, fake, fake, fake, 16, 16, fake, 1e6, bkv.AGG_MEAN, fake, fake, big, P]
+    a = list(ok); a[9] = 2
+    assert sa(*a) == bkv.E_SHAPE  # unknown aggregation
+    a = list(ok); a[1] = None
+    assert sa(*a) == bkv.E_NULL
+    a = list(ok); a[12] = 1024
+    assert sa(*a) == bkv.E_WORKSPACE
