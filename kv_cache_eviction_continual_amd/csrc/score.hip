@@ -337,21 +337,37 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = MF::mma(MF::load(krow, s, lane), qf[s], acc);
       // acc[r]: key sub*32 + acc_row(r, lane), row = lane % 32
-      float v[16];
-      float mx = ninf;
+      if (key0 + sub * kSub + kSub <= L) {
+        // every key present: the scale is positive, so the maximum of the
+        // raw logits scales to the maximum of the scaled ones; one fma and
+        // one hardware exp2 per key (a term below 2^-126 of the running
+        // maximum is flushed to 0, which the sum of at least 1 cannot see)
+        float mx = acc[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = key0 + sub * kSub + acc_row(r, lane);
-        v[r] = (j < L) ? acc[r] * scale2 : ninf;
-        mx = fmaxf(mx, v[r]);
-      }
-      const float m_new = fmaxf(run_m, mx);
-      if (m_new != ninf) {
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        const float m_new = fmaxf(run_m, mx * scale2);
         float sum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum += exp2f(v[r] - m_new);
-        run_s = run_s * exp2f(run_m - m_new) + sum;
+        for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -m_new));
+        run_s = run_s * __builtin_amdgcn_exp2f(run_m - m_new) + sum;
         run_m = m_new;
+      } else {
+        float v[16];
+        float mx = ninf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = key0 + sub * kSub + acc_row(r, lane);
+          v[r] = (j < L) ? acc[r] * scale2 : ninf;
+          mx = fmaxf(mx, v[r]);
+        }
+        const float m_new = fmaxf(run_m, mx);
+        if (m_new != ninf) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum += exp2f(v[r] - m_new);
+          run_s = run_s * exp2f(run_m - m_new) + sum;
+          run_m = m_new;
+        }
       }
     }
   }
@@ -401,12 +417,12 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
       if constexpr (kMean) {  // sum of the rows' probabilities (absent rows: lse +inf, probability 0)
         t = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t += exp2f(acc[r] * scale2 - lse_r[r]);
+        for (int r = 0; r < 16; ++r) t += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -lse_r[r]));
         t += __shfl_xor(t, 32, 64);
       } else {  // maximum of the rows' log2-probabilities
         t = ninf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) t = fmaxf(t, acc[r] * scale2 - lse_r[r]);
+        for (int r = 0; r < 16; ++r) t = fmaxf(t, fmaf(acc[r], scale2, -lse_r[r]));
         t = fmaxf(t, __shfl_xor(t, 32, 64));
       }
       if (lane < 32) part[wave * kTile + sub * kSub + lane] = t;
