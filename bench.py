@@ -613,7 +613,9 @@ def fps_compare(reps: int = 3):
     print(json.dumps(result), flush=True)
 
 
-def load_traffic(src_hash):
+def load_traffic(src_hash, workload):
+    """The recorded counter figures, if they were taken on this workload with
+    these kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -621,7 +623,7 @@ def load_traffic(src_hash):
         t = json.load(open(path))
     except Exception:
         return None
-    if t.get("kernel_source_hash") != src_hash:
+    if t.get("kernel_source_hash") != src_hash or t.get("workload") != workload:
         return None
     return t
 
@@ -722,7 +724,7 @@ def main():
     dom_bytes = compact_bytes if dominant == "compact" else score_bytes
     achieved = dom_bytes / (stage_ms[dominant] * 1e6)
     src_hash = kernel_source_hash()
-    traffic = load_traffic(src_hash)
+    traffic = load_traffic(src_hash, w.name)
     dom_traffic = None
     if traffic and dominant in traffic.get("kernels", {}):
         dom_traffic = traffic["kernels"][dominant].get("hbm_bytes_per_launch")
