@@ -15,6 +15,9 @@
 // all rows; then repeatedly add the row with the lowest maximum cosine to the
 // picked set; ties go to the lower row.
 //
+// Capacities above 128 rows use a second, cooperative routine (fps_coop):
+// one workgroup of eight waves per head, described where it is defined.
+//
 // One wavefront per query head, no block barriers.  The head's rows stay in
 // global memory (they are read once into matrix-core fragments, and again
 // only for binary64 decisions and the write-back); LDS holds the packed
@@ -212,13 +215,13 @@ __device__ inline uint32_t wave_min_key(uint32_t a) {
 
 // binary64 a.b, a.a and b.b of two rows; each row's loads go out together
 // (up to 8 units of 16 bytes at a time) before the arithmetic
-template <int DT, int D>
+template <int DT, int D, int kBatch = 8>
 __device__ inline void fps_dots64(const typename Elem<DT>::T* a, const typename Elem<DT>::T* b, double& ab,
                                   double& aa, double& bb) {
   using E = Elem<DT>;
   constexpr int kPer16 = 16 / E::kBytes;
   constexpr int kU = D / kPer16;
-  constexpr int kC = kU < 8 ? kU : 8;
+  constexpr int kC = kU < kBatch ? kU : kBatch;
   const uint4* xa = reinterpret_cast<const uint4*>(a);
   const uint4* xb = reinterpret_cast<const uint4*>(b);
   ab = aa = bb = 0.0;
@@ -252,9 +255,10 @@ __device__ inline void fps_dots64(const typename Elem<DT>::T* a, const typename 
 // cosine to all c rows (sum_mode) or the maximum cosine to picks[0, npicked),
 // cosines as a.b / (max(|a|, 1e-12) max(|b|, 1e-12)).  The lanes split the
 // partner rows; the result is wave-uniform.
-template <int DT, int D, int SL>
-__device__ __attribute__((always_inline)) int fps_exact_argmin(const FpsRows<DT, D>& src, const FpsLds& s, const uint64_t* inmask, int c,
-                                int npicked, bool sum_mode) {
+template <int DT, int D, int SL, class LdsT, int kBatch = 8>
+__device__ __attribute__((always_inline)) int fps_exact_argmin(const FpsRows<DT, D>& src, const LdsT& s,
+                                                               const uint64_t* inmask, int c, int npicked,
+                                                               bool sum_mode) {
   const int lane = fps_lane();
   const int npart = sum_mode ? c : npicked;
   const double inf = __builtin_huge_val();
@@ -272,7 +276,7 @@ __device__ __attribute__((always_inline)) int fps_exact_argmin(const FpsRows<DT,
       for (int q = lane; q < npart; q += 64) {
         const int b = sum_mode ? q : s.picks[q];
         double ab, aa, bb;
-        fps_dots64<DT, D>(xa, src.row(b), ab, aa, bb);
+        fps_dots64<DT, D, kBatch>(xa, src.row(b), ab, aa, bb);
         const double na = sqrt(aa), nb = sqrt(bb);
         const double v = ab * (1.0 / (na < 1e-12 ? 1e-12 : na)) * (1.0 / (nb < 1e-12 ? 1e-12 : nb));
         acc = sum_mode ? acc + v : fmax(acc, v);
@@ -576,6 +580,327 @@ __device__ __attribute__((always_inline)) int fps_dispatch(const FpsRows<DT, D>&
   return 0;
 }
 
+
+// ---------------------------------------------------------------------------
+// FPS of one head by NT cooperating waves
+// ---------------------------------------------------------------------------
+//
+// Wave w owns the 32 rows of tile w as candidates.  Lane (n, h) holds half of
+// row 32 w + n in matrix-core fragments (h = lane / 32), and, after the Gram
+// step, the column G(., 32 w + n) for the rows i with (i % 8) / 4 == h:
+// gc[16 t + r] = G(32 t + 8 (r / 4) + 4 h + r % 4, 32 w + n), the layout of
+// the MFMA accumulator of tile pair (t, w).  A greedy round reads its pick's
+// entry by a uniform register index (and the partner half by a lane swap),
+// so no Gram matrix is kept in LDS.  Each round the waves publish
+// their smallest and second-smallest candidate key in LDS; after one
+// barrier every wave knows the best key k1 and the runner-up k2.  If k2's
+// bucket starts above key_hi(k1) + window, k1's row is the binary64 argmin;
+// otherwise the candidates within the window are decided in binary64 by
+// wave 0 (a superset of the single-wave test, so never fewer binary64
+// decisions).
+
+struct FpsCoopLds {
+  unsigned char* stage;  // [M][D] storage: picks staged for the buffer write-back
+  float* inv32;          // [cap] fp32 1 / |x| (0 for rows past the count)
+  int* map;              // [cap]
+  int* picks;            // [cap]
+  int* pos;              // [cap]
+  uint32_t* pub;         // [2][NT][2]: smallest and second-smallest key per wave, by round parity
+  uint32_t* mask;        // [NT]: window members of each wave's tile (bit n = row 32 w + n)
+  int* flags;            // [NT]: per-wave unsafe-norm flag
+  int* slot;             // [1]: pick of a binary64 decision
+};
+
+template <int DT, int D>
+__host__ __device__ constexpr size_t fps_coop_stage_bytes(int M) {
+  return ((size_t)M * D * Elem<DT>::kBytes + 15) & ~(size_t)15;
+}
+
+template <int DT, int D>
+__host__ __device__ constexpr size_t fps_coop_lds_bytes(int NT, int M) {
+  return fps_coop_stage_bytes<DT, D>(M) + (size_t)32 * NT * 16 + (size_t)NT * (16 + 4 + 4) + 16;
+}
+
+template <int DT, int D>
+__device__ inline FpsCoopLds fps_coop_carve(unsigned char* smem, int NT, int M) {
+  const int cap = 32 * NT;
+  FpsCoopLds s;
+  s.stage = smem;
+  unsigned char* p = smem + fps_coop_stage_bytes<DT, D>(M);
+  s.inv32 = reinterpret_cast<float*>(p);
+  s.map = reinterpret_cast<int*>(p + (size_t)cap * 4);
+  s.picks = reinterpret_cast<int*>(p + (size_t)cap * 8);
+  s.pos = reinterpret_cast<int*>(p + (size_t)cap * 12);
+  s.pub = reinterpret_cast<uint32_t*>(p + (size_t)cap * 16);
+  s.mask = s.pub + 4 * NT;
+  s.flags = reinterpret_cast<int*>(s.mask + NT);
+  s.slot = s.flags + NT;
+  return s;
+}
+
+// Lowest value of a key's bucket.
+__device__ inline float key_lo(uint32_t k) {
+  const uint32_t ord = k & 0xFFFFFF00u;
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+
+// One FPS decision of the block (see above).  `key` and `val` are this
+// lane's candidate key (0xFFFFFFFF if none) and its fp32 objective; both
+// lanes of a row hold the same.  Every thread must call it; the result is
+// uniform.
+template <int DT, int D, int NT>
+__device__ __attribute__((always_inline)) int coop_decide(uint32_t key, float val, float win, int parity,
+                                                          const FpsRows<DT, D>& src, const FpsCoopLds& s, int c,
+                                                          int npicked, bool sum_mode) {
+  constexpr int SL = (NT + 1) / 2;
+  const int lane = fps_lane();
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const uint32_t k1w = wave_min_key(key);
+  const uint32_t k2w = wave_min_key(key == k1w ? 0xFFFFFFFFu : key);
+  uint32_t* pub = s.pub + 2 * NT * parity;
+  if (lane == 0) {
+    pub[2 * wv] = k1w;
+    pub[2 * wv + 1] = k2w;
+  }
+  __syncthreads();
+  uint32_t k1 = 0xFFFFFFFFu, k2 = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NT; ++w) {
+    const uint32_t a = pub[2 * w], b = pub[2 * w + 1];
+    if (a < k1) {
+      k2 = min(k1, b);
+      k1 = a;
+    } else {
+      k2 = min(k2, a);
+    }
+  }
+  k1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)k1);
+  k2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)k2);
+  const float hi1 = key_hi(k1) + win;
+  if (k2 == 0xFFFFFFFFu || key_lo(k2) > hi1) return (int)(k1 & 0xFFu);
+  // binary64 decision over the candidates within the window
+  const uint64_t m = __ballot((lane >> 5) == 0 && key != 0xFFFFFFFFu && val <= hi1);
+  if (lane == 0) s.mask[wv] = (uint32_t)m;
+  __syncthreads();
+  if (wv == 0) {
+    uint64_t inmask[SL];
+#pragma unroll
+    for (int q = 0; q < SL; ++q)
+      inmask[q] = (uint64_t)s.mask[2 * q] | ((2 * q + 1 < NT) ? ((uint64_t)s.mask[2 * q + 1] << 32) : 0ull);
+    // rare path: small load batches keep its registers below the rounds' own
+    const int p = fps_exact_argmin<DT, D, SL, FpsCoopLds, 2>(src, s, inmask, c, npicked, sum_mode);
+    if (lane == 0) *s.slot = p;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*s.slot);
+}
+
+// Rows of the picks written to wb + i d (pick i) from the fragments of their
+// owner waves; no-op when wb is null.  Every thread of the block must call it.
+template <int DT, int D, int NT>
+__device__ __forceinline__ void coop_write_picks(const FpsCoopLds& s, int kk,
+                                                 const typename FpsFrag<DT, D>::V (&fr)[FpsFrag<DT, D>::kSteps],
+                                                 typename Elem<DT>::T* wb, int j, int h, bool inrow) {
+  using FR = FpsFrag<DT, D>;
+  if (wb == nullptr) return;
+  for (int r = threadIdx.x; r < 32 * NT; r += 64 * NT) s.pos[r] = -1;
+  __syncthreads();
+  for (int i = threadIdx.x; i < kk; i += 64 * NT) s.pos[s.picks[i]] = i;
+  __syncthreads();
+  const int i = s.pos[j];
+  if (inrow && i >= 0) {
+#pragma unroll
+    for (int ks = 0; ks < FR::kSteps; ++ks) FR::store(wb + (size_t)i * D, ks, h, fr[ks]);
+  }
+}
+
+// Writes the FPS picks of rows [0, c) (c <= 32 NT) to s.picks, min(k, c) of
+// them, and returns the count.  When `wb` is given, also writes pick i's row
+// to wb + i d from the owner waves' fragments.  Every thread of the block
+// (64 NT) must call it.
+template <int DT, int D, int NT>
+__device__ __attribute__((always_inline)) int fps_coop(const FpsRows<DT, D>& src, const FpsCoopLds& s, int c, int k,
+                                                       typename Elem<DT>::T* wb = nullptr) {
+  using FR = FpsFrag<DT, D>;
+  using V = typename FR::V;
+  using T = typename Elem<DT>::T;
+  constexpr int KS = FR::kSteps;
+  constexpr int SL = (NT + 1) / 2;
+  constexpr float kEps = 4.0f * (D + 8) * kFpsU;
+  const int kk = k < c ? k : c;
+  if (kk <= 0) return 0;
+  int lane = fps_lane();
+  __asm__ volatile("" : "+v"(lane));
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n = lane & 31, h = lane >> 5;
+  const int j = 32 * wv + n;  // this lane's candidate row
+  const bool inrow = j < c;
+  const float finf = __builtin_huge_valf();
+
+  // 1. fragments of this wave's rows (rows past the count read row c - 1 and are zeroed)
+  V fr[KS];
+  {
+    const T* rp = src.row(min(j, c - 1));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const V v = FR::load(rp, ks, h);
+      fr[ks] = inrow ? v : FR::zero();
+    }
+  }
+
+  // 2. fp32 inverse norm of row j (both lanes of the row hold it)
+  float inv = 0.0f;
+  int unsafe = 0;
+  {
+    float ss = 0.0f;
+    uint32_t nz = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ss = FR::sumsq(fr[ks], ss);
+      nz |= FR::nonzero(fr[ks]);
+    }
+    ss += __shfl_xor(ss, 32, 64);
+    nz |= (uint32_t)__shfl_xor((int)nz, 32, 64);
+    if (inrow) {
+      if (ss > 0.0f) {
+        if (!(ss >= 1e-30f && ss <= 1e36f)) unsafe = 1;
+        inv = (float)(1.0 / sqrt((double)ss));
+      } else {
+        if (nz) unsafe = 1;  // nonzero row whose fp32 squares underflow
+        inv = 1e12f;         // zero row: norm clamped at 1e-12, every cosine 0
+      }
+    }
+    if (h == 0) s.inv32[j] = inv;
+    const bool wunsafe = __ballot(unsafe) != 0;
+    if (lane == 0) s.flags[wv] = wunsafe ? 1 : 0;
+  }
+  __syncthreads();
+  int any_unsafe = 0;
+#pragma unroll
+  for (int w = 0; w < NT; ++w) any_unsafe |= s.flags[w];
+
+  if (any_unsafe) {  // binary64 rounds over every candidate, by wave 0
+    if (wv == 0) {
+      uint64_t avail[SL];
+#pragma unroll
+      for (int q = 0; q < SL; ++q) {
+        const int cnt = c - 64 * q;
+        avail[q] = cnt >= 64 ? ~0ull : (cnt > 0 ? ((1ull << cnt) - 1) : 0ull);
+      }
+      for (int t = 0; t < kk; ++t) {
+        const int pick = fps_exact_argmin<DT, D, SL, FpsCoopLds, 2>(src, s, avail, c, t, t == 0);
+#pragma unroll
+        for (int q = 0; q < SL; ++q)
+          if ((pick >> 6) == q) avail[q] &= ~(1ull << (pick & 63));
+        if (lane == 0) s.picks[t] = pick;
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();
+    coop_write_picks<DT, D, NT>(s, kk, fr, wb, j, h, inrow);
+    return kk;
+  }
+
+  // 3. Gram columns of this wave's candidates, one 32-row tile at a time
+  // (straight-line MFMA chains); one 16-float vector per tile, so that a
+  // uniform element index stays a register move
+  fps_floatx16 gc[NT];
+#pragma unroll
+  for (int tr = 0; tr < NT; ++tr) {
+    const int ri = 32 * tr + n;
+    const T* rp = src.row(min(ri, c - 1));
+    V a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const V v = FR::load(rp, ks, h);
+      a[ks] = ri < c ? v : FR::zero();
+    }
+    fps_floatx16 acc = fps_floatx16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = FR::mma(a[ks], fr[ks], acc);
+    gc[tr] = acc;
+    // one tile's rows in registers at a time (other waves hide the latency)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 4. start: lowest mean cosine, from this column's sum of G_ij / |x_i|
+  int pick;
+  {
+    float cs = 0.0f;
+#pragma unroll
+    for (int tr = 0; tr < NT; ++tr) {
+      const float4* ivp = reinterpret_cast<const float4*>(s.inv32 + 32 * tr + 4 * h);
+      const float4 iv[4] = {ivp[0], ivp[2], ivp[4], ivp[6]};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float4 q = iv[r >> 2];
+        const float w = (r & 3) == 0 ? q.x : (r & 3) == 1 ? q.y : (r & 3) == 2 ? q.z : q.w;
+        cs = fmaf(gc[tr][r], w, cs);
+      }
+    }
+    cs += __shfl_xor(cs, 32, 64);
+    const float mu = inrow ? (cs * inv) / (float)c : finf;
+    const float eps_mu = kEps + 4.0f * (float)(c + 8) * kFpsU;
+    pick = coop_decide<DT, D, NT>(inrow ? cand_key(mu, j) : 0xFFFFFFFFu, mu, 2.0f * eps_mu, 0, src, s, c, 0, true);
+  }
+  if (threadIdx.x == 0) s.picks[0] = pick;
+
+  // 5. greedy rounds on fp32 cosines
+  const float eps2 = 2.0f * kEps;
+  float mt = -finf;
+  bool picked = j == pick;
+  for (int t = 1; t < kk; ++t) {
+    const int p = pick;
+    const float inv_p = s.inv32[p];
+    const int pr = 4 * ((p & 31) >> 3) + (p & 3);  // uniform element index within tile p / 32
+    float vo = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const float x = gc[q][pr];
+      vo = (q == (p >> 5)) ? x : vo;
+    }
+    const float vp = __shfl_xor(vo, 32, 64);
+    const float g = (h == ((p >> 2) & 1)) ? vo : vp;
+    mt = fmaxf(mt, (g * inv) * inv_p);
+    const bool live = inrow && !picked;
+    pick = coop_decide<DT, D, NT>(live ? cand_key(mt, j) : 0xFFFFFFFFu, mt, eps2, t & 1, src, s, c, t, false);
+    picked = picked || (j == pick);
+    if (threadIdx.x == 0) s.picks[t] = pick;
+  }
+  __syncthreads();
+  coop_write_picks<DT, D, NT>(s, kk, fr, wb, j, h, inrow);
+  return kk;
+}
+
+
+// Copies n 16-byte units, unit u from src_at(u) to dst_at(u, v), over the
+// block's NTH threads with eight loads per thread in flight (clamped in
+// bounds) ahead of their stores.
+template <int NTH, typename SrcF, typename DstF>
+__device__ inline void copy_units_n(int n, SrcF src_at, DstF dst_at) {
+  const int l = threadIdx.x;
+  for (int u0 = 0; u0 < n; u0 += 8 * NTH) {
+    const int m = n - 1;
+    const uint4 v0 = src_at(min(u0 + l, m));
+    const uint4 v1 = src_at(min(u0 + NTH + l, m));
+    const uint4 v2 = src_at(min(u0 + 2 * NTH + l, m));
+    const uint4 v3 = src_at(min(u0 + 3 * NTH + l, m));
+    const uint4 v4 = src_at(min(u0 + 4 * NTH + l, m));
+    const uint4 v5 = src_at(min(u0 + 5 * NTH + l, m));
+    const uint4 v6 = src_at(min(u0 + 6 * NTH + l, m));
+    const uint4 v7 = src_at(min(u0 + 7 * NTH + l, m));
+    if (u0 + l < n) dst_at(u0 + l, v0);
+    if (u0 + NTH + l < n) dst_at(u0 + NTH + l, v1);
+    if (u0 + 2 * NTH + l < n) dst_at(u0 + 2 * NTH + l, v2);
+    if (u0 + 3 * NTH + l < n) dst_at(u0 + 3 * NTH + l, v3);
+    if (u0 + 4 * NTH + l < n) dst_at(u0 + 4 * NTH + l, v4);
+    if (u0 + 5 * NTH + l < n) dst_at(u0 + 5 * NTH + l, v5);
+    if (u0 + 6 * NTH + l < n) dst_at(u0 + 6 * NTH + l, v6);
+    if (u0 + 7 * NTH + l < n) dst_at(u0 + 7 * NTH + l, v7);
+  }
+}
+
+
 // Copies n 16-byte units, unit u from src_at(u) to dst_at(u, v), with eight
 // loads per lane in flight (clamped in bounds) ahead of their stores.
 template <typename SrcF, typename DstF>
@@ -731,6 +1056,112 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   }
 }
 
+// One workgroup of NT waves per query head (NT = 32-row tiles of C).
+template <int DT, int D, int NT>
+__global__ __launch_bounds__(64 * NT) void fps_update_coop_kernel(const typename Elem<DT>::T* __restrict__ q_new, int T,
+                                                             typename Elem<DT>::T* __restrict__ qbuf,
+                                                             int32_t* __restrict__ qcount, int C, int M,
+                                                             int32_t* __restrict__ ws_words) {
+  constexpr int NTH = 64 * NT;
+  constexpr int kRowBytes = D * Elem<DT>::kBytes;
+  constexpr int kU = kRowBytes / 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  using ET = typename Elem<DT>::T;
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x;
+  ET* buf = qbuf + (size_t)head * C * D;
+  const ET* qn = q_new + (size_t)head * T * D;
+  const int c0 = qcount[head];
+  if (c0 < 0 || c0 >= C) {
+    if (tid == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
+    return;
+  }
+  if (c0 + T < C) {  // no shrink in this call: plain append
+    copy16(buf + (size_t)c0 * D, qn, T * kRowBytes, tid, NTH);
+    if (tid == 0) qcount[head] = c0 + T;
+    return;
+  }
+  FpsCoopLds s = fps_coop_carve<DT, D>(smem, NT, M);
+  const FpsRows<DT, D> src{buf, qn, s.map, C};
+  for (int r = tid; r < c0; r += NTH) s.map[r] = r;
+  int c = c0, t = 0, nlast = 0;
+  while (t < T) {
+    const int take = (T - t) < (C - c) ? (T - t) : (C - c);
+    for (int u = tid; u < take; u += NTH) s.map[c + u] = C + t + u;
+    c += take;
+    t += take;
+    __syncthreads();
+    if (c == C) {
+      // the buffer becomes its picks through the row map
+      const int np = fps_coop<DT, D, NT>(src, s, C, M);
+      const int nm = tid < np ? s.map[s.picks[tid]] : 0;  // np <= M < C <= NTH / 2
+      __syncthreads();
+      if (tid < np) s.map[tid] = nm;
+      __syncthreads();
+      c = np;
+      nlast = np;
+    }
+  }
+  uint4* bufu = reinterpret_cast<uint4*>(buf);
+  {
+    // the retained picks may be rows of the entry buffer, so they are staged
+    // in LDS before any row of the buffer is overwritten
+    uint4* stage = reinterpret_cast<uint4*>(s.stage);
+    copy_units_n<NTH>(nlast * kU, [&](int u) { return reinterpret_cast<const uint4*>(src.row(u / kU))[u % kU]; },
+                    [&](int u, uint4 v) { stage[u] = v; });
+    __syncthreads();
+    copy_units_n<NTH>(nlast * kU, [&](int u) { return stage[u]; }, [&](int u, uint4 v) { bufu[u] = v; });
+  }
+  // the rows after the picks are the last arrivals of the call, contiguous in q_new
+  if (c > nlast) {
+    const uint4* tail = reinterpret_cast<const uint4*>(src.row(nlast));
+    uint4* dst = bufu + (size_t)nlast * kU;
+    copy_units_n<NTH>((c - nlast) * kU, [&](int u) { return tail[u]; }, [&](int u, uint4 v) { dst[u] = v; });
+  }
+  if (tid == 0) qcount[head] = c;
+}
+
+// One workgroup of NT waves per query head (capacities above 128 rows).  Writes beacons[head][0] = the pick count
+// min(nb, count), beacons[head][1 + b] = buffer row of pick b, in pick
+// order, and a copy of the picked rows to rows[head][b] (so that scoring
+// does not read the buffer, which the next ingest may already be changing).
+// The score kernel rotates them.
+template <int DT, int D, int NT>
+__global__ __launch_bounds__(64 * NT) void beacon_pick_coop_kernel(const typename Elem<DT>::T* __restrict__ qbuf,
+                                                              const int32_t* __restrict__ qcount, int C, int nb,
+                                                              int32_t* __restrict__ beacons,
+                                                              typename Elem<DT>::T* __restrict__ rows,
+                                                              int32_t* __restrict__ ws_words) {
+  constexpr int NTH = 64 * NT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x;
+  int c = qcount[head];
+  if (c < 0 || c >= C) {
+    if (tid == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
+    c = 0;
+  }
+  const int want = nb < c ? nb : c;
+  FpsCoopLds s = fps_coop_carve<DT, D>(smem, NT, 0);
+  const FpsRows<DT, D> src{qbuf + (size_t)head * C * D, nullptr, s.map, C};
+  int kk = 0;
+  if (want > 0) {
+    for (int r = tid; r < c; r += NTH) s.map[r] = r;
+    __syncthreads();
+    kk = fps_coop<DT, D, NT>(src, s, c, want);
+  }
+  int32_t* out = beacons + (size_t)head * (nb + 1);
+  for (int b = tid; b < kk; b += NTH) out[1 + b] = s.picks[b];
+  if (tid == 0) out[0] = kk;
+  // the picked rows, 16 bytes per thread and load
+  constexpr int kU = D * Elem<DT>::kBytes / 16;
+  uint4* dst = reinterpret_cast<uint4*>(rows + (size_t)head * nb * D);
+  for (int u = tid; u < kk * kU; u += NTH) {
+    const int b = u / kU, q = u - b * kU;
+    dst[u] = reinterpret_cast<const uint4*>(src.row(s.picks[b]))[q];
+  }
+}
+
 // Beacons given by the caller instead of chosen by FPS (the policy variants
 // the pages compare against: the earliest queries of a head, or rows drawn at
 // random from its buffer).  Head h takes rows idx[h][0, cnt) of its source
@@ -787,8 +1218,24 @@ static hipError_t launch_fps_update_nt(const void* q_new, int T, void* qbuf, int
   return hipGetLastError();
 }
 
-// one instantiation per 32-row tile count of the capacity (5 .. 8 tiles share
-// the 8-tile kernel)
+// Capacities above 128 rows: one workgroup of eight waves per head (the
+// single-wave kernel's 130 KB Gram triangle would leave one wave per CU).
+template <int DT, int D>
+static hipError_t launch_fps_update_coop(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M,
+                                         int heads, int32_t* ws_words, hipStream_t st) {
+  using ET = typename Elem<DT>::T;
+  constexpr int NT = 8;
+  const size_t smem = fps_coop_lds_bytes<DT, D>(NT, M);
+  auto kern = fps_update_coop_kernel<DT, D, NT>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(heads), dim3(64 * NT), smem, st, (const ET*)q_new, T, (ET*)qbuf, qcount, C, M,
+                     ws_words);
+  return hipGetLastError();
+}
+
+// one instantiation per 32-row tile count of the capacity up to 4 tiles; the
+// cooperative kernel above that
 template <int DT, int D>
 hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcount, int C, int M, int heads,
                              int32_t* ws_words, hipStream_t st) {
@@ -797,7 +1244,7 @@ hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcou
     case 2: return launch_fps_update_nt<DT, D, 2>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
     case 3: return launch_fps_update_nt<DT, D, 3>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
     case 4: return launch_fps_update_nt<DT, D, 4>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
-    default: return launch_fps_update_nt<DT, D, 8>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
+    default: return launch_fps_update_coop<DT, D>(q_new, T, qbuf, qcount, C, M, heads, ws_words, st);
   }
 }
 
@@ -815,11 +1262,25 @@ static hipError_t launch_picks_nt(const void* qbuf, const int32_t* qcount, int C
 }
 
 template <int DT, int D>
+static hipError_t launch_picks_coop(const void* qbuf, const int32_t* qcount, int C, int nb, int heads,
+                                    int32_t* beacons, void* rows, int32_t* ws_words, hipStream_t st) {
+  using ET = typename Elem<DT>::T;
+  constexpr int NT = 8;
+  const size_t smem = fps_coop_lds_bytes<DT, D>(NT, 0);
+  auto kern = beacon_pick_coop_kernel<DT, D, NT>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(heads), dim3(64 * NT), smem, st, (const ET*)qbuf, qcount, C, nb, beacons,
+                     (ET*)rows, ws_words);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
 hipError_t launch_beacon_picks(const void* qbuf, const int32_t* qcount, int C, int nb, int heads, int32_t* beacons,
                                void* rows, int32_t* ws_words, hipStream_t st) {
   if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
   if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
-  return launch_picks_nt<DT, D, 8>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  return launch_picks_coop<DT, D>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
 }
 
 template hipError_t launch_fps_update<BKV_F32, 64>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
