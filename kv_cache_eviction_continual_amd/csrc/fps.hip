@@ -566,7 +566,8 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
   return kk;
 }
 
-// FPS over rows [0, c) with the tile count of c (1 .. 4 tiles of 32, else 8).
+// FPS over rows [0, c) with the tile count of c (1 .. 4 tiles of 32; larger
+// capacities take the cooperative routine below).
 template <int DT, int D, int NTMAX>
 __device__ __attribute__((always_inline)) int fps_dispatch(const FpsRows<DT, D>& src, const FpsLds& s, int c, int k) {
   const int nt = (c + 31) >> 5;
@@ -576,7 +577,7 @@ __device__ __attribute__((always_inline)) int fps_dispatch(const FpsRows<DT, D>&
     if (nt == 3) return fps_wave<DT, D, 3>(src, s, c, k);
     if (nt == 4) return fps_wave<DT, D, 4>(src, s, c, k);
   }
-  if constexpr (NTMAX >= 8) return fps_wave<DT, D, 8>(src, s, c, k);  // 5 .. 8 tiles
+  static_assert(NTMAX <= 4, "capacities above 128 rows use fps_coop");
   return 0;
 }
 
