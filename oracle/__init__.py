@@ -69,6 +69,8 @@ def lib():
         L.orc_score_unit.restype = I
         L.orc_score_given.argtypes = [I, I, I, P, I, P, P, I, P, P, I, LONG, D, I, P, P, P, P]
         L.orc_score_given.restype = I
+        L.orc_decode_attention.argtypes = [I, I, I, P, P, I, P, P, P]
+        L.orc_decode_attention.restype = None
         L.orc_select.argtypes = [P, I, I, I, P]
         L.orc_select.restype = I
         L.orc_compact.argtypes = [P, LONG, P, I]
@@ -290,6 +292,21 @@ def score_given(K: np.ndarray, L: int, recent: np.ndarray, recent_pos: np.ndarra
     if rc != 0:
         raise ValueError("oracle score_given rejected a beacon count")
     return scores[:L].copy(), obs[:rows].copy(), valid[:rows].copy(), lse[:rows].copy()
+
+
+def decode_attention(K: np.ndarray, V: np.ndarray, L: int, q: np.ndarray):
+    """One decode step of one KV head: q [G, d] storage (rotated), K, V
+    [>=L, d] storage.  Returns (out float64 [G, d], probs float64 [G, L])."""
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    q = np.ascontiguousarray(q)
+    G, d = q.shape
+    dt = dtype_code(K)
+    assert dtype_code(V) == dt and dtype_code(q) == dt
+    out = np.zeros((G, d), dtype=np.float64)
+    probs = np.zeros((G, max(L, 1)), dtype=np.float64)
+    lib().orc_decode_attention(dt, d, G, _ptr(K), _ptr(V), L, _ptr(q), _ptr(probs), _ptr(out))
+    return out, probs[:, :L].copy()
 
 
 def score(K, lens, recent, recent_pos, qbuf, qcount, nb, pos_now, theta, units=None):

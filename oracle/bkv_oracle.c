@@ -590,6 +590,55 @@ int orc_score_given(int dtype, int d, int G, const void *K, int L, const void *r
 }
 
 /* ------------------------------------------------------------------------ */
+/* Decode attention with the recent rows' probabilities captured              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * orc_decode_attention: one decode step of the G query heads of one KV head.
+ * Each query q_g (already rotated at its own position) attends to the L
+ * cached keys present at this step: p_g(j) = softmax_j(q_g . k_j / sqrt(d)),
+ * out_g = sum_j p_g(j) v_j, in binary64.
+ *
+ * [WZ, 信标查询怎么用] scores keys with the attention of the recent queries;
+ * [WZ, 信标和最近查询该怎么分配] places the extra cost of scoring in the
+ * beacons' attention.  Reading (R24): a recent query's probabilities can be
+ * taken from its own decode step, over the keys present then, instead of
+ * being recomputed at eviction time over the whole cache; the per-key
+ * aggregate is the maximum over the recent steps and the G heads, as for
+ * the eviction-time rows.
+ *
+ * Layouts: K, V [L][d] storage; q [G][d] storage.  probs [G][L] (binary64,
+ * optional), out [G][d] (binary64).  L = 0 gives out = 0.
+ */
+void orc_decode_attention(int dtype, int d, int G, const void *K, const void *V, int L, const void *q,
+                          double *probs, double *out) {
+  double *qg = (double *)malloc(sizeof(double) * d);
+  double *kj = (double *)malloc(sizeof(double) * d);
+  double *s = (double *)malloc(sizeof(double) * (L > 0 ? L : 1));
+  double inv_sqrt_d = 1.0 / sqrt((double)d);
+  for (int g = 0; g < G; ++g) {
+    for (int t = 0; t < d; ++t) qg[t] = orc_load(q, dtype, (long)g * d + t);
+    double mx = -INFINITY;
+    for (int j = 0; j < L; ++j) {
+      for (int t = 0; t < d; ++t) kj[t] = orc_load(K, dtype, (long)j * d + t);
+      s[j] = dot(qg, kj, d) * inv_sqrt_d;
+      if (s[j] > mx) mx = s[j];
+    }
+    double sum = 0.0;
+    for (int j = 0; j < L; ++j) sum += exp(s[j] - mx);
+    for (int t = 0; t < d; ++t) out[(size_t)g * d + t] = 0.0;
+    for (int j = 0; j < L; ++j) {
+      double p = exp(s[j] - mx) / sum;
+      if (probs) probs[(size_t)g * L + j] = p;
+      for (int t = 0; t < d; ++t) out[(size_t)g * d + t] += p * orc_load(V, dtype, (long)j * d + t);
+    }
+  }
+  free(qg);
+  free(kj);
+  free(s);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Selection and compaction                                                   */
 /* ------------------------------------------------------------------------ */
 
