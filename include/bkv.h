@@ -326,6 +326,44 @@ int bkv_select_compact_fill(const bkv_shape *shape, const float *scores, void *K
                             int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Recent-query scores captured during decoding ([WZ] 信标查询怎么用: the score
+ * of a key takes the attention of the recent queries with the beacons';
+ * [WZ] 信标和最近查询该怎么分配: the beacons' attention is the extra cost).
+ * Decoding computes every recent query's attention anyway, so its
+ * probabilities can be kept as they are produced, and at eviction only the
+ * beacons need a scoring pass.  A captured probability is normalised over the
+ * keys present at its own decode step (the eviction-time rows of bkv_score
+ * are normalised over the whole cache).
+ *
+ * bkv_decode_attention -- one decode step of attention for every query head:
+ *     q       [N][Hq][d]     the step's queries, already rotated (read only)
+ *     K, V    [N][Hkv][Lmax][d]  the cache, rows [0, len[n]) present
+ *     len     [N]            int32, in [0, Lmax] (else BKV_DEV_BAD_LEN, unit
+ *                            untouched)
+ *     out     [N][Hq][d]     float: softmax_j(q . k_j / sqrt(d)) v_j summed
+ *                            over the present keys; 0 when len = 0
+ *     capture [N][Hkv][Lmax] float or NULL: for j < len[n],
+ *                            capture[j] = max(capture[j], max_g p_g(j)) over
+ *                            the G query heads of the KV head; the caller
+ *                            zeroes it where the recent window starts
+ *   ws: its own workspace, 256-byte aligned: bkv_decode_workspace_size(shape)
+ *   bytes with a capture array (the step's logits are staged there), 256
+ *   without.  G = Hq / Hkv in {1, 2, 4, 5, 8}.
+ *
+ * bkv_score_picked_capture -- the eviction scores from the beacons alone
+ *   (bkv_score_picked with R = 0: the workspace of shape, 0, nb, after
+ *   bkv_beacon_picks with R = 0), each key's score then raised to its
+ *   captured recent maximum: scores[j] = max(beacon score, capture[j]).
+ */
+size_t bkv_decode_workspace_size(const bkv_shape *shape);
+int bkv_decode_attention(const bkv_shape *shape, const void *q, const void *K, const void *V,
+                         const int32_t *len, float *out, float *capture, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+int bkv_score_picked_capture(const bkv_shape *shape, const void *K, const int32_t *len,
+                             const float *capture, int32_t nb, const int32_t *pos_now, double rope_theta,
+                             float *scores, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * bkv_fps_full -- FPS over each query head's WHOLE stored history: the naive
  * alternative that Continual FPS replaces ([WZ] 怎么挑出这几个信标: FPS over
  * every past query would keep the full history of each head, which the

@@ -44,6 +44,9 @@ EXPORTS = (
     "bkv_select_fill",
     "bkv_compact_fill",
     "bkv_select_compact_fill",
+    "bkv_decode_workspace_size",
+    "bkv_decode_attention",
+    "bkv_score_picked_capture",
     "bkv_fps_full_workspace_size",
     "bkv_fps_full",
     "bkv_status_string",
@@ -113,6 +116,12 @@ def load() -> ctypes.CDLL:
     L.bkv_score_picked_agg.restype = ctypes.c_int
     L.bkv_beacon_rows.argtypes = [SP, P, I32, P, I32, I32, P, SZ, P]
     L.bkv_beacon_rows.restype = ctypes.c_int
+    L.bkv_decode_workspace_size.argtypes = [SP]
+    L.bkv_decode_workspace_size.restype = SZ
+    L.bkv_decode_attention.argtypes = [SP, P, P, P, P, P, P, P, SZ, P]
+    L.bkv_decode_attention.restype = ctypes.c_int
+    L.bkv_score_picked_capture.argtypes = [SP, P, P, P, I32, P, ctypes.c_double, P, P, SZ, P]
+    L.bkv_score_picked_capture.restype = ctypes.c_int
     L.bkv_fps_full_workspace_size.argtypes = [SP, I32]
     L.bkv_fps_full_workspace_size.restype = SZ
     L.bkv_fps_full.argtypes = [SP, P, I32, I32, P, P, SZ, P]
@@ -241,6 +250,22 @@ def bkv_select_compact_fill(shape: Shape, scores, K, V, pos, length, budget: int
     _check(load().bkv_select_compact_fill(ctypes.byref(shape), _ptr(scores), _ptr(K), _ptr(V), _ptr(pos),
                                           _ptr(length), budget, window, _ptr(kept), _ptr(ws),
                                           ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_decode_workspace_size(shape: Shape) -> int:
+    return int(load().bkv_decode_workspace_size(ctypes.byref(shape)))
+
+
+def bkv_decode_attention(shape: Shape, q, K, V, length, out, capture, ws, stream=None) -> None:
+    _check(load().bkv_decode_attention(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(length), _ptr(out),
+                                       _ptr(capture), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def bkv_score_picked_capture(shape: Shape, K, length, capture, nb: int, pos_now, rope_theta: float, scores, ws,
+                             stream=None) -> None:
+    _check(load().bkv_score_picked_capture(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(capture), nb,
+                                           _ptr(pos_now), float(rope_theta), _ptr(scores), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def bkv_fps_full_workspace_size(shape: Shape, n: int) -> int:

@@ -15,7 +15,10 @@ hipError_t launch_beacon_picks(const void*, const int32_t*, int, int, int, int32
 template <int DT, int D>
 hipError_t launch_score(const void*, const int32_t*, int, int, int, int, const void*, const int32_t*, int,
                         const int32_t*, const void*, int, const int32_t*, double, float2*, void*, int32_t*, int,
-                        float*, float*, int32_t*, bool, hipStream_t);
+                        float*, float*, int32_t*, bool, const float*, hipStream_t);
+template <int DT, int D>
+hipError_t launch_decode(const void*, const void*, const void*, const int32_t*, int, int, int, int, float*, float*,
+                         float*, int32_t*, hipStream_t);
 hipError_t launch_beacon_rows(const void*, int, const int32_t*, int, int, int, int32_t*, void*, int32_t*,
                               hipStream_t);
 hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
@@ -132,7 +135,8 @@ int check_score_args(const bkv_shape* shape, const void* K, const int32_t* len, 
 // The RoPE tables and the score kernel, with the beacon picks already in ws.
 int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
                   const int32_t* recent_pos, int32_t R, int32_t nb, const int32_t* pos_now, double rope_theta,
-                  float* scores, void* ws, const WsLayout& w, bool mean, hipStream_t stream) {
+                  float* scores, void* ws, const WsLayout& w, bool mean, hipStream_t stream,
+                  const float* capture = nullptr) {
   const int N = shape->n_seq, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads;
   if (N == 0) return BKV_OK;
   unsigned char* base = (unsigned char*)ws;
@@ -146,7 +150,7 @@ int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, con
   hipError_t e;
 #define BKV_SCORE_CASE(DT, D)                                                                                  \
   e = launch_score<DT, D>(K, len, N, Hkv, Hq, shape->max_len, recent, recent_pos, R, beacons, brows, nb,       \
-                          pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, mean, stream);
+                          pos_now, rope_theta, tab, obs, valid, w.RP, scores, lse, words, mean, capture, stream);
   if (shape->dtype == BKV_BF16) {
     if (shape->head_dim == 128) {
       BKV_SCORE_CASE(BKV_BF16, 128)
@@ -284,6 +288,46 @@ int bkv_score_picked_agg(const bkv_shape* shape, const void* K, const int32_t* l
   if (st != BKV_OK) return st;
   return enqueue_score(shape, K, len, recent, recent_pos, R, nb, pos_now, rope_theta, scores, ws, w,
                        aggregation == BKV_AGG_MEAN, stream);
+}
+
+int bkv_score_picked_capture(const bkv_shape* shape, const void* K, const int32_t* len, const float* capture,
+                             int32_t nb, const int32_t* pos_now, double rope_theta, float* scores, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  WsLayout w;
+  int st = check_score_args(shape, K, len, nullptr, nullptr, 0, nullptr, nullptr, false, -1, nb, pos_now, rope_theta,
+                            scores, ws, ws_bytes, &w);
+  if (st != BKV_OK) return st;
+  if (!capture) return BKV_E_NULL;
+  return enqueue_score(shape, K, len, nullptr, nullptr, 0, nb, pos_now, rope_theta, scores, ws, w, false, stream,
+                       capture);
+}
+
+size_t bkv_decode_workspace_size(const bkv_shape* shape) {
+  if (check_shape(shape) != BKV_OK) return 0;
+  const size_t G = (size_t)(shape->n_q_heads / shape->n_kv_heads);
+  return align256(kHeaderBytes) + align256((size_t)shape->n_seq * shape->n_kv_heads * G * shape->max_len * 4);
+}
+
+int bkv_decode_attention(const bkv_shape* shape, const void* q, const void* K, const void* V, const int32_t* len,
+                         float* out, float* capture, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  const int G = shape->n_q_heads / shape->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 5 && G != 8) return BKV_E_SHAPE;
+  if (!q || !K || !V || !len || !out) return BKV_E_NULL;
+  if ((st = check_ws(ws, ws_bytes, capture ? bkv_decode_workspace_size(shape) : kHeaderBytes)) != BKV_OK) return st;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if (N == 0) return BKV_OK;
+  int32_t* words = (int32_t*)ws;
+  float* logits = capture ? (float*)((unsigned char*)ws + align256(kHeaderBytes)) : nullptr;
+  hipError_t e;
+#define BKV_DEC(DT, D) launch_decode<DT, D>(q, K, V, len, N, Hkv, G, shape->max_len, out, capture, logits, words, stream)
+  if (shape->dtype == BKV_BF16)
+    e = shape->head_dim == 128 ? BKV_DEC(BKV_BF16, 128) : BKV_DEC(BKV_BF16, 64);
+  else
+    e = shape->head_dim == 128 ? BKV_DEC(BKV_F32, 128) : BKV_DEC(BKV_F32, 64);
+#undef BKV_DEC
+  return hip_status(e);
 }
 
 int bkv_beacon_rows(const bkv_shape* shape, const void* src, int32_t S, const int32_t* idx, int32_t R, int32_t nb,

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
     const int32_t* __restrict__ beacons, const typename Elem<DT>::T* __restrict__ brows, int nb,
     const float2* __restrict__ tab, typename Elem<DT>::T* __restrict__ obs, int32_t* __restrict__ obs_valid, int RP,
-    float* __restrict__ scores, float* __restrict__ lse_out, int32_t* __restrict__ ws_words) {
+    float* __restrict__ scores, float* __restrict__ lse_out, const float* __restrict__ capture,
+    int32_t* __restrict__ ws_words) {
   using Lay = ScoreLayout<DT, D>;
   using MF = Mfma<DT, D>;
   using Frag = typename MF::Frag;
@@ -437,7 +438,9 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
           out[j] = t * inv_present;
         } else {
           for (int w = 1; w < nrow_waves; ++w) t = fmaxf(t, part[w * kTile + k]);
-          out[j] = exp2f(t);  // exp2(-inf) = 0 when no row is present
+          float v = exp2f(t);  // exp2(-inf) = 0 when no row is present
+          if (capture != nullptr) v = fmaxf(v, capture[unit * (size_t)Lmax + j]);  // the recent rows' captured maxima
+          out[j] = v;
         }
       }
     }
@@ -448,7 +451,8 @@ template <int DT, int D, int NW, bool kMean>
 static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax,
                                   const void* recent, const int32_t* recent_pos, int R, const int32_t* beacons,
                                   const void* brows, int nb, const float2* tab, void* obs, int32_t* obs_valid,
-                                  int RP, float* scores, float* lse, int32_t* ws_words, hipStream_t st) {
+                                  int RP, float* scores, float* lse, const float* capture, int32_t* ws_words,
+                                  hipStream_t st) {
   using Lay = ScoreLayout<DT, D>;
   using ET = typename Elem<DT>::T;
   const size_t smem = (size_t)kTile * Lay::kRowStride + (size_t)NW * kTile * sizeof(float) + RP * sizeof(float) +
@@ -458,7 +462,7 @@ static hipError_t launch_score_nw(const void* K, const int32_t* len, int N, int 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(N * Hkv), dim3(64 * NW), smem, st, (const ET*)K, len, Hkv, Hq, Lmax,
                      (const ET*)recent, recent_pos, R, beacons, (const ET*)brows, nb, tab, (ET*)obs, obs_valid, RP,
-                     scores, lse, ws_words);
+                     scores, lse, capture, ws_words);
   return hipGetLastError();
 }
 
@@ -468,16 +472,18 @@ template <int DT, int D>
 hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int Hq, int Lmax, const void* recent,
                         const int32_t* recent_pos, int R, const int32_t* beacons, const void* brows, int nb,
                         const int32_t* pos_now, double theta, float2* tab, void* obs, int32_t* obs_valid, int RP,
-                        float* scores, float* lse, int32_t* ws_words, bool mean, hipStream_t st) {
+                        float* scores, float* lse, int32_t* ws_words, bool mean, const float* capture,
+                        hipStream_t st) {
   hipLaunchKernelGGL(rope_table_kernel<D>, dim3(N), dim3(256), 0, st, recent_pos, pos_now, R, theta, tab);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int tiles = RP / 32;
 #define BKV_SCORE_NW(NW)                                                                                       \
   return mean ? launch_score_nw<DT, D, NW, true>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, beacons, brows, \
-                                                 nb, tab, obs, obs_valid, RP, scores, lse, ws_words, st)         \
+                                                 nb, tab, obs, obs_valid, RP, scores, lse, nullptr, ws_words, st) \
               : launch_score_nw<DT, D, NW, false>(K, len, N, Hkv, Hq, Lmax, recent, recent_pos, R, beacons,      \
-                                                  brows, nb, tab, obs, obs_valid, RP, scores, lse, ws_words, st)
+                                                  brows, nb, tab, obs, obs_valid, RP, scores, lse, capture,      \
+                                                  ws_words, st)
   if (tiles <= 2) BKV_SCORE_NW(2);
   if (tiles <= 4) BKV_SCORE_NW(4);
   BKV_SCORE_NW(8);
@@ -488,7 +494,7 @@ hipError_t launch_score(const void* K, const int32_t* len, int N, int Hkv, int H
   template hipError_t launch_score<DT, D>(const void*, const int32_t*, int, int, int, int, const void*,       \
                                           const int32_t*, int, const int32_t*, const void*, int,              \
                                           const int32_t*, double, float2*, void*, int32_t*, int, float*,      \
-                                          float*, int32_t*, bool, hipStream_t);
+                                          float*, int32_t*, bool, const float*, hipStream_t);
 BKV_INST_SCORE(BKV_F32, 64)
 BKV_INST_SCORE(BKV_F32, 128)
 BKV_INST_SCORE(BKV_BF16, 64)

@@ -202,3 +202,26 @@ def test_policy_entry_points_validation(lib):
     assert sa(*a) == bkv.E_NULL
     a = list(ok); a[12] = 1024
     assert sa(*a) == bkv.E_WORKSPACE
+
+
+def test_decode_entry_points_validation(lib):
+    s = shape()
+    fake, big, P = 256, 1 << 40, None
+    d = lib.bkv_decode_attention
+    assert d(None, fake, fake, fake, fake, fake, None, fake, big, P) == bkv.E_NULL
+    assert d(ctypes.byref(s), None, fake, fake, fake, fake, None, fake, big, P) == bkv.E_NULL
+    assert d(ctypes.byref(s), fake, fake, fake, fake, None, None, fake, big, P) == bkv.E_NULL
+    assert d(ctypes.byref(shape(n_q_heads=24)), fake, fake, fake, fake, fake, None, fake, big, P) == bkv.E_SHAPE  # G = 3
+    need = bkv.bkv_decode_workspace_size(s)
+    assert need >= 256 + 2 * 8 * 4 * 2176 * 4
+    assert d(ctypes.byref(s), fake, fake, fake, fake, fake, fake, fake, need - 1, P) == bkv.E_WORKSPACE
+    assert d(ctypes.byref(s), fake, fake, fake, fake, fake, None, fake + 8, big, P) == bkv.E_WORKSPACE
+    assert d(ctypes.byref(shape(n_seq=0)), fake, fake, fake, fake, fake, None, fake, 256, P) == bkv.OK
+    c = lib.bkv_score_picked_capture
+    ok = [ctypes.byref(s), fake, fake, fake, 16, fake, 1e6, fake, fake, big, P]
+    a = list(ok); a[3] = None
+    assert c(*a) == bkv.E_NULL
+    a = list(ok); a[4] = 0
+    assert c(*a) == bkv.E_SHAPE  # no observation rows at all
+    a = list(ok); a[9] = 1024
+    assert c(*a) == bkv.E_WORKSPACE
