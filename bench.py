@@ -54,7 +54,7 @@ def kernel_source_hash() -> str:
     import re
 
     h = hashlib.sha256()
-    for name in ("fps.hip", "score.hip", "select.hip", "bkv_api.hip", "bkv_device.hpp", "fps_full.hip"):
+    for name in ("fps.hip", "score.hip", "select.hip", "bkv_api.hip", "bkv_device.hpp", "fps_full.hip", "decode.hip"):
         with open(os.path.join(ROOT, "kv_cache_eviction_continual_amd", "csrc", name), encoding="utf-8") as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -613,6 +613,63 @@ def fps_compare(reps: int = 3):
     print(json.dumps(result), flush=True)
 
 
+def decode_compare(reps: int = 20):
+    """One decode step of attention over the benchmark workload's cache, with
+    and without the recent-query capture, and the eviction scoring it
+    shortens: recent and beacon rows at eviction time, against the beacons
+    alone raised to the captured maxima.  Prints its own JSON line."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bkv.load()
+    w = configs.get(CFG)
+    st = State(w, dev, n_pool=w.warm_steps // w.interval + 2)
+    N, Hkv, Hq, d, L = st.N, w.n_kv_heads, w.n_q_heads, w.head_dim, w.length
+    q = st.recent[st.block(0)][:, :, -1].contiguous()  # one query per head: [N, Hq, d]
+    out = torch.empty(N, Hq, d, device=dev)
+    capture = torch.zeros(N, Hkv, w.max_len, device=dev)
+    ws_dec = torch.zeros(bkv.bkv_decode_workspace_size(st.shape), dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    plain = timed(lambda: bkv.bkv_decode_attention(st.shape, q, st.K, st.V, st.length, out, None, ws_dec))
+    capt = timed(lambda: bkv.bkv_decode_attention(st.shape, q, st.K, st.V, st.length, out, capture, ws_dec))
+    assert bkv.bkv_read_device_status(ws_dec) == 0
+    kv_bytes = 2 * N * Hkv * L * d * st.K.element_size()
+    # eviction scoring: recent + beacon rows at eviction time, or the beacons alone plus the capture
+    bkv.bkv_beacon_picks(st.shape, st.qbuf, st.qcount, w.capacity, w.n_recent, w.n_beacons, st.ws)
+    full = timed(lambda: st.score_picked(0, Group(st, 0, N, st.ws, None, None), torch.cuda.current_stream()))
+    ws0 = bkv.alloc_workspace(st.shape, 0, w.n_beacons, device=dev)
+    bkv.bkv_beacon_picks(st.shape, st.qbuf, st.qcount, w.capacity, 0, w.n_beacons, ws0)
+    pos_now = st.pos_now[0]
+    beac = timed(lambda: bkv.bkv_score_picked_capture(st.shape, st.K, st.length, capture, w.n_beacons, pos_now,
+                                                      w.rope_theta, st.scores, ws0))
+    assert bkv.bkv_read_device_status(ws0) == 0 and bkv.bkv_read_device_status(st.ws) == 0
+    result = {
+        "metric": "decode attention step with the recent-query capture; eviction scoring with and without it",
+        "workload": "%s: %d slots x %d KV heads, %d query heads, cache %d, one query per head" % (w.name, N, Hkv, Hq, L),
+        "data": "synthetic",
+        "dtype": "bf16 storage, fp32 arithmetic",
+        "decode_ms": plain,
+        "decode_with_capture_ms": capt,
+        "capture_overhead": capt / plain - 1.0,
+        "decode_kv_GBps": kv_bytes / (plain * 1e6),
+        "decode_with_capture_kv_GBps": kv_bytes / (capt * 1e6),
+        "eviction_score_recent_and_beacons_ms": full,
+        "eviction_score_beacons_plus_capture_ms": beac,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def load_traffic(src_hash, workload):
     """The recorded counter figures, if they were taken on this workload with
     these kernel sources."""
@@ -641,6 +698,8 @@ def main():
     ap.add_argument("--no-all-cores", action="store_true", help="skip the all-host-threads oracle timing")
     ap.add_argument("--workload", type=int, default=CFG, choices=(3, 4, 5),
                     help="3: Qwen3-4B b16 B=2K (default); 4: Qwen3-4B b320 B=1K; 5: Qwen3-14B b32 B=4K")
+    ap.add_argument("--decode-compare", action="store_true",
+                    help="instead of the eviction pass: decode attention with and without the recent-query capture")
     ap.add_argument("--fps-compare", action="store_true",
                     help="instead of the eviction pass: full-history FPS vs Continual FPS on one Qwen3-14B layer")
     args = ap.parse_args()
@@ -651,6 +710,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.fps_compare:
         fps_compare()
+        return
+    if args.decode_compare:
+        decode_compare()
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -17,8 +17,9 @@
 // reduced across the sixteen lanes, an online softmax per query head in the
 // log2 domain, and the value rows accumulated under it.  The four key groups
 // of a wave, then the four waves, are merged at the end.  With a capture
-// array, each key's logits go to a workspace slice, and a last sweep turns
-// them into probabilities with the final log-sum-exp and folds them in.
+// array, each key's logits are kept (in LDS when the unit's G x Lmax of them
+// fit in 48 KB, else in a workspace slice), and a last sweep turns them into
+// probabilities with the final log-sum-exp and folds them in.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -67,18 +68,29 @@ struct DecPart {
   }
 };
 
+// Sum over a row of sixteen lanes, left in every lane of the row, by DPP
+// moves (no LDS): swap neighbours, swap pairs, mirror the halves of the row,
+// mirror the row.  Each step adds two values in either order, so every lane
+// ends with the same bits.
+template <int CTRL>
+__device__ inline float dec_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
 __device__ inline float dec_sum16(float v) {
-  v += __shfl_xor(v, 8, 16);
-  v += __shfl_xor(v, 4, 16);
-  v += __shfl_xor(v, 2, 16);
-  v += __shfl_xor(v, 1, 16);
+  v += dec_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dec_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dec_dpp<0x141>(v);  // row_half_mirror
+  v += dec_dpp<0x140>(v);  // row_mirror
   return v;
 }
 
 // exp2 of x - m for a running maximum m that may still be -inf (nothing seen).
 __device__ inline float dec_rescale(float x, float m) { return m == -__builtin_huge_valf() ? 0.0f : exp2f(x - m); }
 
-template <int DT, int D, int G>
+constexpr int kDecLdsLogits = 48 * 1024;  // bytes of logits kept in LDS at most
+
+template <int DT, int D, int G, bool kLdsLogits>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     const typename Elem<DT>::T* __restrict__ q, const typename Elem<DT>::T* __restrict__ K,
     const typename Elem<DT>::T* __restrict__ V, const int32_t* __restrict__ len, int Hkv, int Lmax,
@@ -90,6 +102,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   __shared__ float red_m[NW][G], red_l[NW][G];
   __shared__ float red_acc[NW][G][D];
   __shared__ float lse2[G];
+  extern __shared__ float lds_logits[];  // [G][Lmax] when kLdsLogits
 
   const size_t unit = blockIdx.x;
   const int n = (int)(unit / Hkv);
@@ -121,14 +134,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
     for (int k = 0; k < EL; ++k) acc[g][k] = 0.0f;
   }
 
+  // the rows of the next block are loaded while this block is computed
+  typename P::R kr[kDecSteps], vr[kDecSteps];
+#pragma unroll
+  for (int u = 0; u < kDecSteps; ++u) {
+    const int j = 16 * u + 4 * wave + sub;
+    if (j < L) {
+      kr[u] = P::load(Kb + (size_t)j * D, part);
+      vr[u] = P::load(Vb + (size_t)j * D, part);
+    }
+  }
   for (int j0 = 0; j0 < L; j0 += 16 * kDecSteps) {
-    typename P::R kr[kDecSteps], vr[kDecSteps];
+    typename P::R kn[kDecSteps], vn[kDecSteps];
 #pragma unroll
     for (int u = 0; u < kDecSteps; ++u) {
-      const int j = j0 + 16 * u + 4 * wave + sub;
+      const int j = j0 + 16 * kDecSteps + 16 * u + 4 * wave + sub;
       if (j < L) {
-        kr[u] = P::load(Kb + (size_t)j * D, part);
-        vr[u] = P::load(Vb + (size_t)j * D, part);
+        kn[u] = P::load(Kb + (size_t)j * D, part);
+        vn[u] = P::load(Vb + (size_t)j * D, part);
       }
     }
     float sv[kDecSteps][G];
@@ -146,7 +169,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
         }
         d = dec_sum16(d);
         sv[u][g] = j < L ? d * scale2 : ninf;
-        if (logits != nullptr && part == 0 && j < L) logits[(unit * G + g) * (size_t)Lmax + j] = sv[u][g];
+        if (capture != nullptr && part == 0 && j < L) {
+          if constexpr (kLdsLogits) lds_logits[g * Lmax + j] = sv[u][g];
+          else logits[(unit * G + g) * (size_t)Lmax + j] = sv[u][g];
+        }
       }
     }
 #pragma unroll
@@ -175,6 +201,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
 #pragma unroll
         for (int k = 0; k < EL; ++k) acc[g][k] = fmaf(p, v[k], acc[g][k]);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecSteps; ++u) {
+      kr[u] = kn[u];
+      vr[u] = vn[u];
     }
   }
 
@@ -227,7 +258,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(
   for (int j = threadIdx.x; j < L; j += kDecThreads) {
     float c = cap[j];
 #pragma unroll
-    for (int g = 0; g < G; ++g) c = fmaxf(c, exp2f(logits[(unit * G + g) * (size_t)Lmax + j] - lse2[g]));
+    for (int g = 0; g < G; ++g) {
+      const float s2 = kLdsLogits ? lds_logits[g * Lmax + j] : logits[(unit * G + g) * (size_t)Lmax + j];
+      c = fmaxf(c, exp2f(s2 - lse2[g]));
+    }
     cap[j] = c;
   }
 }
@@ -237,8 +271,17 @@ static hipError_t launch_decode_g(const void* q, const void* K, const void* V, c
                                   int Lmax, float* out, float* capture, float* logits, int32_t* ws_words,
                                   hipStream_t st) {
   using ET = typename Elem<DT>::T;
-  hipLaunchKernelGGL((decode_kernel<DT, D, G>), dim3(N * Hkv), dim3(kDecThreads), 0, st, (const ET*)q,
-                     (const ET*)K, (const ET*)V, len, Hkv, Lmax, out, capture, logits, ws_words);
+  const size_t lds = (size_t)G * Lmax * sizeof(float);
+  if (capture != nullptr && lds <= (size_t)kDecLdsLogits) {
+    auto kern = decode_kernel<DT, D, G, true>;
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(N * Hkv), dim3(kDecThreads), lds, st, (const ET*)q, (const ET*)K, (const ET*)V,
+                       len, Hkv, Lmax, out, capture, logits, ws_words);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<DT, D, G, false>), dim3(N * Hkv), dim3(kDecThreads), 0, st, (const ET*)q,
+                       (const ET*)K, (const ET*)V, len, Hkv, Lmax, out, capture, logits, ws_words);
+  }
   return hipGetLastError();
 }
 
