@@ -133,3 +133,40 @@ def test_captured_recent_steps_plus_beacons_equal_oracle(cfg):
             err = np.abs(got[n, h, :L_end] - want)
             assert np.all(err <= RTOL * want + 1e-30), (n, h, float(np.max(err / want)))
     log("  capture + beacons: %d units" % (N * w.n_kv_heads))
+
+
+def test_decode_full_size_benchmark_workload():
+    """The decode step at the benchmark workload's full size (576 slots x 8 KV
+    heads, 32 query heads, cache 2176), in the launch configuration
+    bench.py --decode-compare times; the oracle recomputes a seeded sample of
+    units, and every unit's capture is checked to be a probability (0, 1]
+    on present keys and 0 beyond."""
+    w = configs.get(3)
+    syn = synth.Synth(w, seed=5, device="cuda")
+    K, V = syn.keys(), syn.values()
+    q = syn.query_block(0)[:, :, -1].contiguous()
+    N, Hkv, G, d = w.n_slots, w.n_kv_heads, w.group, w.head_dim
+    rng = np.random.default_rng(5)
+    lengths = rng.integers(w.budget, w.length + 1, size=N).astype(np.int32)
+    lengths[0], lengths[-1] = w.length, 1
+    shape = bkv.make_shape(N, Hkv, w.n_q_heads, d, w.max_len, K.dtype)
+    capture = torch.zeros(N, Hkv, w.max_len, device="cuda")
+    out, status = _decode(shape, q, K, V, torch.from_numpy(lengths).cuda(), capture)
+    assert status == 0
+    L_idx = torch.arange(w.max_len, device="cuda")
+    present = L_idx[None, None, :] < torch.from_numpy(lengths).cuda()[:, None, None]
+    assert torch.all((capture > 0) == present) and torch.all(capture <= 1.0)
+    out_h, cap_h = out.cpu().numpy(), capture.cpu().numpy()
+    units = {(0, 0), (N - 1, Hkv - 1)}
+    while len(units) < 8:
+        units.add((int(rng.integers(0, N)), int(rng.integers(0, Hkv))))
+    for n, h in sorted(units):
+        L = int(lengths[n])
+        Kh = synth.to_numpy_storage(K[n, h])
+        Vh = synth.to_numpy_storage(V[n, h])
+        qh = synth.to_numpy_storage(q[n, h * G:(h + 1) * G])
+        o_out, o_p = oracle.decode_attention(Kh, Vh, L, qh)
+        _check_out(out_h[n, h * G:(h + 1) * G], o_out, o_p, oracle.to_double(Vh), L)
+        want = o_p.max(axis=0)
+        assert np.all(np.abs(cap_h[n, h, :L] - want) <= RTOL * want + 1e-30), (n, h)
+    log("  full-size decode: %d sampled units" % len(units))
