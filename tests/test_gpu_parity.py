@@ -143,6 +143,14 @@ def test_head_dim_64_bf16_and_128_f32():
     run_and_compare(configs.get(2, dtype="f32", length=600, budget=512, warm_steps=600), check_blocks=False)
 
 
+def test_maximum_observation_rows():
+    """G (R + nb) = 256 rows per unit, the largest the score kernel takes
+    (eight row tiles): 32 recent + 32 beacons, then 64 recent queries alone
+    (the largest R)."""
+    run_and_compare(configs.get(2, n_recent=32, n_beacons=32), N=1, steps=400, lengths=[2176], check_blocks=False)
+    run_and_compare(configs.get(2, n_recent=64, n_beacons=0), N=1, steps=400, lengths=[2176], check_blocks=False)
+
+
 def test_capacity_256_qwen3_14b_shape_one_slot():
     w = configs.get(5)
     run_and_compare(w, N=1, steps=1100, lengths=[4224], check_blocks=False)
