@@ -1026,7 +1026,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 template <int DT, int D, int NTMAX>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void beacon_pick_kernel(
     const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
-    int32_t* __restrict__ beacons, typename Elem<DT>::T* __restrict__ rows, int32_t* __restrict__ ws_words) {
+    int32_t* __restrict__ beacons, typename Elem<DT>::T* __restrict__ rows, int32_t* __restrict__ ws_words,
+    int cmax) {
   constexpr int cap = 32 * NTMAX;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
@@ -1036,6 +1037,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     if (lane == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
     c = 0;
   }
+  if (c > cmax) return;  // more live rows than this kernel holds: the cooperative kernel takes the head
   const int want = nb < c ? nb : c;
   FpsLds s = fps_carve<DT, D>(smem, cap, 0);
   const FpsRows<DT, D> src{qbuf + (size_t)head * C * D, nullptr, s.map, C};
@@ -1132,7 +1134,7 @@ __global__ __launch_bounds__(64 * NT) void beacon_pick_coop_kernel(const typenam
                                                               const int32_t* __restrict__ qcount, int C, int nb,
                                                               int32_t* __restrict__ beacons,
                                                               typename Elem<DT>::T* __restrict__ rows,
-                                                              int32_t* __restrict__ ws_words) {
+                                                              int32_t* __restrict__ ws_words, int cmin) {
   constexpr int NTH = 64 * NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
@@ -1142,6 +1144,7 @@ __global__ __launch_bounds__(64 * NT) void beacon_pick_coop_kernel(const typenam
     if (tid == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
     c = 0;
   }
+  if (c <= cmin) return;  // few enough live rows for the single-wave kernel, which takes the head
   const int want = nb < c ? nb : c;
   FpsCoopLds s = fps_coop_carve<DT, D>(smem, NT, 0);
   const FpsRows<DT, D> src{qbuf + (size_t)head * C * D, nullptr, s.map, C};
@@ -1251,20 +1254,20 @@ hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcou
 
 template <int DT, int D, int NTMAX>
 static hipError_t launch_picks_nt(const void* qbuf, const int32_t* qcount, int C, int nb, int heads,
-                                  int32_t* beacons, void* rows, int32_t* ws_words, hipStream_t st) {
+                                  int32_t* beacons, void* rows, int32_t* ws_words, int cmax, hipStream_t st) {
   using ET = typename Elem<DT>::T;
   const size_t smem = fps_lds_bytes<DT, D>(32 * NTMAX, 0);
   auto kern = beacon_pick_kernel<DT, D, NTMAX>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(heads), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, beacons, (ET*)rows,
-                     ws_words);
+                     ws_words, cmax);
   return hipGetLastError();
 }
 
 template <int DT, int D>
 static hipError_t launch_picks_coop(const void* qbuf, const int32_t* qcount, int C, int nb, int heads,
-                                    int32_t* beacons, void* rows, int32_t* ws_words, hipStream_t st) {
+                                    int32_t* beacons, void* rows, int32_t* ws_words, int cmin, hipStream_t st) {
   using ET = typename Elem<DT>::T;
   constexpr int NT = 8;
   const size_t smem = fps_coop_lds_bytes<DT, D>(NT, 0);
@@ -1272,16 +1275,21 @@ static hipError_t launch_picks_coop(const void* qbuf, const int32_t* qcount, int
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(heads), dim3(64 * NT), smem, st, (const ET*)qbuf, qcount, C, nb, beacons,
-                     (ET*)rows, ws_words);
+                     (ET*)rows, ws_words, cmin);
   return hipGetLastError();
 }
 
+// Capacities above 128 rows: heads with at most 128 live rows take the
+// single-wave kernel (four waves per CU), the others the cooperative one;
+// each launch skips the other's heads.
 template <int DT, int D>
 hipError_t launch_beacon_picks(const void* qbuf, const int32_t* qcount, int C, int nb, int heads, int32_t* beacons,
                                void* rows, int32_t* ws_words, hipStream_t st) {
-  if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
-  if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
-  return launch_picks_coop<DT, D>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, C, st);
+  if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, C, st);
+  hipError_t e = launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, 128, st);
+  if (e != hipSuccess) return e;
+  return launch_picks_coop<DT, D>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, 128, st);
 }
 
 template hipError_t launch_fps_update<BKV_F32, 64>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
