@@ -199,6 +199,10 @@ class Schedule:
             a, b = bounds[k], bounds[k + 1]
             ws = st.ws if groups == 1 else st.group_workspace((a, b))
             self.groups.append(Group(st, a, b, ws, cur if k == 0 else torch.cuda.Stream(), side))
+        # the new streams start after everything already enqueued on the current one
+        for s in {g.main for g in self.groups} | ({side} if side is not None else set()):
+            if s != cur:
+                s.wait_stream(cur)
         self.last_scored = None
 
     @property
