@@ -61,3 +61,47 @@ def test_serial_and_pipelined_passes_agree_at_full_size():
             a, b = a[:, :, :w.length], b[:, :, :w.length]
         assert torch.equal(_bits(a) if a.is_floating_point() else a, _bits(b) if b.is_floating_point() else b), k
     log("  serial and pipelined passes agree on %d units" % (st.N * w.n_kv_heads))
+
+
+def test_hole_fill_serial_and_pipelined_agree_at_full_size():
+    """The same for the hole-filling layout: positions written each pass at
+    rows [B, L), one-call selection and filling, serial against pipelined."""
+    import bench
+
+    w = configs.get(3)
+    dev = torch.device("cuda:0")
+    st = bench.State(w, dev, n_pool=w.warm_steps // w.interval + 4)
+    N, Hkv, B, L = st.N, w.n_kv_heads, w.budget, w.length
+    pos = torch.arange(w.max_len, dtype=torch.int32, device=dev).expand(N, Hkv, w.max_len).contiguous()
+    snap = {k: getattr(st, k).clone() for k in ("K", "V", "qbuf", "qcount")}
+    pos0 = pos.clone()
+
+    def run(groups):
+        def grow(i, g):
+            st.length[g.sl].copy_(st.len_full[g.sl])
+            pos[g.sl, :, B:L].copy_(torch.arange(L - B, dtype=torch.int32, device=dev) + w.max_len + (L - B) * i)
+
+        def tail(i, rec, g):
+            bkv.bkv_select_compact_fill(g.shape, st.scores[g.sl], st.K[g.sl], st.V[g.sl], pos[g.sl], st.length[g.sl],
+                                        B, w.window, st.kept[g.sl], g.ws)
+
+        sched = bench.Schedule(st, grow, tail, groups > 0, ("select_compact",), groups=max(groups, 1))
+        for i in range(3):
+            sched.run(i)
+        torch.cuda.synchronize()
+        for ws in sched.workspaces:
+            assert bkv.bkv_read_device_status(ws) == 0
+
+    run(0)
+    ref = {k: getattr(st, k).clone() for k in ("K", "V", "kept", "length")}
+    ref_pos = pos.clone()
+    for k, v in snap.items():
+        getattr(st, k).copy_(v)
+    pos.copy_(pos0)
+    st.kept.fill_(-7)
+    torch.cuda.synchronize()
+    run(2)
+    for k in ("K", "V", "kept", "length"):
+        a, b = getattr(st, k), ref[k]
+        assert torch.equal(_bits(a) if a.is_floating_point() else a, _bits(b) if b.is_floating_point() else b), k
+    assert torch.equal(pos, ref_pos)
