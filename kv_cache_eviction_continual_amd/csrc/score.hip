@@ -23,7 +23,9 @@
 // prefetched into registers while the current one is multiplied).  Two
 // passes over K:
 //   pass 1: S^T = K Q^T on MFMA (lane = row, 16 keys per lane), online
-//           row max and sum of exp2 -> per-row log2-sum-exp;
+//           row max and sum of exp2 -> per-row log2-sum-exp; in a full tile
+//           the next sub-tile's products are issued among the current one's
+//           exp work, so one wave keeps the matrix core and the VALU busy;
 //   pass 2: S = Q K^T on MFMA (lane = key, 16 rows per lane), per-key max of
 //           (s - lse) over the wave's rows, then over the waves through LDS;
 //           one exp2 per key.  Pass 2 walks the tiles in reverse so that the
@@ -94,6 +96,29 @@ struct Mfma<BKV_F32, D> {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
 };
+
+// Scheduling pattern for one 32x32 sub-tile's eight products (each with
+// its LDS fragment reads) issued among the vector work of the previous
+// sub-tile: a product occupies the matrix core for 32 cycles, long enough
+// for about six vector instructions of the same wave.
+__device__ inline void interleave_products_with_exp() {
+  constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
+#define BKV_MFMA_THEN_VALU(nds)                           \
+  __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);      \
+  __builtin_amdgcn_sched_group_barrier(kValu, 6, 0);      \
+  __builtin_amdgcn_sched_group_barrier(kDsRead, nds, 0);
+  BKV_MFMA_THEN_VALU(2)
+  BKV_MFMA_THEN_VALU(0)
+  BKV_MFMA_THEN_VALU(2)
+  BKV_MFMA_THEN_VALU(0)
+  BKV_MFMA_THEN_VALU(2)
+  BKV_MFMA_THEN_VALU(0)
+  BKV_MFMA_THEN_VALU(0)
+  BKV_MFMA_THEN_VALU(0)
+#undef BKV_MFMA_THEN_VALU
+}
 
 // Accumulator element r of lane l holds output row 8 (r / 4) + 4 (l / 32) +
 // r % 4 and output column l % 32 (32x32 MFMA family, checked on gfx950).
@@ -197,6 +222,15 @@ struct ScoreLayout {
   static constexpr int kU = kRowBytes / 16;  // 16-byte units per key row
 };
 
+// Waves per SIMD the registers of a NW-wave block are budgeted for: three
+// blocks per CU for rows of at most 256 bytes, two for two-wave blocks (each
+// lane stages twice as much of a tile); wider (binary32, d = 128) rows take
+// what their fragments need.
+template <int DT, int D, int NW>
+constexpr int score_waves_per_simd() {
+  return ScoreLayout<DT, D>::kRowBytes > 256 ? 1 : NW == 2 ? 2 : 3;
+}
+
 // NW waves per block; the first RP / 32 of them own a row tile each, the
 // others only help to stage K.  Observation row r of the unit is, for
 // g = r / (R + nb) and k = r % (R + nb): recent query k of query head
@@ -204,7 +238,7 @@ struct ScoreLayout {
 // (present if below the pick count; read from the picks kernel's row copy);
 // rows from G (R + nb) to RP are padding.
 template <int DT, int D, int NW, bool kMean>
-__global__ __launch_bounds__(64 * NW) void score_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_waves_per_simd<DT, D, NW>()))) void score_kernel(
     const typename Elem<DT>::T* __restrict__ K, const int32_t* __restrict__ len, int Hkv, int Hq, int Lmax,
     const typename Elem<DT>::T* __restrict__ recent, const int32_t* __restrict__ recent_pos, int R,
     const int32_t* __restrict__ beacons, const typename Elem<DT>::T* __restrict__ brows, int nb,
@@ -324,34 +358,59 @@ __global__ __launch_bounds__(64 * NW) void score_kernel(
 
   // ---------------- pass 1: per-row log2-sum-exp ----------------
   float run_m = ninf, run_s = 0.0f;
+  // S^T for key sub-tile `sub` of the LDS tile: acc[r] is key
+  // sub*32 + acc_row(r, lane) of row lane % 32
+  auto logits_t = [&](int sub) {
+    const unsigned char* krow = ktile + (size_t)(sub * kSub + (lane & 31)) * Lay::kRowStride;
+    floatx16_t acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = MF::mma(MF::load(krow, s, lane), qf[s], acc);
+    return acc;
+  };
+  // every key of the sub-tile present: the scale is positive, so the maximum
+  // of the raw logits scales to the maximum of the scaled ones; one fma and
+  // one hardware exp2 per key (a term below 2^-126 of the running maximum is
+  // flushed to 0, which the sum of at least 1 cannot see)
+  auto fold_full = [&](const floatx16_t& acc) {
+    float mx = acc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+    const float m_new = fmaxf(run_m, mx * scale2);
+    float sum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -m_new));
+    run_s = run_s * __builtin_amdgcn_exp2f(run_m - m_new) + sum;
+    run_m = m_new;
+  };
   for (int tile = 0; tile < ntiles; ++tile) {
     __syncthreads();  // previous tile fully consumed
     commit();
     __syncthreads();
     if (tile + 1 < ntiles) prefetch(tile + 1);
     const int key0 = tile * kTile;
+    if (!has_rows) continue;
+    if (key0 + kTile <= L) {
+      // a full tile: the products of sub-tile sub + 1 are issued before the
+      // exp work of sub-tile sub, so the matrix cores and the vector ALUs of
+      // the wave overlap
+      floatx16_t cur = logits_t(0);
+#pragma unroll
+      for (int sub = 0; sub < kTile / kSub; ++sub) {
+        floatx16_t next = cur;
+        if (sub + 1 < kTile / kSub) next = logits_t(sub + 1);
+        fold_full(cur);
+        if (sub + 1 < kTile / kSub) interleave_products_with_exp();
+        __builtin_amdgcn_sched_barrier(0);  // one sub-tile pair per scheduling region
+        cur = next;
+      }
+      continue;
+    }
 #pragma unroll
     for (int sub = 0; sub < kTile / kSub; ++sub) {
-      if (!has_rows || key0 + sub * kSub >= L) break;
-      const unsigned char* krow = ktile + (size_t)(sub * kSub + (lane & 31)) * Lay::kRowStride;
-      floatx16_t acc = {};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = MF::mma(MF::load(krow, s, lane), qf[s], acc);
-      // acc[r]: key sub*32 + acc_row(r, lane), row = lane % 32
+      if (key0 + sub * kSub >= L) break;
+      const floatx16_t acc = logits_t(sub);
       if (key0 + sub * kSub + kSub <= L) {
-        // every key present: the scale is positive, so the maximum of the
-        // raw logits scales to the maximum of the scaled ones; one fma and
-        // one hardware exp2 per key (a term below 2^-126 of the running
-        // maximum is flushed to 0, which the sum of at least 1 cannot see)
-        float mx = acc[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-        const float m_new = fmaxf(run_m, mx * scale2);
-        float sum = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -m_new));
-        run_s = run_s * __builtin_amdgcn_exp2f(run_m - m_new) + sum;
-        run_m = m_new;
+        fold_full(acc);
       } else {
         float v[16];
         float mx = ninf;
