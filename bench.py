@@ -1,8 +1,9 @@
 """Benchmark of the BeaconKV eviction hot path on one MI355X.
 
 One step = one eviction period of the whole path over the full batch:
-  1. the cache grows back to L by the period's 128 decode steps (the length
-     array is reset; the 128 tail rows hold earlier, already-written keys),
+  1. the cache grows back to L by the period's 128 decode steps: fresh
+     synthetic K/V rows are copied into rows [B, L) (from a pre-generated
+     pool, never repeating a row still cached) and the length is reset,
   2. bkv_fps_update ingests the period's 128 pre-RoPE queries per query head
      (Continual FPS, shrinking buffers that fill),
   3. bkv_score selects beacons, rotates observation rows and scores every
@@ -14,12 +15,14 @@ Workload: all 36 layers of Qwen3-4B (32 query / 8 KV heads, d = 128) at batch
 16, bf16, evicting 2176 -> 2048 (window 32, 16 recent + 16 beacons, buffer
 128 -> 16), seeded synthetic data.  Inputs are resident in HBM before timing.
 
-Two schedules of the same passes are timed.  Serial: every stage on one
+Three schedules of the same passes are timed.  Serial: every stage on one
 stream, in order (stage times and the roofline come from it: each kernel runs
-alone).  Overlapped (the reported throughput): the ingest and beacon FPS of
-pass i + 1 run on a second stream while pass i scores, selects and compacts,
-as a decode loop would feed the buffers while the cache is being evicted;
-events keep every data dependency.
+alone).  Overlapped: the ingest and beacon FPS of pass i + 1 run on a second
+stream while pass i scores, selects and compacts, as a decode loop would feed
+the buffers while the cache is being evicted.  Pipelined (the reported
+throughput): as overlapped, with the slots in two groups whose scorings take
+turns, so one group compacts while the other scores.  Events keep every data
+dependency.
 
 Prints one JSON line (see the keys below).  --gpus N > 1 is refused: this
 build targets one GPU.
@@ -46,6 +49,8 @@ CFG = 3             # the benchmark workload (qwen3-4b-36layers-b16-B2048); 4 an
 POOL_MAX = 64       # distinct 128-step query blocks (0.6 GB each at the default workload) cycled over the steps
 POOL_BYTES = 60e9   # cap on the query-block pool of the larger workloads
 N_EVENTS = 240      # evictions in a 32K-token generation (first at L = 2176)
+APPEND_BLOCKS = 4   # pre-generated blocks of new tokens' K/V rows, appended at [B, L) before every pass
+APPEND_BYTES = 24e9 # cap on that pool (the largest workload holds two blocks)
 
 
 def kernel_source_hash() -> str:
@@ -93,6 +98,16 @@ class State:
         self.qcount = torch.zeros(N, Hq, dtype=torch.int32, device=dev)
         self.len_full = torch.full((N,), w.length, dtype=torch.int32, device=dev)
         self.length = self.len_full.clone()
+        # the tokens of every decode period are new: pass t writes fresh K/V rows at [B, L) (block t % P of
+        # the pool, the pool's slots rotated by t // P, so that no appended row repeats one still cached); a
+        # pass that only reset the length would find stale copies of earlier rows there, whose exact ties
+        # with their originals push every eviction to the tail and shrink the compaction pass by pass
+        n_new = w.length - w.budget
+        blk_bytes = 2 * N * Hkv * n_new * d * self.K.element_size()
+        self.n_append = max(2, min(APPEND_BLOCKS, int(APPEND_BYTES // blk_bytes)))
+        self.new_k = [syn.keys(max_len=n_new, block=1 + b) for b in range(self.n_append)]
+        self.new_v = [syn.values(max_len=n_new, block=1 + b) for b in range(self.n_append)]
+        self.pass_base = 0  # pass t = pass_base + i; advanced after every timed phase
         self.scores = torch.empty(N, Hkv, w.max_len, dtype=torch.float32, device=dev)
         self.kept = torch.empty(N, Hkv, w.budget, dtype=torch.int32, device=dev)
         now0 = w.length - 1
@@ -110,6 +125,22 @@ class State:
 
     def block(self, i):
         return (self.n_warm + i) % self.n_pool
+
+    def append_new_tokens(self, i, g):
+        """The decode period's new tokens: fresh K/V rows at [B, L) of group g's slots (enqueued on the current
+        stream)."""
+        w, N = self.w, self.N
+        t = self.pass_base + i
+        nk, nv = self.new_k[t % self.n_append], self.new_v[t % self.n_append]
+        rot = (t // self.n_append) % N
+        B, L = w.budget, w.length
+        s, e = g.sl.start, g.sl.stop
+        while s < e:
+            src = (s + rot) % N
+            n = min(e - s, N - src)
+            self.K[s:s + n, :, B:L].copy_(nk[src:src + n])
+            self.V[s:s + n, :, B:L].copy_(nv[src:src + n])
+            s += n
 
     def ingest(self, i, g, stream):
         w = self.w
@@ -167,7 +198,8 @@ HEAD_STAGES = ("grow", "fps_update", "beacon_picks", "score")
 class Schedule:
     """Enqueues eviction passes i = 0, 1, ... in order.
 
-    grow(i, g) resets the cache length of group g (and writes new positions),
+    grow(i, g) appends the decode period's new tokens to group g's slots and
+    resets their cache length (the hole-filling phase also writes positions),
     tail(i, rec, g) selects and compacts it; both run on the group's main
     stream.  Serial: one group (every slot) and one stream; ingest and scoring
     (beacon FPS included) of pass i run there too, in order.  Overlapped: a
@@ -189,8 +221,11 @@ class Schedule:
         self.st, self.grow, self.tail, self.overlap = st, grow, tail, overlap
         self.tail_stages = tail_stages
         assert overlap or groups == 1
-        # group 0 runs on the current stream, every other group on a stream of its own; one side stream serves
-        # all groups (few streams: the device has only a few hardware queues per process)
+        # serial: the current stream.  Overlapped: every group on a stream of its own and one side stream for
+        # all groups, all taken from torch's pool in a row, none of them the current (default) stream: a process
+        # has only four hardware queues, and a stream that shares one with another busy stream is serialised
+        # behind it (measured: successive schedules that left group 0 on the default stream alternated between
+        # about 3.0 and 3.5 ms per pass as the pool handed out streams on other queues)
         cur = torch.cuda.current_stream()
         side = torch.cuda.Stream() if overlap else None
         bounds = [st.N * k // groups for k in range(groups + 1)]
@@ -198,7 +233,7 @@ class Schedule:
         for k in range(groups):
             a, b = bounds[k], bounds[k + 1]
             ws = st.ws if groups == 1 else st.group_workspace((a, b))
-            self.groups.append(Group(st, a, b, ws, cur if k == 0 else torch.cuda.Stream(), side))
+            self.groups.append(Group(st, a, b, ws, torch.cuda.Stream() if overlap else cur, side))
         # the new streams start after everything already enqueued on the current one
         for s in {g.main for g in self.groups} | ({side} if side is not None else set()):
             if s != cur:
@@ -297,6 +332,7 @@ def timed_passes(sched, warmup, steps):
         assert status == 0, "device status %d" % status
     rows_moved = sum(bkv.ws_rows_moved(ws) for ws in sched.workspaces)
     stage_ms = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in evs[0]}
+    sched.st.pass_base += warmup + steps  # the next phase appends other new tokens
     return elapsed, stage_ms, spread(evs, sched), rows_moved
 
 
@@ -328,6 +364,7 @@ def time_hole_fill(st, warmup, steps, overlap, groups=1):
 
     def grow(i, g):
         st.length[g.sl].copy_(st.len_full[g.sl])
+        st.append_new_tokens(i, g)
         pos[g.sl, :, B:L].copy_(fresh[i % len(fresh)][g.sl] + new_rows * len(fresh) * (i // len(fresh)))
 
     def tail(i, rec, g):
@@ -735,6 +772,7 @@ def main():
 
     def grow(i, g):
         st.length[g.sl].copy_(st.len_full[g.sl])
+        st.append_new_tokens(i, g)
 
     def tail(i, rec, g):
         rec("select", 0)

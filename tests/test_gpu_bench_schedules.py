@@ -2,7 +2,8 @@
 Qwen3-4B, cache 2176 -> 2048), in the launch configurations bench.py
 times: two eviction passes run serially (one stream) and pipelined (two slot
 groups with their own workspaces and streams, ingest and beacon FPS of the
-next pass on a side stream) leave bit-identical caches, scores and kept
+next pass on a side stream), each appending the period's new tokens first,
+leave bit-identical caches, scores and kept
 indices.  Together with the full-size oracle checks of the single-call path,
 this ties the reported throughput to results the oracle vouches for."""
 import pytest
@@ -19,6 +20,7 @@ def _run(bench, st, groups, passes):
 
     def grow(i, g):
         st.length[g.sl].copy_(st.len_full[g.sl])
+        st.append_new_tokens(i, g)
 
     def tail(i, rec, g):
         rec("select", 0)
@@ -79,6 +81,7 @@ def test_hole_fill_serial_and_pipelined_agree_at_full_size():
     def run(groups):
         def grow(i, g):
             st.length[g.sl].copy_(st.len_full[g.sl])
+            st.append_new_tokens(i, g)
             pos[g.sl, :, B:L].copy_(torch.arange(L - B, dtype=torch.int32, device=dev) + w.max_len + (L - B) * i)
 
         def tail(i, rec, g):
@@ -105,3 +108,50 @@ def test_hole_fill_serial_and_pipelined_agree_at_full_size():
         a, b = getattr(st, k), ref[k]
         assert torch.equal(_bits(a) if a.is_floating_point() else a, _bits(b) if b.is_floating_point() else b), k
     assert torch.equal(pos, ref_pos)
+
+
+def test_bench_appends_fresh_tokens():
+    """Every pass appends fresh tokens at [B, L): after passes of the serial
+    schedule, the rows the next pass appends duplicate no row still cached in
+    [0, B), and nearly every kept row still moves.  A pass that only reset the
+    length would find stale copies of cached rows at [B, L); their exact ties
+    with the originals push the evictions to the tail, and the rows moved per
+    pass fell from 2029 to 1581 per unit within 320 passes that way."""
+    import bench
+
+    w = configs.get(3)
+    dev = torch.device("cuda:0")
+    st = bench.State(w, dev, n_pool=w.warm_steps // w.interval + 4)
+    B, L = w.budget, w.length
+
+    def grow(i, g):
+        st.length[g.sl].copy_(st.len_full[g.sl])
+        st.append_new_tokens(i, g)
+
+    def tail(i, rec, g):
+        rec("select", 0)
+        bkv.bkv_select(g.shape, st.scores[g.sl], st.length[g.sl], w.budget, w.window, st.kept[g.sl], g.ws)
+        rec("select", 1)
+        rec("compact", 0)
+        bkv.bkv_compact(g.shape, st.K[g.sl], st.V[g.sl], st.length[g.sl], w.budget, st.kept[g.sl], g.ws)
+        rec("compact", 1)
+
+    sched = bench.Schedule(st, grow, tail, False)
+    units = st.N * w.n_kv_heads
+    _, _, _, rows = bench.timed_passes(sched, 0, 12)
+    moved = rows / 12 / units / 2
+    assert moved > 1900, moved  # evictions spread over the cache: nearly every kept row moves
+    # the next pass's append, then exact duplicates between [0, B) and [B, L) by row hashes of the bits
+    st.append_new_tokens(0, sched.groups[0])
+    words = st.K.view(torch.int16).to(torch.int64)  # [N, Hkv, Lmax, d]
+    mult = torch.randint(1, 1 << 30, (w.head_dim,), device=dev, dtype=torch.int64) * 2 + 1
+    h = (words * mult).sum(-1)  # row hashes
+    old, new = h[:, :, :B], h[:, :, B:L]
+    dup = (new.unsqueeze(-1) == old.unsqueeze(-2)).any(-1)  # [N, Hkv, L - B]
+    confirmed = 0
+    for n, hk, j in dup.nonzero().tolist():  # equal hashes: compare the bits
+        for i in (old[n, hk] == new[n, hk, j]).nonzero().flatten().tolist():
+            confirmed += int(torch.equal(words[n, hk, i], words[n, hk, B + j]))
+    log("  rows moved per unit and pass %.1f; appended rows equal to a cached one: %d of %d"
+        % (moved, confirmed, dup.numel()))
+    assert confirmed == 0
