@@ -101,7 +101,7 @@ struct Mfma<BKV_F32, D> {
 // its LDS fragment reads) issued among the vector work of the previous
 // sub-tile: a product occupies the matrix core for 32 cycles, long enough
 // for about six vector instructions of the same wave.
-__device__ inline void interleave_products_with_exp() {
+__device__ inline void interleave_products_with_valu() {
   constexpr int kMfma = 0x008, kValu = 0x002, kDsRead = 0x100;
   __builtin_amdgcn_sched_group_barrier(kDsRead, 2, 0);
   __builtin_amdgcn_sched_group_barrier(kValu, 4, 0);
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
         floatx16_t next = cur;
         if (sub + 1 < kTile / kSub) next = logits_t(sub + 1);
         fold_full(cur);
-        if (sub + 1 < kTile / kSub) interleave_products_with_exp();
+        if (sub + 1 < kTile / kSub) interleave_products_with_valu();
         __builtin_amdgcn_sched_barrier(0);  // one sub-tile pair per scheduling region
         cur = next;
       }
@@ -459,6 +459,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
 
   // ---------------- pass 2: per-key max of (s - lse) ----------------
   float* out = scores + unit * (size_t)Lmax;
+  // S for key sub-tile `sub`: acc[r] is row 32 wave + acc_row(r, lane) of
+  // key sub*32 + lane % 32
+  auto logits = [&](int sub) {
+    const unsigned char* krow = ktile + (size_t)(sub * kSub + (lane & 31)) * Lay::kRowStride;
+    floatx16_t acc = {};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = MF::mma(qf[s], MF::load(krow, s, lane), acc);
+    return acc;
+  };
+  // the wave's rows folded per key into part[wave][key]
+  auto reduce_rows = [&](const floatx16_t& acc, int sub) {
+    float t;
+    if constexpr (kMean) {  // sum of the rows' probabilities (absent rows: lse +inf, probability 0)
+      t = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -lse_r[r]));
+      t += __shfl_xor(t, 32, 64);
+    } else {  // maximum of the rows' log2-probabilities
+      t = ninf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t = fmaxf(t, fmaf(acc[r], scale2, -lse_r[r]));
+      t = fmaxf(t, __shfl_xor(t, 32, 64));
+    }
+    if (lane < 32) part[wave * kTile + sub * kSub + lane] = t;
+  };
   prefetch(ntiles - 1);
   for (int tile = ntiles - 1; tile >= 0; --tile) {
     __syncthreads();
@@ -466,26 +491,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
     __syncthreads();
     if (tile > 0) prefetch(tile - 1);
     const int key0 = tile * kTile;
+    if (has_rows && key0 + kTile <= L) {
+      // a full tile: products of sub-tile sub + 1 among the reduction of sub
+      floatx16_t cur = logits(0);
 #pragma unroll
-    for (int sub = 0; sub < kTile / kSub; ++sub) {
-      if (!has_rows || key0 + sub * kSub >= L) break;
-      const unsigned char* krow = ktile + (size_t)(sub * kSub + (lane & 31)) * Lay::kRowStride;
-      floatx16_t acc = {};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = MF::mma(qf[s], MF::load(krow, s, lane), acc);
-      float t;
-      if constexpr (kMean) {  // sum of the rows' probabilities (absent rows: lse +inf, probability 0)
-        t = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -lse_r[r]));
-        t += __shfl_xor(t, 32, 64);
-      } else {  // maximum of the rows' log2-probabilities
-        t = ninf;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t = fmaxf(t, fmaf(acc[r], scale2, -lse_r[r]));
-        t = fmaxf(t, __shfl_xor(t, 32, 64));
+      for (int sub = 0; sub < kTile / kSub; ++sub) {
+        floatx16_t next = cur;
+        if (sub + 1 < kTile / kSub) next = logits(sub + 1);
+        reduce_rows(cur, sub);
+        if (sub + 1 < kTile / kSub) interleave_products_with_valu();
+        __builtin_amdgcn_sched_barrier(0);
+        cur = next;
       }
-      if (lane < 32) part[wave * kTile + sub * kSub + lane] = t;
+    } else if (has_rows) {
+#pragma unroll
+      for (int sub = 0; sub < kTile / kSub; ++sub) {
+        if (key0 + sub * kSub >= L) break;
+        reduce_rows(logits(sub), sub);
+      }
     }
     __syncthreads();
     for (int k = tid; k < kTile; k += nthreads) {
