@@ -20,7 +20,7 @@ stream, in order (stage times and the roofline come from it: each kernel runs
 alone).  Overlapped: the ingest and beacon FPS of pass i + 1 run on a second
 stream while pass i scores, selects and compacts, as a decode loop would feed
 the buffers while the cache is being evicted.  Pipelined (the reported
-throughput): as overlapped, with the slots in two groups whose scorings take
+throughput): as overlapped, with the slots in three groups whose scorings take
 turns, so one group compacts while the other scores.  Events keep every data
 dependency.
 
@@ -734,7 +734,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--no-hole-fill", action="store_true", help="skip the hole-filling layout phase")
     ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped and pipelined schedules")
-    ap.add_argument("--groups", type=int, default=2, help="slot groups of the pipelined schedule")
+    ap.add_argument("--groups", type=int, default=3, help="slot groups of the pipelined schedule")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-all-cores", action="store_true", help="skip the all-host-threads oracle timing")
     ap.add_argument("--workload", type=int, default=CFG, choices=(3, 4, 5),
