@@ -1,6 +1,6 @@
 """The benchmark's schedules at its full workload size (576 slots of
 Qwen3-4B, cache 2176 -> 2048), in the launch configurations bench.py
-times: two eviction passes run serially (one stream) and pipelined (two slot
+times: two eviction passes run serially (one stream) and pipelined (three slot
 groups with their own workspaces and streams, ingest and beacon FPS of the
 next pass on a side stream), each appending the period's new tokens first,
 leave bit-identical caches, scores and kept
@@ -56,7 +56,7 @@ def test_serial_and_pipelined_passes_agree_at_full_size():
     st.scores.zero_()
     st.kept.fill_(-7)
     torch.cuda.synchronize()  # the restored state is in place before other streams start on it
-    _run(bench, st, 2, 2)  # pipelined, two slot groups
+    _run(bench, st, 3, 2)  # pipelined, three slot groups (the bench default)
     for k in ("K", "V", "scores", "kept", "length"):
         a, b = getattr(st, k), ref[k]
         if k == "scores":
@@ -103,7 +103,7 @@ def test_hole_fill_serial_and_pipelined_agree_at_full_size():
     pos.copy_(pos0)
     st.kept.fill_(-7)
     torch.cuda.synchronize()
-    run(2)
+    run(3)
     for k in ("K", "V", "kept", "length"):
         a, b = getattr(st, k), ref[k]
         assert torch.equal(_bits(a) if a.is_floating_point() else a, _bits(b) if b.is_floating_point() else b), k
