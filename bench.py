@@ -73,6 +73,23 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def append_plan(t: int, n_blocks: int, N: int, a: int, e: int):
+    """Copies that give slots [a, e) their new tokens of pass t: slot s takes
+    slot (s + r) % N of pool block t % n_blocks, r = (t // n_blocks) % N, so a
+    (block, rotation) pair comes back only after n_blocks * N passes.  Returns
+    (first destination slot, first source slot, count) runs of contiguous
+    slots."""
+    rot = (t // n_blocks) % N
+    runs = []
+    s = a
+    while s < e:
+        src = (s + rot) % N
+        n = min(e - s, N - src)
+        runs.append((s, src, n))
+        s += n
+    return runs
+
+
 class State:
     """Device-resident state of the metric workload."""
 
@@ -129,18 +146,13 @@ class State:
     def append_new_tokens(self, i, g):
         """The decode period's new tokens: fresh K/V rows at [B, L) of group g's slots (enqueued on the current
         stream)."""
-        w, N = self.w, self.N
+        w = self.w
         t = self.pass_base + i
         nk, nv = self.new_k[t % self.n_append], self.new_v[t % self.n_append]
-        rot = (t // self.n_append) % N
         B, L = w.budget, w.length
-        s, e = g.sl.start, g.sl.stop
-        while s < e:
-            src = (s + rot) % N
-            n = min(e - s, N - src)
-            self.K[s:s + n, :, B:L].copy_(nk[src:src + n])
-            self.V[s:s + n, :, B:L].copy_(nv[src:src + n])
-            s += n
+        for dst, src, n in append_plan(t, self.n_append, self.N, g.sl.start, g.sl.stop):
+            self.K[dst:dst + n, :, B:L].copy_(nk[src:src + n])
+            self.V[dst:dst + n, :, B:L].copy_(nv[src:src + n])
 
     def ingest(self, i, g, stream):
         w = self.w

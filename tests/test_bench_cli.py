@@ -1,5 +1,7 @@
 """bench.py's host-side contract, checked without a GPU: more than one GPU
-is refused with a message, before anything touches a device."""
+is refused with a message, before anything touches a device; the kernel
+source hash ignores comments; the new-token appends give every slot its
+rotated source slot."""
 import os
 import subprocess
 import sys
@@ -33,3 +35,29 @@ def test_kernel_source_hash_ignores_comments(tmp_path, monkeypatch):
             "// a comment\n\n/* and a\n block */\n" + text.replace("\n", "  // note\n", 3), encoding="utf-8")
     monkeypatch.setattr(bench, "ROOT", str(fake_root))
     assert bench.kernel_source_hash() == h
+
+
+def test_append_plan_gives_every_slot_its_rotated_source():
+    """bench.py's new-token appends: slot s of a group gets source slot
+    (s + r) % N of the pass's pool block, in contiguous runs, and the
+    (block, rotation) pair of a pass repeats only after n_blocks * N passes."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    N, P = 7, 3
+    seen = set()
+    for t in range(P * N):
+        rot = (t // P) % N
+        seen.add((t % P, rot))
+        for a, e in [(0, N), (2, 5), (4, 7), (3, 3)]:
+            runs = bench.append_plan(t, P, N, a, e)
+            got = {}
+            for dst, src, n in runs:
+                assert n >= 1 and src + n <= N and dst + n <= e
+                for k in range(n):
+                    got[dst + k] = src + k
+            assert got == {s: (s + rot) % N for s in range(a, e)}, (t, a, e, runs)
+            assert len(runs) <= 2  # one wrap at most
+    assert len(seen) == P * N
