@@ -26,13 +26,14 @@ F32 = 0
 BF16 = 1
 
 
+BUILD_FLAGS = ("-O2", "-std=c11", "-fPIC", "-shared")  # gcc; no fast-math, no vectorisation flags
+
+
 def build(force: bool = False) -> str:
-    """Compile liboracle.so with gcc (-O2, no fast-math)."""
+    """Compile liboracle.so with gcc (BUILD_FLAGS)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
-        )
+        subprocess.check_call(["gcc", *BUILD_FLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -71,6 +72,10 @@ def lib():
         L.orc_score_given.restype = I
         L.orc_decode_attention.argtypes = [I, I, I, P, P, I, P, P, P]
         L.orc_decode_attention.restype = None
+        L.orc_capture_step.argtypes = [I, I, I, P, I, P, P]
+        L.orc_capture_step.restype = None
+        L.orc_score_capture.argtypes = [I, I, I, P, I, P, P, I, I, LONG, D, P, P]
+        L.orc_score_capture.restype = I
         L.orc_select.argtypes = [P, I, I, I, P]
         L.orc_select.restype = I
         L.orc_compact.argtypes = [P, LONG, P, I]
@@ -307,6 +312,41 @@ def decode_attention(K: np.ndarray, V: np.ndarray, L: int, q: np.ndarray):
     probs = np.zeros((G, max(L, 1)), dtype=np.float64)
     lib().orc_decode_attention(dt, d, G, _ptr(K), _ptr(V), L, _ptr(q), _ptr(probs), _ptr(out))
     return out, probs[:, :L].copy()
+
+
+def capture_step(K: np.ndarray, L: int, q: np.ndarray, capture: np.ndarray) -> None:
+    """Folds one decode step into a KV head's capture, in place: capture[j] =
+    max(capture[j], max_g p_g(j)) for j < L.  q [G, d] storage (rotated), K
+    [>=L, d] storage, capture float64 [>=L]."""
+    K = np.ascontiguousarray(K)
+    q = np.ascontiguousarray(q)
+    assert capture.dtype == np.float64 and capture.flags["C_CONTIGUOUS"] and capture.shape[0] >= L
+    G, d = q.shape
+    dt = dtype_code(K)
+    assert dtype_code(q) == dt
+    lib().orc_capture_step(dt, d, G, _ptr(K), L, _ptr(q), _ptr(capture))
+
+
+def score_capture(K: np.ndarray, L: int, qbuf: np.ndarray, qcount: np.ndarray, nb: int, pos_now: int, theta: float,
+                  capture: np.ndarray) -> np.ndarray:
+    """Eviction scores of one KV head from its beacon rows (FPS of the
+    buffers, rotated to pos_now) raised to the captured recent maxima.
+    qbuf [G, C, d] storage; qcount [G]; capture float64 [>=L].  Returns
+    float64 [L]."""
+    K = np.ascontiguousarray(K)
+    qbuf = np.ascontiguousarray(qbuf)
+    qc = np.ascontiguousarray(qcount, dtype=np.int32)
+    cap = np.ascontiguousarray(capture, dtype=np.float64)
+    assert cap.shape[0] >= L
+    G, C, d = qbuf.shape
+    dt = dtype_code(K)
+    assert dtype_code(qbuf) == dt
+    scores = np.zeros(max(L, 1), dtype=np.float64)
+    rc = lib().orc_score_capture(dt, d, G, _ptr(K), L, _ptr(qbuf), _ptr(qc), C, nb, int(pos_now), float(theta),
+                                 _ptr(cap), _ptr(scores))
+    if rc != 0:
+        raise ValueError("oracle score_capture rejected a query count")
+    return scores[:L].copy()
 
 
 def score(K, lens, recent, recent_pos, qbuf, qcount, nb, pos_now, theta, units=None):

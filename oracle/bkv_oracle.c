@@ -610,8 +610,9 @@ int orc_score_given(int dtype, int d, int G, const void *K, int L, const void *r
  * Layouts: K, V [L][d] storage; q [G][d] storage.  probs [G][L] (binary64,
  * optional), out [G][d] (binary64).  L = 0 gives out = 0.
  */
-void orc_decode_attention(int dtype, int d, int G, const void *K, const void *V, int L, const void *q,
-                          double *probs, double *out) {
+/* step_probs: p_g(j) = softmax_j(q_g . k_j / sqrt(d)) over the L keys, for
+ * the G rows of q, in binary64 (probs [G][L]). */
+static void step_probs(int dtype, int d, int G, const void *K, int L, const void *q, double *probs) {
   double *qg = (double *)malloc(sizeof(double) * d);
   double *kj = (double *)malloc(sizeof(double) * d);
   double *s = (double *)malloc(sizeof(double) * (L > 0 ? L : 1));
@@ -626,16 +627,65 @@ void orc_decode_attention(int dtype, int d, int G, const void *K, const void *V,
     }
     double sum = 0.0;
     for (int j = 0; j < L; ++j) sum += exp(s[j] - mx);
-    for (int t = 0; t < d; ++t) out[(size_t)g * d + t] = 0.0;
-    for (int j = 0; j < L; ++j) {
-      double p = exp(s[j] - mx) / sum;
-      if (probs) probs[(size_t)g * L + j] = p;
-      for (int t = 0; t < d; ++t) out[(size_t)g * d + t] += p * orc_load(V, dtype, (long)j * d + t);
-    }
+    for (int j = 0; j < L; ++j) probs[(size_t)g * L + j] = exp(s[j] - mx) / sum;
   }
   free(qg);
   free(kj);
   free(s);
+}
+
+void orc_decode_attention(int dtype, int d, int G, const void *K, const void *V, int L, const void *q,
+                          double *probs, double *out) {
+  double *p = (double *)malloc(sizeof(double) * (size_t)G * (L > 0 ? L : 1));
+  step_probs(dtype, d, G, K, L, q, p);
+  for (int g = 0; g < G; ++g) {
+    for (int t = 0; t < d; ++t) out[(size_t)g * d + t] = 0.0;
+    for (int j = 0; j < L; ++j) {
+      double pj = p[(size_t)g * L + j];
+      if (probs) probs[(size_t)g * L + j] = pj;
+      for (int t = 0; t < d; ++t) out[(size_t)g * d + t] += pj * orc_load(V, dtype, (long)j * d + t);
+    }
+  }
+  free(p);
+}
+
+/*
+ * orc_capture_step: folds one decode step of the G query heads of a KV head
+ * into the recent-query capture (reading R24).  [WZ, 信标查询怎么用]: a key's
+ * score takes the largest attention any recent query (or beacon) gives it;
+ * a recent query's attention is the one of its own decode step, over the L
+ * keys present at that step.  capture[j] = max(capture[j], max_g p_g(j)) for
+ * j < L; entries at or beyond L are left as they were (the step gives them
+ * probability 0).  The caller zeroes the capture where the recent window
+ * starts.  q [G][d] storage rows, already rotated at the step's position.
+ */
+void orc_capture_step(int dtype, int d, int G, const void *K, int L, const void *q, double *capture) {
+  double *p = (double *)malloc(sizeof(double) * (size_t)G * (L > 0 ? L : 1));
+  step_probs(dtype, d, G, K, L, q, p);
+  for (int j = 0; j < L; ++j)
+    for (int g = 0; g < G; ++g)
+      if (p[(size_t)g * L + j] > capture[j]) capture[j] = p[(size_t)g * L + j];
+  free(p);
+}
+
+/*
+ * orc_score_capture: the eviction score of one KV head when the recent
+ * queries' attention was captured during decoding (reading R24): the
+ * beacon rows alone are scored at eviction time ([WZ, 信标和最近查询该怎么分配]
+ * puts the extra cost of scoring in the beacons' attention), exactly as
+ * orc_score_unit with no recent rows, and each key's score is then the larger
+ * of that beacon score and its captured value: the maximum over the beacon
+ * rows and the captured recent steps, as [WZ, 信标查询怎么用] aggregates.
+ * Layouts as orc_score_unit; capture [L] (binary64).  Returns 0, or -1 for an
+ * invalid qcount.
+ */
+int orc_score_capture(int dtype, int d, int G, const void *K, int L, const void *qbuf, const int *qcount, int C,
+                      int nb, long pos_now, double theta, const double *capture, double *scores) {
+  int status = orc_score_unit(dtype, d, G, K, L, NULL, NULL, 0, qbuf, qcount, C, nb, pos_now, theta, scores, NULL,
+                              NULL, NULL);
+  for (int j = 0; j < L; ++j)
+    if (capture[j] > scores[j]) scores[j] = capture[j];
+  return status;
 }
 
 /* ------------------------------------------------------------------------ */

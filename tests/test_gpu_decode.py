@@ -114,7 +114,7 @@ def test_captured_recent_steps_plus_beacons_equal_oracle(cfg):
     bkv.bkv_score_picked_capture(g.shape, inp.K, length, capture, w.n_beacons, g.pos_now, w.rope_theta, scores, ws0)
     torch.cuda.synchronize()
     assert bkv.bkv_read_device_status(ws0) == 0
-    Kh, Vh = synth.to_numpy_storage(inp.K), synth.to_numpy_storage(inp.V)
+    Kh = synth.to_numpy_storage(inp.K)
     qh = [synth.to_numpy_storage(x) for x in qs]
     got = scores.cpu().numpy()
     G = w.group
@@ -122,14 +122,9 @@ def test_captured_recent_steps_plus_beacons_equal_oracle(cfg):
         for h in range(w.n_kv_heads):
             cap = np.zeros(L_end)
             for t in range(R):
-                Lt = L0 + t + 1
-                _, p = oracle.decode_attention(Kh[n, h], Vh[n, h], Lt, qh[t][n, h * G:(h + 1) * G])
-                cap[:Lt] = np.maximum(cap[:Lt], p.max(axis=0))
-            sb, _, _, _ = oracle.score_unit(Kh[n, h], L_end, np.zeros((G, 0, w.head_dim), Kh.dtype),
-                                            np.zeros(0, np.int32), o.qbuf[n, h * G:(h + 1) * G],
-                                            o.qcount[n, h * G:(h + 1) * G], w.n_beacons, int(inp.pos_now[n]),
-                                            w.rope_theta)
-            want = np.maximum(cap, sb)
+                oracle.capture_step(Kh[n, h], L0 + t + 1, qh[t][n, h * G:(h + 1) * G], cap)
+            want = oracle.score_capture(Kh[n, h], L_end, o.qbuf[n, h * G:(h + 1) * G], o.qcount[n, h * G:(h + 1) * G],
+                                        w.n_beacons, int(inp.pos_now[n]), w.rope_theta, cap)
             err = np.abs(got[n, h, :L_end] - want)
             assert np.all(err <= RTOL * want + 1e-30), (n, h, float(np.max(err / want)))
     log("  capture + beacons: %d units" % (N * w.n_kv_heads))
