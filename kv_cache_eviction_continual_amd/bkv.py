@@ -141,12 +141,70 @@ def _check(status: int) -> None:
         raise BkvError(status, load().bkv_status_string(status).decode())
 
 
-def _ptr(t):
+def _storage_dtype(shape: Shape):
+    return torch.bfloat16 if shape.dtype == BF16 else torch.float32 if shape.dtype == F32 else None
+
+
+def _count(*dims) -> int:
+    n = 1
+    for x in dims:
+        n *= max(0, int(x))
+    return n
+
+
+class _Arg:
+    """A tensor argument that passed the structural checks of _dev."""
+
+    __slots__ = ("t", "name")
+
+    def __init__(self, t, name):
+        self.t, self.name = t, name
+
+
+def _dev(t, name: str, dtype, numel: int, optional: bool = False):
+    """Tensor argument `name` after the checks the C ABI cannot make: a
+    dense tensor of the element type the header states, holding at least the
+    `numel` elements the call will touch.  None stays None (NULL) when the
+    argument is optional; the library then checks whether the call needs it.
+    Where it lives is checked by _on_gpu, once every argument has passed
+    these checks."""
     if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    return t.data_ptr()
+        if optional:
+            return None
+        raise ValueError("%s: a tensor is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch.Tensor, got %s" % (name, type(t).__name__))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous (dense row-major)" % name)
+    if t.numel() < numel:
+        raise ValueError("%s: holds %d elements, the call needs %d" % (name, t.numel(), numel))
+    return _Arg(t, name)
+
+
+def _ws(ws, name: str = "ws"):
+    """A workspace argument: a dense uint8 tensor (its size and alignment are
+    checked by the library, which receives its byte count)."""
+    return _dev(ws, name, torch.uint8, 0)
+
+
+def _on_gpu(*args):
+    """Device pointers of checked arguments (None for NULL), each on the
+    current GPU."""
+    out = []
+    for a in args:
+        if a is None:
+            out.append(None)
+            continue
+        t = a.t
+        if not t.is_cuda:
+            raise ValueError("%s: must be on the GPU, got device %s" % (a.name, t.device))
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError("%s: on %s, but the current device is cuda:%d" % (a.name, t.device,
+                                                                              torch.cuda.current_device()))
+        out.append(t.data_ptr())
+    return out
 
 
 def _stream(stream):
@@ -184,72 +242,126 @@ def bkv_workspace_layout(shape: Shape, R: int, nb: int):
     return [int(o) for o in offs]
 
 
+def _nbytes(ws) -> int:
+    return ws.numel()  # uint8: one byte per element
+
+
 def bkv_fps_update(shape: Shape, q_new, T: int, qbuf, qcount, C: int, M: int, ws, stream=None) -> None:
-    _check(load().bkv_fps_update(ctypes.byref(shape), _ptr(q_new), T, _ptr(qbuf), _ptr(qcount), C, M, _ptr(ws),
-                                 ws.numel() * ws.element_size(), _stream(stream)))
+    N, Hq, d, st = shape.n_seq, shape.n_q_heads, shape.head_dim, _storage_dtype(shape)
+    qn, qb, qc, w = _on_gpu(_dev(q_new, "q_new", st, _count(N, Hq, T, d), optional=T <= 0),
+                            *_buffers(shape, qbuf, qcount, C), _ws(ws))
+    _check(load().bkv_fps_update(ctypes.byref(shape), qn, T, qb, qc, C, M, w, _nbytes(ws), _stream(stream)))
+
+
+def _score_common(shape: Shape, K, length, recent, recent_pos, R: int, pos_now, scores):
+    """The arguments every scoring call shares, checked."""
+    N, Hkv, Hq, d, Lmax, st = (shape.n_seq, shape.n_kv_heads, shape.n_q_heads, shape.head_dim, shape.max_len,
+                               _storage_dtype(shape))
+    return (_dev(K, "K", st, _count(N, Hkv, Lmax, d)), _dev(length, "len", torch.int32, _count(N)),
+            _dev(recent, "recent", st, _count(N, Hq, R, d), optional=R <= 0),
+            _dev(recent_pos, "recent_pos", torch.int32, _count(N, R), optional=R <= 0),
+            _dev(pos_now, "pos_now", torch.int32, _count(N)),
+            _dev(scores, "scores", torch.float32, _count(N, Hkv, Lmax)))
+
+
+def _buffers(shape: Shape, qbuf, qcount, C: int):
+    N, Hq, d = shape.n_seq, shape.n_q_heads, shape.head_dim
+    return (_dev(qbuf, "qbuf", _storage_dtype(shape), _count(N, Hq, C, d)),
+            _dev(qcount, "qcount", torch.int32, _count(N, Hq)))
 
 
 def bkv_score(shape: Shape, K, length, recent, recent_pos, R: int, qbuf, qcount, C: int, nb: int, pos_now,
               rope_theta: float, scores, ws, stream=None) -> None:
-    _check(load().bkv_score(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos), R,
-                            _ptr(qbuf), _ptr(qcount), C, nb, _ptr(pos_now), float(rope_theta), _ptr(scores),
-                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    k, ln, rc, rp, pn, sc, qb, qc, w = _on_gpu(*_score_common(shape, K, length, recent, recent_pos, R, pos_now, scores),
+                                               *_buffers(shape, qbuf, qcount, C), _ws(ws))
+    _check(load().bkv_score(ctypes.byref(shape), k, ln, rc, rp, R, qb, qc, C, nb, pn, float(rope_theta), sc, w,
+                            _nbytes(ws), _stream(stream)))
 
 
 def bkv_beacon_picks(shape: Shape, qbuf, qcount, C: int, R: int, nb: int, ws, stream=None) -> None:
-    _check(load().bkv_beacon_picks(ctypes.byref(shape), _ptr(qbuf), _ptr(qcount), C, R, nb, _ptr(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)))
+    qb, qc, w = _on_gpu(*_buffers(shape, qbuf, qcount, C), _ws(ws))
+    _check(load().bkv_beacon_picks(ctypes.byref(shape), qb, qc, C, R, nb, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_score_picked(shape: Shape, K, length, recent, recent_pos, R: int, nb: int, pos_now, rope_theta: float,
                      scores, ws, stream=None) -> None:
-    _check(load().bkv_score_picked(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos), R,
-                                   nb, _ptr(pos_now), float(rope_theta), _ptr(scores), _ptr(ws),
-                                   ws.numel() * ws.element_size(), _stream(stream)))
+    k, ln, rc, rp, pn, sc, w = _on_gpu(*_score_common(shape, K, length, recent, recent_pos, R, pos_now, scores),
+                                       _ws(ws))
+    _check(load().bkv_score_picked(ctypes.byref(shape), k, ln, rc, rp, R, nb, pn, float(rope_theta), sc, w,
+                                   _nbytes(ws), _stream(stream)))
 
 
 def bkv_score_picked_agg(shape: Shape, K, length, recent, recent_pos, R: int, nb: int, pos_now, rope_theta: float,
                          aggregation: int, scores, ws, stream=None) -> None:
-    _check(load().bkv_score_picked_agg(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(recent), _ptr(recent_pos),
-                                       R, nb, _ptr(pos_now), float(rope_theta), int(aggregation), _ptr(scores),
-                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    k, ln, rc, rp, pn, sc, w = _on_gpu(*_score_common(shape, K, length, recent, recent_pos, R, pos_now, scores),
+                                       _ws(ws))
+    _check(load().bkv_score_picked_agg(ctypes.byref(shape), k, ln, rc, rp, R, nb, pn, float(rope_theta),
+                                       int(aggregation), sc, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_beacon_rows(shape: Shape, src, S: int, idx, R: int, nb: int, ws, stream=None) -> None:
-    _check(load().bkv_beacon_rows(ctypes.byref(shape), _ptr(src), S, _ptr(idx), R, nb, _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream)))
+    N, Hq, d = shape.n_seq, shape.n_q_heads, shape.head_dim
+    sr, ix, w = _on_gpu(_dev(src, "src", _storage_dtype(shape), _count(N, Hq, S, d), optional=S <= 0 or nb <= 0),
+                        _dev(idx, "idx", torch.int32, _count(N, Hq, nb), optional=nb <= 0), _ws(ws))
+    _check(load().bkv_beacon_rows(ctypes.byref(shape), sr, S, ix, R, nb, w, _nbytes(ws), _stream(stream)))
+
+
+def _select_common(shape: Shape, scores, length, budget: int, kept):
+    N, Hkv, Lmax = shape.n_seq, shape.n_kv_heads, shape.max_len
+    return (_dev(scores, "scores", torch.float32, _count(N, Hkv, Lmax)), _dev(length, "len", torch.int32, _count(N)),
+            _dev(kept, "kept", torch.int32, _count(N, Hkv, budget)))
+
+
+def _kv(shape: Shape, K, V):
+    n = _count(shape.n_seq, shape.n_kv_heads, shape.max_len, shape.head_dim)
+    st = _storage_dtype(shape)
+    return _dev(K, "K", st, n), _dev(V, "V", st, n)
+
+
+def _len_kept(shape: Shape, length, budget: int, kept):
+    return (_dev(length, "len", torch.int32, _count(shape.n_seq)),
+            _dev(kept, "kept", torch.int32, _count(shape.n_seq, shape.n_kv_heads, budget)))
+
+
+def _positions(shape: Shape, pos):
+    return _dev(pos, "pos", torch.int32, _count(shape.n_seq, shape.n_kv_heads, shape.max_len))
 
 
 def bkv_select(shape: Shape, scores, length, budget: int, window: int, kept, ws, stream=None) -> None:
-    _check(load().bkv_select(ctypes.byref(shape), _ptr(scores), _ptr(length), budget, window, _ptr(kept), _ptr(ws),
-                             ws.numel() * ws.element_size(), _stream(stream)))
+    sc, ln, kp, w = _on_gpu(*_select_common(shape, scores, length, budget, kept), _ws(ws))
+    _check(load().bkv_select(ctypes.byref(shape), sc, ln, budget, window, kp, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_compact(shape: Shape, K, V, length, budget: int, kept, ws, stream=None) -> None:
-    _check(load().bkv_compact(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(length), budget, _ptr(kept), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(stream)))
+    k, v, ln, kp, w = _on_gpu(*_kv(shape, K, V), *_len_kept(shape, length, budget, kept), _ws(ws))
+    _check(load().bkv_compact(ctypes.byref(shape), k, v, ln, budget, kp, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_select_compact(shape: Shape, scores, K, V, length, budget: int, window: int, kept, ws, stream=None) -> None:
-    _check(load().bkv_select_compact(ctypes.byref(shape), _ptr(scores), _ptr(K), _ptr(V), _ptr(length), budget,
-                                     window, _ptr(kept), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    sc, ln, kp, k, v, w = _on_gpu(*_select_common(shape, scores, length, budget, kept), *_kv(shape, K, V), _ws(ws))
+    _check(load().bkv_select_compact(ctypes.byref(shape), sc, k, v, ln, budget, window, kp, w, _nbytes(ws),
+                                     _stream(stream)))
 
 
 def bkv_select_fill(shape: Shape, scores, pos, length, budget: int, window: int, kept, ws, stream=None) -> None:
-    _check(load().bkv_select_fill(ctypes.byref(shape), _ptr(scores), _ptr(pos), _ptr(length), budget, window,
-                                  _ptr(kept), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    sc, ln, kp, ps, w = _on_gpu(*_select_common(shape, scores, length, budget, kept), _positions(shape, pos),
+                                _ws(ws))
+    _check(load().bkv_select_fill(ctypes.byref(shape), sc, ps, ln, budget, window, kp, w, _nbytes(ws),
+                                  _stream(stream)))
 
 
 def bkv_compact_fill(shape: Shape, K, V, pos, length, budget: int, kept, ws, stream=None) -> None:
-    _check(load().bkv_compact_fill(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(pos), _ptr(length), budget,
-                                   _ptr(kept), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    k, v, ps, ln, kp, w = _on_gpu(*_kv(shape, K, V), _positions(shape, pos), *_len_kept(shape, length, budget, kept),
+                                  _ws(ws))
+    _check(load().bkv_compact_fill(ctypes.byref(shape), k, v, ps, ln, budget, kp, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_select_compact_fill(shape: Shape, scores, K, V, pos, length, budget: int, window: int, kept, ws,
                             stream=None) -> None:
-    _check(load().bkv_select_compact_fill(ctypes.byref(shape), _ptr(scores), _ptr(K), _ptr(V), _ptr(pos),
-                                          _ptr(length), budget, window, _ptr(kept), _ptr(ws),
-                                          ws.numel() * ws.element_size(), _stream(stream)))
+    sc, ln, kp, k, v, ps, w = _on_gpu(*_select_common(shape, scores, length, budget, kept), *_kv(shape, K, V),
+                                      _positions(shape, pos), _ws(ws))
+    _check(load().bkv_select_compact_fill(ctypes.byref(shape), sc, k, v, ps, ln, budget, window, kp, w, _nbytes(ws),
+                                          _stream(stream)))
 
 
 def bkv_decode_workspace_size(shape: Shape) -> int:
@@ -257,15 +369,22 @@ def bkv_decode_workspace_size(shape: Shape) -> int:
 
 
 def bkv_decode_attention(shape: Shape, q, K, V, length, out, capture, ws, stream=None) -> None:
-    _check(load().bkv_decode_attention(ctypes.byref(shape), _ptr(q), _ptr(K), _ptr(V), _ptr(length), _ptr(out),
-                                       _ptr(capture), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    N, Hkv, Hq, d, Lmax = shape.n_seq, shape.n_kv_heads, shape.n_q_heads, shape.head_dim, shape.max_len
+    qp, k, v, ln, op, cp, w = _on_gpu(_dev(q, "q", _storage_dtype(shape), _count(N, Hq, d)), *_kv(shape, K, V),
+                                      _dev(length, "len", torch.int32, _count(N)),
+                                      _dev(out, "out", torch.float32, _count(N, Hq, d)),
+                                      _dev(capture, "capture", torch.float32, _count(N, Hkv, Lmax), optional=True),
+                                      _ws(ws))
+    _check(load().bkv_decode_attention(ctypes.byref(shape), qp, k, v, ln, op, cp, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_score_picked_capture(shape: Shape, K, length, capture, nb: int, pos_now, rope_theta: float, scores, ws,
                              stream=None) -> None:
-    _check(load().bkv_score_picked_capture(ctypes.byref(shape), _ptr(K), _ptr(length), _ptr(capture), nb,
-                                           _ptr(pos_now), float(rope_theta), _ptr(scores), _ptr(ws),
-                                           ws.numel() * ws.element_size(), _stream(stream)))
+    N, Hkv, Lmax = shape.n_seq, shape.n_kv_heads, shape.max_len
+    k, ln, _, _, pn, sc, cp, w = _on_gpu(*_score_common(shape, K, length, None, None, 0, pos_now, scores),
+                                         _dev(capture, "capture", torch.float32, _count(N, Hkv, Lmax)), _ws(ws))
+    _check(load().bkv_score_picked_capture(ctypes.byref(shape), k, ln, cp, nb, pn, float(rope_theta), sc, w,
+                                           _nbytes(ws), _stream(stream)))
 
 
 def bkv_fps_full_workspace_size(shape: Shape, n: int) -> int:
@@ -273,8 +392,10 @@ def bkv_fps_full_workspace_size(shape: Shape, n: int) -> int:
 
 
 def bkv_fps_full(shape: Shape, hist, n: int, k: int, picks, ws, stream=None) -> None:
-    _check(load().bkv_fps_full(ctypes.byref(shape), _ptr(hist), n, k, _ptr(picks), _ptr(ws),
-                               ws.numel() * ws.element_size(), _stream(stream)))
+    N, Hq, d = shape.n_seq, shape.n_q_heads, shape.head_dim
+    hp, pk, w = _on_gpu(_dev(hist, "hist", _storage_dtype(shape), _count(N, Hq, n, d), optional=n <= 0),
+                        _dev(picks, "picks", torch.int32, _count(N, Hq, k), optional=k <= 0), _ws(ws))
+    _check(load().bkv_fps_full(ctypes.byref(shape), hp, n, k, pk, w, _nbytes(ws), _stream(stream)))
 
 
 def bkv_status_string(status: int) -> str:
@@ -283,12 +404,14 @@ def bkv_status_string(status: int) -> str:
 
 def bkv_read_device_status(ws, stream=None) -> int:
     out = ctypes.c_int32(0)
-    _check(load().bkv_read_device_status(_ptr(ws), ctypes.byref(out), _stream(stream)))
+    (w,) = _on_gpu(_ws(ws))
+    _check(load().bkv_read_device_status(w, ctypes.byref(out), _stream(stream)))
     return int(out.value)
 
 
 def bkv_reset_device_status(ws, stream=None) -> None:
-    _check(load().bkv_reset_device_status(_ptr(ws), _stream(stream)))
+    (w,) = _on_gpu(_ws(ws))
+    _check(load().bkv_reset_device_status(w, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
