@@ -134,7 +134,9 @@ int bkv_workspace_layout(const bkv_shape *shape, int32_t R, int32_t nb, size_t o
  * cosine similarity: start at the row with the lowest mean cosine to all
  * rows, then repeatedly add the row whose maximum cosine to the picked set
  * is lowest; ties go to the lower row.  Cosines are evaluated in binary64.
- * Rows at or beyond the final count are unspecified.
+ * Rows at or beyond the final count are unspecified.  Query rows must be
+ * finite; with non-finite rows the picks are unspecified, though always rows
+ * of the buffer (the same holds for the beacon FPS of the scoring calls).
  */
 int bkv_fps_update(const bkv_shape *shape, const void *q_new, int32_t T, void *qbuf,
                    int32_t *qcount, int32_t C, int32_t M, void *ws, size_t ws_bytes,

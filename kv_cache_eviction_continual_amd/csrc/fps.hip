@@ -251,7 +251,9 @@ __device__ inline void fps_dots64(const typename Elem<DT>::T* a, const typename 
 }
 
 // Lowest binary64 objective among the candidates flagged in `inmask` (bit b
-// of word w = row 64 w + b), ties to the lower row.  Objective: the mean
+// of word w = row 64 w + b, at least one set), ties to the lower row; a
+// flagged row in every case (with NaN objectives, from non-finite rows, the
+// lowest flagged row that no finite objective beats).  Objective: the mean
 // cosine to all c rows (sum_mode) or the maximum cosine to picks[0, npicked),
 // cosines as a.b / (max(|a|, 1e-12) max(|b|, 1e-12)).  The lanes split the
 // partner rows; the result is wave-uniform.
@@ -287,7 +289,10 @@ __device__ __attribute__((always_inline)) int fps_exact_argmin(const FpsRows<DT,
         acc = sum_mode ? acc + o : fmax(acc, o);
       }
       const double obj = readfirstlane_f64(sum_mode ? acc / (double)c : acc);
-      if (obj < best) {  // candidates come in increasing row order: ties keep the lower row
+      // candidates come in increasing row order: ties keep the lower row.  The
+      // first candidate is always taken, so the result is a flagged row even
+      // when non-finite rows make every objective NaN
+      if (obj < best || besti == 0x7fffffff) {
         best = obj;
         besti = a;
       }
@@ -679,8 +684,9 @@ __device__ __attribute__((always_inline)) int coop_decide(uint32_t key, float va
   k2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)k2);
   const float hi1 = key_hi(k1) + win;
   if (k2 == 0xFFFFFFFFu || key_lo(k2) > hi1) return (int)(k1 & 0xFFu);
-  // binary64 decision over the candidates within the window
-  const uint64_t m = __ballot((lane >> 5) == 0 && key != 0xFFFFFFFFu && val <= hi1);
+  // binary64 decision over the candidates within the window (k1's own row
+  // always among them, so the set is never empty)
+  const uint64_t m = __ballot((lane >> 5) == 0 && key != 0xFFFFFFFFu && (val <= hi1 || key == k1));
   if (lane == 0) s.mask[wv] = (uint32_t)m;
   __syncthreads();
   if (wv == 0) {
