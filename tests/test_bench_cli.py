@@ -61,3 +61,50 @@ def test_append_plan_gives_every_slot_its_rotated_source():
             assert got == {s: (s + rot) % N for s in range(a, e)}, (t, a, e, runs)
             assert len(runs) <= 2  # one wrap at most
     assert len(seen) == P * N
+
+
+def test_query_blocks_are_new_in_every_phase():
+    """bench.py's query blocks: each pass of a phase (its warm-up passes, timed
+    passes and the primed next pass) ingests the block of its own global
+    decode period, and no phase re-ingests a block an earlier phase (or the
+    buffer warm-up) ingested, as long as a phase fits the pool."""
+    import importlib.util
+
+    import torch
+
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+
+    class Syn:
+        def query_block(self, b):
+            return torch.full((1, 1, 4, 1), float(b))
+
+    class W:
+        n_recent = 2
+
+    st = bench.State.__new__(bench.State)
+    st.w, st.syn, st.n_warm, st.pass_base, st.pool_first = W(), Syn(), 17, 0, 0
+    warmup, steps = 5, 20
+    st.n_pool = warmup + steps + 1
+    st.blocks = [Syn().query_block(b) for b in range(st.n_pool)]
+    st.recent = [b[:, :, -2:] for b in st.blocks]
+    st.refresh_blocks(0)  # after the buffer warm-up (periods 0..16)
+    seen = set(range(17))
+    events = set()
+    total = 0
+    for phase, overlap in enumerate((False, True, True, False, True, True)):
+        st.refresh_blocks(warmup + steps)
+        # an overlapped schedule also ingests the block of the pass after its last one
+        n = warmup + steps + (1 if overlap else 0)
+        got = [int(st.blocks[st.block(i)][0, 0, 0, 0]) for i in range(n)]
+        assert got == [st.period(i) for i in range(n)]
+        assert not seen & set(got), phase
+        seen |= set(got)
+        assert int(st.recent[st.block(3)][0, 0, 0, 0]) == st.period(3)
+        events |= {st.event(i) for i in range(n)}
+        total += n
+        # as bench.timed_passes advances it
+        st.pass_base += warmup + steps + (1 if overlap else 0)
+    assert len(seen) == 17 + total
+    assert len(events) == total  # eviction events (positions) advance with the passes too
