@@ -22,7 +22,8 @@
  *     current HIP device.  The caller owns and allocates every buffer,
  *     including the workspace; the library never allocates, frees or
  *     synchronises (bkv_read_device_status excepted) and keeps no state
- *     between calls.
+ *     between calls, except for the one scratch array per device of
+ *     bkv_select_compact_noalloc, which takes no workspace.
  *   - Work is enqueued on `stream` (0 = the null stream), in call order.
  *   - Tensors are dense and row-major in the index order written next to
  *     them.  N = shape->n_seq, Hkv = shape->n_kv_heads, Hq =
@@ -65,7 +66,8 @@ enum bkv_status {
   BKV_E_BUDGET = 4,    /* budget < window, window < 0 or budget > max_len */
   BKV_E_CAPACITY = 5,  /* shrink target not in [1, C), or capacity too large */
   BKV_E_WORKSPACE = 6, /* workspace NULL, too small or not 256-byte aligned */
-  BKV_E_HIP = 7        /* a kernel launch failed */
+  BKV_E_HIP = 7,       /* a kernel launch failed */
+  BKV_E_SCRATCH = 8    /* bkv_select_compact_noalloc: more units than its scratch holds */
 };
 
 enum bkv_dtype { BKV_F32 = 0, BKV_BF16 = 1 };
@@ -265,6 +267,31 @@ int bkv_compact(const bkv_shape *shape, void *K, void *V, int32_t *len, int32_t 
 int bkv_select_compact(const bkv_shape *shape, const float *scores, void *K, void *V,
                        int32_t *len, int32_t budget, int32_t window, int32_t *kept, void *ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * bkv_select_compact_noalloc -- bkv_select_compact for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument; the same kernels
+ * use a scratch array the library holds in device memory, 1 MiB per device
+ * for the life of the process (status word, statistics, and the select table
+ * of at most 131,040 (slot, KV head) units).
+ *
+ *   scores, K, V, len, budget, window, kept  as bkv_select_compact
+ *   dev_status  int32 DEVICE pointer or NULL: receives this call's device
+ *               status word (BKV_DEV_* bits; 0 when every unit was valid)
+ *
+ * Results equal bkv_select_compact's.  Returns BKV_E_SCRATCH (nothing
+ * enqueued) when n_seq * n_kv_heads > 131,040.  Every call on a device uses
+ * that device's one scratch array: calls that overlap on one device (on
+ * different streams, or from several host threads without ordering) race and
+ * must not be issued.  Each call clears the status word first; the select
+ * table is fully rewritten by the selection before the compaction reads it.
+ * Allocates and frees nothing; the first call on a device looks up the
+ * array's device address (hipGetSymbolAddress).
+ */
+int bkv_select_compact_noalloc(const bkv_shape *shape, const float *scores, void *K, void *V,
+                               int32_t *len, int32_t budget, int32_t window, int32_t *kept,
+                               int32_t *dev_status, hipStream_t stream);
 
 /*
  * Hole-filling layout.  The order-preserving compaction above moves every

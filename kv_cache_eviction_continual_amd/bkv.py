@@ -20,7 +20,8 @@ F32 = 0
 BF16 = 1
 
 OK = 0
-E_NULL, E_SHAPE, E_DTYPE, E_BUDGET, E_CAPACITY, E_WORKSPACE, E_HIP = range(1, 8)
+E_NULL, E_SHAPE, E_DTYPE, E_BUDGET, E_CAPACITY, E_WORKSPACE, E_HIP, E_SCRATCH = range(1, 9)
+NOALLOC_MAX_UNITS = 131040  # bkv_select_compact_noalloc: (slot, KV head) units its scratch holds
 DEV_BAD_LEN = 0x1
 DEV_BAD_COUNT = 0x2
 DEV_BAD_INDEX = 0x4
@@ -41,6 +42,7 @@ EXPORTS = (
     "bkv_select",
     "bkv_compact",
     "bkv_select_compact",
+    "bkv_select_compact_noalloc",
     "bkv_select_fill",
     "bkv_compact_fill",
     "bkv_select_compact_fill",
@@ -106,6 +108,8 @@ def load() -> ctypes.CDLL:
     L.bkv_compact.restype = ctypes.c_int
     L.bkv_select_compact.argtypes = [SP, P, P, P, P, I32, I32, P, P, SZ, P]
     L.bkv_select_compact.restype = ctypes.c_int
+    L.bkv_select_compact_noalloc.argtypes = [SP, P, P, P, P, I32, I32, P, P, P]
+    L.bkv_select_compact_noalloc.restype = ctypes.c_int
     L.bkv_select_fill.argtypes = [SP, P, P, P, I32, I32, P, P, SZ, P]
     L.bkv_select_fill.restype = ctypes.c_int
     L.bkv_compact_fill.argtypes = [SP, P, P, P, P, I32, P, P, SZ, P]
@@ -341,6 +345,14 @@ def bkv_select_compact(shape: Shape, scores, K, V, length, budget: int, window: 
     sc, ln, kp, k, v, w = _on_gpu(*_select_common(shape, scores, length, budget, kept), *_kv(shape, K, V), _ws(ws))
     _check(load().bkv_select_compact(ctypes.byref(shape), sc, k, v, ln, budget, window, kp, w, _nbytes(ws),
                                      _stream(stream)))
+
+
+def bkv_select_compact_noalloc(shape: Shape, scores, K, V, length, budget: int, window: int, kept,
+                               dev_status=None, stream=None) -> None:
+    sc, ln, kp, k, v, so = _on_gpu(*_select_common(shape, scores, length, budget, kept), *_kv(shape, K, V),
+                                   _dev(dev_status, "dev_status", torch.int32, 1, optional=True))
+    _check(load().bkv_select_compact_noalloc(ctypes.byref(shape), sc, k, v, ln, budget, window, kp, so,
+                                             _stream(stream)))
 
 
 def bkv_select_fill(shape: Shape, scores, pos, length, budget: int, window: int, kept, ws, stream=None) -> None:

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "bkv.h"
 #include "bkv_device.hpp"
 
@@ -39,6 +41,41 @@ size_t fps_full_workspace_bytes(long, long, int);
 __global__ void zero_header_kernel(int32_t* w) {
   if (threadIdx.x < (int)(kHeaderBytes / 4)) w[threadIdx.x] = 0;
 }
+
+__global__ void copy_status_kernel(const int32_t* __restrict__ w, int32_t* __restrict__ out) {
+  if (threadIdx.x == 0) out[0] = w[kStatusWord];
+}
+
+// Scratch memory of bkv_select_compact_noalloc: the workspace header (status
+// word, rows_moved) followed by the select table [N][Hkv][2].  Each device
+// holds its own copy, at its own address, for the life of the process.
+constexpr size_t kNoallocScratchBytes = size_t(1) << 20;
+constexpr long kNoallocMaxUnits = (long)((kNoallocScratchBytes - kHeaderBytes) / (2 * sizeof(int32_t)));
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device, once looked up
+
+// The device address of the current device's `scratch` (looked up on the
+// first call on that device; the host-side name of the array is not a
+// device address and is never passed to a kernel).
+int scratch_on_current_device(unsigned char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BKV_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return BKV_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (unsigned char*)g_scratch_ptr[dev];
+  return BKV_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -396,6 +433,37 @@ int bkv_select_compact(const bkv_shape* shape, const float* scores, void* K, voi
   return bkv_compact(shape, K, V, len, budget, kept, ws, ws_bytes, stream);
 }
 
+int bkv_select_compact_noalloc(const bkv_shape* shape, const float* scores, void* K, void* V, int32_t* len,
+                               int32_t budget, int32_t window, int32_t* kept, int32_t* dev_status,
+                               hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != BKV_OK) return st;
+  if (window < 0 || budget < window || budget < 1 || budget > shape->max_len) return BKV_E_BUDGET;
+  if (!scores || !K || !V || !len || !kept) return BKV_E_NULL;
+  const int N = shape->n_seq, Hkv = shape->n_kv_heads;
+  if ((long)N * Hkv > kNoallocMaxUnits) return BKV_E_SCRATCH;
+  if (N == 0) return BKV_OK;
+  unsigned char* base = nullptr;
+  if ((st = scratch_on_current_device(&base)) != BKV_OK) return st;
+  int32_t* words = (int32_t*)base;
+  int32_t* sel = (int32_t*)(base + kHeaderBytes);
+  unsigned long long* moved = (unsigned long long*)(base + 8);
+  // the previous call's status and statistics are cleared by a kernel (no
+  // memset node, so the call can be captured into a graph)
+  hipLaunchKernelGGL(zero_header_kernel, dim3(1), dim3(64), 0, stream, words);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_select(scores, len, N, Hkv, shape->max_len, budget, window, kept, sel, words, stream);
+  if (e == hipSuccess) {
+    const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
+    e = launch_compact(K, V, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, stream);
+  }
+  if (e == hipSuccess && dev_status) {
+    hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, stream, (const int32_t*)words, dev_status);
+    e = hipGetLastError();
+  }
+  return hip_status(e);
+}
+
 int bkv_select_fill(const bkv_shape* shape, const float* scores, const int32_t* pos, const int32_t* len,
                     int32_t budget, int32_t window, int32_t* kept, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_shape(shape);
@@ -455,6 +523,9 @@ const char* bkv_status_string(int status) {
     case BKV_E_CAPACITY: return "buffer capacity, shrink target or beacon count out of range";
     case BKV_E_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
     case BKV_E_HIP: return "a HIP kernel launch failed";
+    case BKV_E_SCRATCH:
+      return "n_seq * n_kv_heads exceeds the 131,040 (slot, KV head) units the static scratch of "
+             "bkv_select_compact_noalloc holds";
     default: return "unknown status";
   }
 }

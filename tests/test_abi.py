@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 8):
+    for s in range(0, 9):
         assert bkv.bkv_status_string(s)
     assert bkv.bkv_status_string(0) == "ok"
     assert "unknown" in bkv.bkv_status_string(99)
@@ -154,6 +154,26 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.bkv_fps_update(ctypes.byref(s), fake, 4, fake, fake, 128, 16, fake, 1 << 20, None) == bkv.OK
     assert lib.bkv_select(ctypes.byref(s), fake, fake, 2048, 32, fake, fake, 1 << 20, None) == bkv.OK
     assert lib.bkv_compact(ctypes.byref(s), fake, fake, fake, 2048, fake, fake, 1 << 20, None) == bkv.OK
+    assert lib.bkv_select_compact_noalloc(ctypes.byref(s), fake, fake, fake, fake, 2048, 32, fake, None, None) == bkv.OK
+
+
+def test_noalloc_entry_point_validation(lib):
+    """bkv_select_compact_noalloc checks what bkv_select_compact checks (no
+    workspace), and refuses more (slot, KV head) units than its static
+    scratch holds before touching the device."""
+    f = lib.bkv_select_compact_noalloc
+    fake, P = 256, None
+    s = shape()
+    assert f(None, fake, fake, fake, fake, 2048, 32, fake, None, P) == bkv.E_NULL
+    assert f(ctypes.byref(s), fake, fake, fake, fake, 2048, 4096, fake, None, P) == bkv.E_BUDGET
+    assert f(ctypes.byref(s), fake, fake, fake, fake, 0, 0, fake, None, P) == bkv.E_BUDGET
+    assert f(ctypes.byref(s), fake, fake, fake, fake, 1 << 20, 32, fake, None, P) == bkv.E_BUDGET
+    assert f(ctypes.byref(s), None, fake, fake, fake, 2048, 32, fake, None, P) == bkv.E_NULL
+    assert f(ctypes.byref(s), fake, fake, None, fake, 2048, 32, fake, None, P) == bkv.E_NULL
+    assert f(ctypes.byref(s), fake, fake, fake, fake, 2048, 32, None, None, P) == bkv.E_NULL
+    big = shape(n_seq=bkv.NOALLOC_MAX_UNITS // 8 + 1, n_kv_heads=8, n_q_heads=32)
+    assert f(ctypes.byref(big), fake, fake, fake, fake, 2048, 32, fake, None, P) == bkv.E_SCRATCH
+    assert "131,040" in bkv.bkv_status_string(bkv.E_SCRATCH)
 
 
 def test_fps_full_validation_and_workspace_size(lib):
