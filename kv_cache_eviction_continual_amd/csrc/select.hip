@@ -5,8 +5,8 @@
 // Selection (inkeast.github.io MessageDaily paper-reading post on BeaconKV,
 // section 三: I = TopK(score(K,V), B_KV); aimodeling.com "BeaconKV: Beacon
 // Queries Fix KV Eviction for Long Reasoning", section "Beacon queries
-// anticipate what will be revisited": the recent sliding window is always
-// kept).  B_KV counts the window; the other B_KV - W entries are the highest
+// anticipate what will be revisited": the newest W entries are kept whatever
+// their scores).  B_KV counts the window; the other B_KV - W entries are the highest
 // scores of the rest, ties at the cut going to the lower index (the older
 // position in the hole-filling layout).
 //

@@ -707,8 +707,8 @@ static int by_score_desc_index_asc(const void *pa, const void *pb) {
 /*
  * orc_select: the kept set of one KV head.
  * [IK, 三]: at eviction time keep I = TopK(score, B_KV).  [AM, "Beacon queries
- * anticipate what will be revisited"]: the highest-scoring entries survive
- * while a recent sliding window is always preserved.
+ * anticipate what will be revisited"]: keep the top scores; the last W
+ * entries (the recent window) are kept whatever their scores.
  *
  * Readings: B_KV counts every kept entry, the window included; the window is
  * the last W entries [L-W, L); the other B-W are the top scores of [0, L-W),
@@ -787,7 +787,7 @@ static int by_score_desc_pos_asc_row_asc(const void *pa, const void *pb) {
  * orc_select_fill: the kept set of one KV head when rows are not kept in
  * position order, and the gather map that fills the evicted rows.
  * [IK, 三]: keep I = TopK(score, B_KV); [AM, "Beacon queries anticipate what
- * will be revisited"]: the recent sliding window is always kept.
+ * will be revisited"]: the newest W entries are kept whatever their scores.
  *
  * Readings: row j holds the token at position pos[j].  The window is the W
  * newest tokens, i.e. the first W rows by (position descending, row
