@@ -808,6 +808,177 @@ def decode_compare(reps: int = 20):
     print(json.dumps(result), flush=True)
 
 
+def planted_recall(planted, kept, L, W):
+    """(planted keys kept, planted keys among the candidates) of one eviction
+    of one (slot, KV head): candidates are the rows [0, L - W) that the
+    window does not protect; planted is a bool array over the L rows before
+    the eviction, kept the ascending kept rows."""
+    cand = int(np.count_nonzero(planted[:max(L - W, 0)]))
+    kept = np.asarray(kept)
+    k = kept[(kept >= 0) & (kept < L - W)]
+    return int(np.count_nonzero(planted[k])), cand
+
+
+POLICIES = ("beaconkv", "no_beacons", "mean", "initial_recent", "random")
+
+
+def policy_recall(n_periods: int = 8, budget: int = 256, n_slots: int = 16, seed: int = 7, split_reps: int = 20):
+    """Synthetic planted-key recall of the scoring policies the pages compare
+    (BeaconKV's FPS beacons with max aggregation; no beacons, recent queries
+    only; mean aggregation; InitialRecent; random representatives drawn from
+    the buffer) and of the split between recent queries and beacons, on two
+    data recipes of the one-layer Qwen3-4B workload: the preset as stated
+    (5 % of keys planted along unit cluster centres, 10 % of queries around
+    them, local queries i.i.d.), and the "revisit" recipe (local queries that
+    resemble one another, clustered queries of the same norm that alone single
+    out the planted keys).  Evicts to `budget` every period.  Also times the
+    score stage against the split at 32 rows per query head on the benchmark
+    workload.  Prints its own JSON line."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bkv.load()
+
+    def study(w):
+        N, Hkv, Hq, d = n_slots, w.n_kv_heads, w.n_q_heads, w.head_dim
+        C, M, T, W, B = w.capacity, w.shrink_to, w.interval, w.window, budget
+        L0 = Lmax = w.length  # the cache when the first eviction runs (2176)
+        syn = synth.Synth(w, n_slots=N, seed=seed, device=dev)
+        shape = bkv.make_shape(N, Hkv, Hq, d, Lmax, torch.bfloat16)
+        n_warm = w.warm_steps // T
+        warm = [syn.query_block(b) for b in range(n_warm)]
+        K0, V0, P0 = syn.keys(max_len=Lmax), syn.values(max_len=Lmax), syn.planted(max_len=Lmax)
+        blocks = [syn.query_block(n_warm + p) for p in range(n_periods)]
+        newk = [syn.keys(max_len=T, block=1 + p) for p in range(n_periods)]
+        newv = [syn.values(max_len=T, block=1 + p) for p in range(n_periods)]
+        newp = [syn.planted(max_len=T, block=1 + p) for p in range(n_periods)]
+        qbuf0 = torch.zeros(N, Hq, C, d, dtype=torch.bfloat16, device=dev)
+        qcount0 = torch.zeros(N, Hq, dtype=torch.int32, device=dev)
+        ws0 = bkv.alloc_workspace(shape, 0, 0, device=dev)
+        for blk in warm:
+            bkv.bkv_fps_update(shape, blk, T, qbuf0, qcount0, C, M, ws0)
+        torch.cuda.synchronize()
+        gen = torch.Generator(device=dev)
+
+        def run(policy, R, nb):
+            first_q = warm[0][:, :, :nb].contiguous()  # InitialRecent: each head's earliest queries
+            K, V, planted = K0.clone(), V0.clone(), P0.clone()
+            qbuf, qcount = qbuf0.clone(), qcount0.clone()
+            length = torch.full((N,), L0, dtype=torch.int32, device=dev)
+            ws = bkv.alloc_workspace(shape, R, nb, device=dev)
+            scores = torch.zeros(N, Hkv, Lmax, device=dev)
+            kept = torch.empty(N, Hkv, B, dtype=torch.int32, device=dev)
+            gen.manual_seed(seed)
+            kept_planted = cand_planted = 0
+            per_eviction = []
+            for p in range(n_periods):
+                blk = blocks[p]
+                bkv.bkv_fps_update(shape, blk, T, qbuf, qcount, C, M, ws)
+                now = (n_warm + p + 1) * T - 1
+                rpos = torch.arange(now - R + 1, now + 1, dtype=torch.int32, device=dev).repeat(N, 1).contiguous()
+                pos_now = torch.full((N,), now, dtype=torch.int32, device=dev)
+                recent = blk[:, :, T - R:].contiguous()
+                agg = bkv.AGG_MEAN if policy == "mean" else bkv.AGG_MAX
+                if policy in ("beaconkv", "mean"):
+                    bkv.bkv_beacon_picks(shape, qbuf, qcount, C, R, nb, ws)
+                elif policy == "no_beacons":
+                    bkv.bkv_beacon_rows(shape, None, 0, None, R, 0, ws)
+                elif policy == "initial_recent":
+                    idx = torch.arange(nb, dtype=torch.int32, device=dev).repeat(N, Hq, 1).contiguous()
+                    bkv.bkv_beacon_rows(shape, first_q, nb, idx, R, nb, ws)
+                else:  # nb distinct live rows of each head's buffer, drawn at random
+                    r = torch.rand(N, Hq, C, generator=gen, device=dev)
+                    r = torch.where(torch.arange(C, device=dev) < qcount.unsqueeze(-1), r, torch.full_like(r, 2.0))
+                    idx = r.argsort(dim=-1)[:, :, :nb].to(torch.int32)
+                    idx = torch.where(torch.arange(nb, device=dev) < qcount.unsqueeze(-1), idx,
+                                      torch.full_like(idx, -1))
+                    bkv.bkv_beacon_rows(shape, qbuf, C, idx.contiguous(), R, nb, ws)
+                bkv.bkv_score_picked_agg(shape, K, length, recent, rpos, R, nb, pos_now, w.rope_theta, agg, scores, ws)
+                L = int(length[0])
+                bkv.bkv_select_compact(shape, scores, K, V, length, B, W, kept, ws)
+                pl = planted.cpu().numpy()
+                kp = kept.cpu().numpy()
+                k_sum = c_sum = 0
+                for n in range(N):
+                    for h in range(Hkv):
+                        a_, b_ = planted_recall(pl[n, h], kp[n, h], L, W)
+                        k_sum, c_sum = k_sum + a_, c_sum + b_
+                per_eviction.append(k_sum / max(c_sum, 1))
+                kept_planted, cand_planted = kept_planted + k_sum, cand_planted + c_sum
+                # the planted flags follow their rows; the period's new tokens are appended after the budget
+                planted[:, :, :B] = torch.gather(planted, 2, kept.long())
+                planted[:, :, B:] = False
+                K[:, :, B:B + T].copy_(newk[p])
+                V[:, :, B:B + T].copy_(newv[p])
+                planted[:, :, B:B + T] = newp[p]
+                length.fill_(B + T)
+            torch.cuda.synchronize()
+            assert bkv.bkv_read_device_status(ws) == 0
+            return {"recall": kept_planted / max(cand_planted, 1),
+                    "recall_per_eviction": per_eviction,
+                    "planted_fraction_of_cache_at_end": float(planted[:, :, :B].float().mean().item())}
+
+        R, nb = w.n_recent, w.n_beacons
+        out = {"policies": {pname: run(pname, R, 0 if pname == "no_beacons" else nb)
+                            for pname in POLICIES},
+               "split": [dict(recent=r_, beacons=b_, **run("beaconkv", r_, b_))
+                         for r_, b_ in ((32, 0), (24, 8), (16, 16), (8, 24), (1, 31))],
+               "workload": "%s x %d slots: 8 KV / 32 query heads, d=128, bf16, %.0f%% of keys planted along the %d "
+                           "query-cluster centres, %.0f%% of queries around those centres (norm scale %.3g, noise "
+                           "%.2g), local queries %s; first eviction %d -> %d, then %d periods of %d new tokens "
+                           "evicted back to %d (window %d, buffer %d -> %d)"
+                           % (w.name, N, 100 * w.plant_rate, w.n_centres, 100 * w.p_global, w.global_scale, w.sigma,
+                              "i.i.d. N(0, I)" if w.local_scale == 0 else
+                              "%.3g * a shared direction + N(0, I)" % w.local_scale,
+                              L0, B, n_periods - 1, T, B, W, C, M),
+               "planted_fraction_of_cache_at_start": float(P0.float().mean().item())}
+        return out
+
+    w2 = configs.get(2)
+    recipes = {"stated": study(w2), "revisit": study(configs.revisit(w2))}
+
+    # scoring time against the recent / beacon split at 32 rows per query head, benchmark workload
+    w3 = configs.get(CFG)
+    st = State(w3, dev, n_pool=w3.warm_steps // w3.interval + 2)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(split_reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / split_reps
+
+    split = []
+    blk = st.blocks[st.block(0)]
+    now = int(st.pos_now[0, 0])
+    for r_, b_ in ((32, 0), (24, 8), (16, 16), (8, 24), (1, 31)):
+        ws = bkv.alloc_workspace(st.shape, r_, b_, device=dev)
+        rec = blk[:, :, -r_:].contiguous()
+        rp = torch.arange(now - r_ + 1, now + 1, dtype=torch.int32, device=dev).repeat(st.N, 1).contiguous()
+        picks_ms = timed(lambda: bkv.bkv_beacon_picks(st.shape, st.qbuf, st.qcount, w3.capacity, r_, b_, ws))
+        score_ms = timed(lambda: bkv.bkv_score_picked(st.shape, st.K, st.length, rec, rp, r_, b_, st.pos_now[0],
+                                                      w3.rope_theta, st.scores, ws))
+        assert bkv.bkv_read_device_status(ws) == 0
+        split.append({"recent": r_, "beacons": b_, "beacon_fps_ms": picks_ms, "score_ms": score_ms})
+        del ws
+
+    result = {
+        "metric": "planted-key recall of the scoring policies and of the recent/beacon split; scoring time against "
+                  "the split",
+        "data": "synthetic",
+        "recall_definition": "planted keys kept / planted keys among the eviction candidates (rows outside the "
+                             "window), summed over evictions and (slot, KV head) units",
+        "recipes": recipes,
+        "split_timing_workload": w3.name + " (4,608 units, cache 2176, 32 observation rows per query head)",
+        "split_timing": split,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def load_traffic(src_hash, workload):
     """The recorded counter figures, if they were taken on this workload with
     these kernel sources."""
@@ -840,6 +1011,9 @@ def main():
                     help="instead of the eviction pass: decode attention with and without the recent-query capture")
     ap.add_argument("--fps-compare", action="store_true",
                     help="instead of the eviction pass: full-history FPS vs Continual FPS on one Qwen3-14B layer")
+    ap.add_argument("--policy-recall", action="store_true",
+                    help="instead of the eviction pass: planted-key recall of the scoring policies and the scoring "
+                         "time of the recent/beacon split")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
@@ -848,6 +1022,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.fps_compare:
         fps_compare()
+        return
+    if args.policy_recall:
+        policy_recall()
         return
     if args.decode_compare:
         decode_compare()

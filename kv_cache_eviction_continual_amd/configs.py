@@ -38,6 +38,12 @@ class Workload:
     sigma: float         # per-coordinate noise of clustered queries
     plant_rate: float    # fraction of keys planted near a centre
     warm_steps: int      # query-stream length used to reach a realistic buffer state
+    # optional structure for the policy ablation (the defaults leave every
+    # preset's draws unchanged): local queries are local_scale * u + N(0, I)
+    # with one unit direction u per (slot, KV head), so that they resemble one
+    # another; clustered queries are global_scale * centre + sigma * N(0, I)
+    local_scale: float = 0.0
+    global_scale: float = 1.0
 
     @property
     def n_slots(self) -> int:
@@ -83,6 +89,17 @@ CONFIGS = {
                 n_recent=16, n_beacons=32, capacity=256, shrink_to=32, interval=128, p_global=0.15,
                 n_centres=10, centre_kind="gauss", sigma=0.1, plant_rate=0.0, warm_steps=4224),
 }
+
+
+def revisit(w: Workload) -> Workload:
+    """The ablation's "revisit" recipe on top of a preset: local queries
+    that resemble one another (a shared direction of norm sqrt(d), cosine
+    about 0.5 between two of them) and clustered global queries of the same
+    norm around unit centres (noise 0.3 per coordinate), which alone single
+    out the keys planted along those centres."""
+    d = w.head_dim
+    return replace(w, name=w.name + "-revisit", centre_kind="unit", local_scale=d ** 0.5, global_scale=d ** 0.5,
+                   sigma=0.3, plant_rate=w.plant_rate if w.plant_rate > 0 else 0.05)
 
 
 def get(cfg: int, **overrides) -> Workload:

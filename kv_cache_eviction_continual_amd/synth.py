@@ -91,6 +91,11 @@ class Synth:
         if w.centre_kind == "unit":
             c = c / c.norm(dim=-1, keepdim=True)
         self.centres = c
+        self.local_dir = None
+        if w.local_scale > 0:  # one unit direction per (slot, KV head) shared by its local queries
+            gl = generator(self.device, self.tag, self.seed, _STREAM_CENTRES, 1)
+            u = torch.randn(self.N, w.n_kv_heads, w.head_dim, generator=gl, device=self.device)
+            self.local_dir = u / u.norm(dim=-1, keepdim=True)
 
     # -- queries --------------------------------------------------------------
     def query_block(self, block: int, steps: int | None = None) -> torch.Tensor:
@@ -105,7 +110,11 @@ class Synth:
         m = torch.randint(0, w.n_centres, (N, Hq, steps), generator=g, device=self.device)
         cq = self.centres.repeat_interleave(w.group, dim=1)  # [N, Hq, n_centres, d]
         cen = torch.gather(cq, 2, m.unsqueeze(-1).expand(N, Hq, steps, d))
-        q = torch.where((u < w.p_global).unsqueeze(-1), cen + w.sigma * z, z)
+        local = z
+        if self.local_dir is not None:
+            local = z + w.local_scale * self.local_dir.repeat_interleave(w.group, dim=1).unsqueeze(2)
+        glob = cen + w.sigma * z if w.global_scale == 1.0 else w.global_scale * cen + w.sigma * z
+        q = torch.where((u < w.p_global).unsqueeze(-1), glob, local)
         return to_storage(q, w.dtype)
 
     def stream(self, steps: int) -> torch.Tensor:
@@ -135,6 +144,19 @@ class Synth:
             cen = torch.gather(self.centres, 2, m.unsqueeze(-1).expand(N, H, Lm, d))
             z = torch.where((u < w.plant_rate).unsqueeze(-1), (d ** 0.5) * cen + 0.1 * z, z)
         return to_storage(z, w.dtype)
+
+    def planted(self, max_len: int | None = None, block: int = 0) -> torch.Tensor:
+        """Which rows of keys(max_len, block) are planted near a centre: the
+        same draws replayed, bool [N, Hkv, Lm] (all False without planting)."""
+        w = self.w
+        Lm = w.max_len if max_len is None else max_len
+        N, H, d = self.N, w.n_kv_heads, w.head_dim
+        if w.plant_rate <= 0:
+            return torch.zeros(N, H, Lm, dtype=torch.bool, device=self.device)
+        g = generator(self.device, self.tag, self.seed, _STREAM_KEYS, block)
+        torch.randn(N, H, Lm, d, generator=g, device=self.device)
+        u = torch.rand(N, H, Lm, generator=g, device=self.device)
+        return u < w.plant_rate
 
     def values(self, max_len: int | None = None, block: int = 0) -> torch.Tensor:
         w = self.w

@@ -108,3 +108,42 @@ def test_query_blocks_are_new_in_every_phase():
         st.pass_base += warmup + steps + (1 if overlap else 0)
     assert len(seen) == 17 + total
     assert len(events) == total  # eviction events (positions) advance with the passes too
+
+
+def test_planted_mask_marks_the_planted_keys():
+    """synth.Synth.planted replays the key draws: the rows it marks lie along
+    a centre of their (slot, KV head) (cosine near 1), the others do not."""
+    import torch
+
+    from kv_cache_eviction_continual_amd import configs, synth
+
+    w = configs.get(2)
+    s = synth.Synth(w, n_slots=2, seed=3)
+    K = s.keys(max_len=400, block=5).float()
+    P = s.planted(max_len=400, block=5)
+    c = s.centres / s.centres.norm(dim=-1, keepdim=True)                       # [N, Hkv, n_centres, d]
+    cos = torch.einsum("nhld,nhcd->nhlc", K / K.norm(dim=-1, keepdim=True), c).abs().amax(dim=-1)
+    assert 0.02 < P.float().mean().item() < 0.08
+    assert cos[P].min().item() > 0.95 and cos[~P].max().item() < 0.6
+
+
+def test_planted_recall_counts_candidates_only(orc):
+    """bench.planted_recall on a hand-worked eviction: L = 10, window 2,
+    budget 6, planted rows {1, 4, 7, 9}; the oracle keeps the top 4 scores
+    of rows 0..7 ({1, 3, 4, 6}) and the window {8, 9}.  Planted candidates
+    are {1, 4, 7} (row 9 is in the window), of which {1, 4} are kept."""
+    import importlib.util
+
+    import numpy as np
+
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    scores = np.array([0.1, 0.9, 0.2, 0.8, 0.7, 0.05, 0.6, 0.3, 0.0, 0.0])
+    kept = orc.select(scores, 10, 6, 2)
+    assert kept.tolist() == [1, 3, 4, 6, 8, 9]
+    planted = np.zeros(10, bool)
+    planted[[1, 4, 7, 9]] = True
+    assert bench.planted_recall(planted, kept, 10, 2) == (2, 3)
+    # every candidate kept (no eviction): recall is complete
+    assert bench.planted_recall(planted, np.arange(10), 10, 2) == (3, 3)
