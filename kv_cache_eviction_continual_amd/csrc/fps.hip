@@ -571,22 +571,6 @@ __device__ __attribute__((always_inline)) int fps_wave(const FpsRows<DT, D>& src
   return kk;
 }
 
-// FPS over rows [0, c) with the tile count of c (1 .. 4 tiles of 32; larger
-// capacities take the cooperative routine below).
-template <int DT, int D, int NTMAX>
-__device__ __attribute__((always_inline)) int fps_dispatch(const FpsRows<DT, D>& src, const FpsLds& s, int c, int k) {
-  const int nt = (c + 31) >> 5;
-  if (nt <= 1) return fps_wave<DT, D, 1>(src, s, c, k);
-  if (nt == 2) return fps_wave<DT, D, 2>(src, s, c, k);
-  if constexpr (NTMAX >= 4) {
-    if (nt == 3) return fps_wave<DT, D, 3>(src, s, c, k);
-    if (nt == 4) return fps_wave<DT, D, 4>(src, s, c, k);
-  }
-  static_assert(NTMAX <= 4, "capacities above 128 rows use fps_coop");
-  return 0;
-}
-
-
 // ---------------------------------------------------------------------------
 // FPS of one head by NT cooperating waves
 // ---------------------------------------------------------------------------
@@ -908,29 +892,19 @@ __device__ inline void copy_units_n(int n, SrcF src_at, DstF dst_at) {
 }
 
 
-// Copies n 16-byte units, unit u from src_at(u) to dst_at(u, v), with eight
+// Copies n 16-byte units, unit u from src_at(u) to dst_at(u, v), with kB
 // loads per lane in flight (clamped in bounds) ahead of their stores.
-template <typename SrcF, typename DstF>
+template <int kB = 8, typename SrcF, typename DstF>
 __device__ inline void copy_units(int n, SrcF src_at, DstF dst_at) {
   const int l = fps_lane();
-  for (int u0 = 0; u0 < n; u0 += 512) {
+  for (int u0 = 0; u0 < n; u0 += 64 * kB) {
     const int m = n - 1;
-    const uint4 v0 = src_at(min(u0 + l, m));
-    const uint4 v1 = src_at(min(u0 + 64 + l, m));
-    const uint4 v2 = src_at(min(u0 + 128 + l, m));
-    const uint4 v3 = src_at(min(u0 + 192 + l, m));
-    const uint4 v4 = src_at(min(u0 + 256 + l, m));
-    const uint4 v5 = src_at(min(u0 + 320 + l, m));
-    const uint4 v6 = src_at(min(u0 + 384 + l, m));
-    const uint4 v7 = src_at(min(u0 + 448 + l, m));
-    if (u0 + l < n) dst_at(u0 + l, v0);
-    if (u0 + 64 + l < n) dst_at(u0 + 64 + l, v1);
-    if (u0 + 128 + l < n) dst_at(u0 + 128 + l, v2);
-    if (u0 + 192 + l < n) dst_at(u0 + 192 + l, v3);
-    if (u0 + 256 + l < n) dst_at(u0 + 256 + l, v4);
-    if (u0 + 320 + l < n) dst_at(u0 + 320 + l, v5);
-    if (u0 + 384 + l < n) dst_at(u0 + 384 + l, v6);
-    if (u0 + 448 + l < n) dst_at(u0 + 448 + l, v7);
+    uint4 v[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) v[b] = src_at(min(u0 + 64 * b + l, m));
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (u0 + 64 * b + l < n) dst_at(u0 + 64 * b + l, v[b]);
   }
 }
 
@@ -1007,11 +981,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     __builtin_amdgcn_wave_barrier();
     copy_units(nlast * kU, [&](int u) { return stage[u]; }, [&](int u, uint4 v) { bufu[u] = v; });
   }
-  // the rows after the picks are the last arrivals of the call, contiguous in q_new
+  // the rows after the picks are the last arrivals of the call, contiguous
+  // in q_new (the fragments are dead by now, so more loads fit in flight)
   if (c > nlast) {
     const uint4* tail = reinterpret_cast<const uint4*>(src.row(nlast));
     uint4* dst = bufu + (size_t)nlast * kU;
-    copy_units((c - nlast) * kU, [&](int u) { return tail[u]; }, [&](int u, uint4 v) { dst[u] = v; });
+    copy_units<16>((c - nlast) * kU, [&](int u) { return tail[u]; }, [&](int u, uint4 v) { dst[u] = v; });
   }
   if (lane == 0) qcount[head] = c;
 }
@@ -1024,17 +999,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 // Beacon selection: FPS over the live buffer of each query head
 // ---------------------------------------------------------------------------
 
-// One wavefront per query head.  Writes beacons[head][0] = the pick count
-// min(nb, count), beacons[head][1 + b] = buffer row of pick b, in pick
-// order, and a copy of the picked rows to rows[head][b] (so that scoring
-// does not read the buffer, which the next ingest may already be changing).
-// The score kernel rotates them.
-template <int DT, int D, int NTMAX>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void beacon_pick_kernel(
-    const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
-    int32_t* __restrict__ beacons, typename Elem<DT>::T* __restrict__ rows, int32_t* __restrict__ ws_words,
-    int cmax) {
-  constexpr int cap = 32 * NTMAX;
+// Waves per SIMD a beacon-pick wave's registers are budgeted for: one tile
+// of rows leaves room for four, more tiles for two.
+template <int NT>
+constexpr int picks_waves_per_simd() {
+  return NT == 1 ? 4 : 2;
+}
+
+
+// One wavefront per query head whose live count c lies in (cmin, cmax], a
+// range within one tile count NT (the launch for one tile takes c = 0 and the
+// heads whose count is out of range too); the other heads are left to the
+// launches for their tile count, so that each kernel holds only one tile
+// count's fragments and Gram triangle.
+// Writes beacons[head][0] = the pick count min(nb, count), beacons[head][1 +
+// b] = buffer row of pick b, in pick order, and a copy of the picked rows to
+// rows[head][b] (so that scoring does not read the buffer, which the next
+// ingest may already be changing).  The score kernel rotates them.
+template <int DT, int D, int NT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, picks_waves_per_simd<NT>()))) void
+beacon_pick_kernel(const typename Elem<DT>::T* __restrict__ qbuf, const int32_t* __restrict__ qcount, int C, int nb,
+                   int32_t* __restrict__ beacons, typename Elem<DT>::T* __restrict__ rows,
+                   int32_t* __restrict__ ws_words, int cmin, int cmax) {
+  constexpr int cap = 32 * NT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int head = blockIdx.x;
   const int lane = fps_lane();
@@ -1043,7 +1030,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     if (lane == 0) set_status(ws_words, BKV_DEV_BAD_COUNT);
     c = 0;
   }
-  if (c > cmax) return;  // more live rows than this kernel holds: the cooperative kernel takes the head
+  if (c <= cmin || c > cmax) return;  // another tile count's launch takes the head
   const int want = nb < c ? nb : c;
   FpsLds s = fps_carve<DT, D>(smem, cap, 0);
   const FpsRows<DT, D> src{qbuf + (size_t)head * C * D, nullptr, s.map, C};
@@ -1051,7 +1038,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   if (want > 0) {
     for (int r = lane; r < c; r += 64) s.map[r] = r;
     __builtin_amdgcn_wave_barrier();
-    kk = fps_dispatch<DT, D, NTMAX>(src, s, c, want);
+    kk = fps_wave<DT, D, NT>(src, s, c, want);
   }
   int32_t* out = beacons + (size_t)head * (nb + 1);
   for (int b = lane; b < kk; b += 64) out[1 + b] = s.picks[b];
@@ -1258,16 +1245,18 @@ hipError_t launch_fps_update(const void* q_new, int T, void* qbuf, int32_t* qcou
   }
 }
 
-template <int DT, int D, int NTMAX>
+template <int DT, int D, int NT>
 static hipError_t launch_picks_nt(const void* qbuf, const int32_t* qcount, int C, int nb, int heads,
-                                  int32_t* beacons, void* rows, int32_t* ws_words, int cmax, hipStream_t st) {
+                                  int32_t* beacons, void* rows, int32_t* ws_words, hipStream_t st) {
+  static_assert(NT >= 1 && NT <= 4, "one to four tiles of 32 rows");
   using ET = typename Elem<DT>::T;
-  const size_t smem = fps_lds_bytes<DT, D>(32 * NTMAX, 0);
-  auto kern = beacon_pick_kernel<DT, D, NTMAX>;
+  const size_t smem = fps_lds_bytes<DT, D>(32 * NT, 0);
+  auto kern = beacon_pick_kernel<DT, D, NT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
+  // live counts (32 (NT - 1), 32 NT]; the one-tile launch also takes 0
   hipLaunchKernelGGL(kern, dim3(heads), dim3(64), smem, st, (const ET*)qbuf, qcount, C, nb, beacons, (ET*)rows,
-                     ws_words, cmax);
+                     ws_words, NT == 1 ? -1 : 32 * (NT - 1), 32 * NT);
   return hipGetLastError();
 }
 
@@ -1285,17 +1274,18 @@ static hipError_t launch_picks_coop(const void* qbuf, const int32_t* qcount, int
   return hipGetLastError();
 }
 
-// Capacities above 128 rows: heads with at most 128 live rows take the
-// single-wave kernel (four waves per CU), the others the cooperative one;
-// each launch skips the other's heads.
+// One launch per 32-row tile count of the live rows up to four tiles (each
+// launch skips the heads of the others), the cooperative kernel for heads
+// with more than 128 live rows.
 template <int DT, int D>
 hipError_t launch_beacon_picks(const void* qbuf, const int32_t* qcount, int C, int nb, int heads, int32_t* beacons,
                                void* rows, int32_t* ws_words, hipStream_t st) {
-  if (C <= 64) return launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, C, st);
-  if (C <= 128) return launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, C, st);
-  hipError_t e = launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, 128, st);
-  if (e != hipSuccess) return e;
-  return launch_picks_coop<DT, D>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, 128, st);
+  hipError_t e = launch_picks_nt<DT, D, 1>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  if (e == hipSuccess && C > 32) e = launch_picks_nt<DT, D, 2>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  if (e == hipSuccess && C > 64) e = launch_picks_nt<DT, D, 3>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  if (e == hipSuccess && C > 96) e = launch_picks_nt<DT, D, 4>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, st);
+  if (e == hipSuccess && C > 128) e = launch_picks_coop<DT, D>(qbuf, qcount, C, nb, heads, beacons, rows, ws_words, 128, st);
+  return e;
 }
 
 template hipError_t launch_fps_update<BKV_F32, 64>(const void*, int, void*, int32_t*, int, int, int, int32_t*,
