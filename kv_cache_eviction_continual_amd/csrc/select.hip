@@ -17,14 +17,18 @@
 // pass gives every thread a contiguous run of entries, so one block scan
 // ranks all kept (or evicted) entries in index order.
 //
-// compact_kernel: one workgroup per (slot, KV head, tensor).  Row i <- row
-// kept[i] for i from the first evicted index up to the kept count.  Because
-// kept is ascending, kept[i] >= i: a row is only ever read by a destination
-// at or before its own index.  Rows move in steps of increasing index; a
-// block-wide barrier after each step's loads have returned orders every read
-// of a row before its overwrite.
+// compact_chunk_kernel: row i <- row kept[i] for i from the first evicted
+// index up to the kept count, in chunks of 64 KB of rows, one workgroup each
+// (see its description).  Because kept is ascending, kept[i] >= i: a
+// row is only ever read by a destination at or before its own index.
+// compact_kernel: the same move with one workgroup per (slot, KV head,
+// tensor), in steps of increasing index; a block-wide barrier after each
+// step's loads have returned orders every read of a row before its
+// overwrite.  It needs no workspace beyond the select table.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "bkv_device.hpp"
 
@@ -321,6 +325,128 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(unsigned char*
     }
 #pragma unroll
     for (int k = 0; k < kCompactUnroll; ++k) cur[k] = nxt[k];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked order-preserving compaction
+// ---------------------------------------------------------------------------
+//
+// The rows of a (unit, tensor) are cut into chunks of CR = kChunkBytes /
+// row_bytes rows, one workgroup each; chunk j moves the destinations [s_j,
+// e_j) = [j CR, (j + 1) CR) within [f, cnt) (f the first hole, cnt the kept
+// count).  It reads kept[i] >= i for i in [s_j, e_j): a later chunk reads
+// only rows at or beyond its own first destination, above every row chunk j
+// writes, and chunk j's own reads all return before its first store.  The
+// one hazard left is a row chunk j overwrites that an earlier chunk j' still
+// reads: a source of j' at or beyond s_j, which exists only while the last
+// source of j', kept[e_j' - 1], is >= s_j (at most (L - cnt) / CR + 1
+// earlier chunks).  So each chunk loads all its rows into registers,
+// publishes "read" in its flag, waits for the flags of the earlier chunks that
+// reach into its rows, then stores.  Blocks are numbered chunk-major, so an
+// earlier chunk of the same (unit, tensor) has a lower block index: each XCD
+// dispatches its blocks in index order, so while a block waits every
+// lower-indexed block is running or done, and it publishes its flag before
+// waiting on anything; the wait is also bounded (BKV_DEV_WAIT_LIMIT).  A
+// block has no stores outstanding when it waits for its loads, so its flag
+// follows its reads alone.  compact_prepare_kernel clears the flags before
+// every call (a kernel, not a memset node, so that the call can be captured
+// into a graph).
+
+constexpr int kChunkBytes = 65536;                                    // bytes of rows per chunk
+constexpr int kChunkPieces = kChunkBytes / 16 / kCompactThreads;     // 16-byte loads per thread
+constexpr int kChunkWaitPolls = 1 << 22;                              // bound of one flag wait (seconds)
+
+__host__ __device__ inline int compact_chunk_rows(int row_bytes) { return kChunkBytes / row_bytes; }
+
+// Zeroes the chunk flags.
+__global__ void compact_prepare_kernel(uint32_t* flags, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    flags[i] = 0u;
+}
+
+__global__ __launch_bounds__(kCompactThreads) void compact_chunk_kernel(
+    unsigned char* __restrict__ K, unsigned char* __restrict__ V, const int32_t* __restrict__ kept,
+    const int32_t* __restrict__ sel, int32_t* __restrict__ len, int Hkv, int Lmax, int B, int row_bytes,
+    unsigned long long* __restrict__ rows_moved, uint32_t* __restrict__ flags, int units, int nchunk,
+    int32_t* __restrict__ ws_words) {
+  __shared__ int s_go;
+  const int tid = threadIdx.x;
+  const uint32_t items_per_chunk = 2u * (uint32_t)units;
+  const int j = (int)(blockIdx.x / items_per_chunk);
+  const uint32_t ut = blockIdx.x % items_per_chunk;  // (unit, tensor)
+  const size_t unit = ut >> 1;
+  const int tensor = (int)(ut & 1u);
+  const int lpr = row_bytes / 16;
+  const int CR = compact_chunk_rows(row_bytes);
+  const int c0 = j * CR;  // chunk j: destinations [c0, c0 + CR) within [f, cnt)
+  const int32_t* kept_u = kept + unit * (size_t)B;
+  // the kept indices of the chunk's rows go out with the select table entry
+  // (kept[i] = i below the first hole, so reading them needs no f)
+  const int rows_here = max(0, min(CR, B - c0));
+  int src[kChunkPieces];
+#pragma unroll
+  for (int b = 0; b < kChunkPieces; ++b) {
+    const int r = (b * kCompactThreads + tid) / lpr;
+    src[b] = r < rows_here ? kept_u[c0 + r] : 0;
+  }
+  const int f = sel[2 * unit];
+  const int cnt = sel[2 * unit + 1];
+  if (cnt < 0) return;  // unit rejected by the selection
+  if (j == 0 && tid == 0) {
+    if (tensor == 0 && unit % Hkv == 0) len[unit / Hkv] = cnt;  // no compaction block reads len
+    if (cnt > f) atomicAdd(rows_moved, (unsigned long long)(cnt - f));
+  }
+  const int start = max(f, c0);
+  const int end = min(cnt, c0 + CR);
+  if (start >= end) return;  // nothing of this chunk moves
+  uint32_t* uflags = flags + ut * (size_t)nchunk;
+  // the nearest earlier chunk, if it moves rows and its reads reach into this
+  // chunk's rows (its flag is read alongside the rows; usually set long since)
+  const bool dep = j > 0 && c0 - 1 >= f && kept_u[c0 - 1] >= start;
+  uint32_t early = 1u;
+  if (tid == 0 && dep) early = __hip_atomic_load(&uflags[j - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned char* base = (tensor ? V : K) + unit * (size_t)Lmax * row_bytes;
+  nt_u32x4 v[kChunkPieces];
+#pragma unroll
+  for (int b = 0; b < kChunkPieces; ++b) {
+    const int p = b * kCompactThreads + tid;
+    const int r = p / lpr;
+    if (c0 + r >= start && c0 + r < end) v[b] = nt_load16(base + (size_t)src[b] * row_bytes + (size_t)(p - r * lpr) * 16);
+  }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every row of the chunk has been read
+  if (tid == 0) {
+    __hip_atomic_store(&uflags[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int go = 1;
+    if (dep) {
+      // the earlier chunks that move rows and whose last source lies at or
+      // beyond this chunk's first moved row: the nearest one (read above),
+      // then further back
+      for (int jp = j - 1; jp >= 0 && go; --jp) {
+        const int last = (jp + 1) * CR - 1;  // last destination of chunk jp (jp < j: a whole chunk)
+        if (last < f || kept_u[last] < start) break;
+        uint32_t fl = jp == j - 1 ? early : 0u;
+        for (int polls = 0; fl == 0u; ++polls) {
+          if (polls >= kChunkWaitPolls) {
+            go = 0;
+            set_status(ws_words, BKV_DEV_WAIT_LIMIT);
+            break;
+          }
+          if (polls > 0) __builtin_amdgcn_s_sleep(2);
+          fl = __hip_atomic_load(&uflags[jp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    s_go = go;
+  }
+  __syncthreads();
+  if (!s_go) return;  // a wait passed its bound: this chunk's rows are left unwritten
+#pragma unroll
+  for (int b = 0; b < kChunkPieces; ++b) {
+    const int p = b * kCompactThreads + tid;
+    const int r = p / lpr;
+    if (c0 + r >= start && c0 + r < end) nt_store16(base + (size_t)(c0 + r) * row_bytes + (size_t)(p - r * lpr) * 16, v[b]);
   }
 }
 
@@ -626,10 +752,40 @@ hipError_t launch_select(const float* scores, const int32_t* len, int N, int Hkv
   return hipGetLastError();
 }
 
-hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* sel, int32_t* len, int N, int Hkv,
-                          int Lmax, int B, int row_bytes, unsigned long long* rows_moved, hipStream_t st) {
+// One block per (unit, tensor), stepping through its rows (no workspace
+// beyond the select table).
+hipError_t launch_compact_stepped(void* K, void* V, const int32_t* kept, const int32_t* sel, int32_t* len, int N,
+                                  int Hkv, int Lmax, int B, int row_bytes, unsigned long long* rows_moved,
+                                  hipStream_t st) {
   hipLaunchKernelGGL(compact_kernel, dim3(N * Hkv * 2), dim3(kCompactThreads), 0, st, (unsigned char*)K, (unsigned char*)V, kept,
                      sel, len, Hkv, Lmax, B, row_bytes, rows_moved);
+  return hipGetLastError();
+}
+
+// Words of the chunked compaction's flags.
+size_t compact_area_words(int units, int Lmax, int row_bytes) {
+  const int cr = compact_chunk_rows(row_bytes);
+  const size_t nchunk = Lmax > 0 ? ((size_t)Lmax + cr - 1) / cr : 1;
+  return 2 * (size_t)units * nchunk;
+}
+
+// The chunked compaction: the flags cleared, then one block per (chunk, unit,
+// tensor), chunk-major.
+hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* sel, int32_t* len, int N, int Hkv,
+                          int Lmax, int B, int row_bytes, unsigned long long* rows_moved, uint32_t* flags,
+                          int32_t* ws_words, hipStream_t st) {
+  const int units = N * Hkv;
+  if (units == 0) return hipSuccess;
+  const int cr = compact_chunk_rows(row_bytes);
+  const int nchunk = Lmax > 0 ? (Lmax + cr - 1) / cr : 1;
+  const size_t words = compact_area_words(units, Lmax, row_bytes);
+  hipLaunchKernelGGL(compact_prepare_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 1024)), dim3(256), 0,
+                     st, flags, words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compact_chunk_kernel, dim3((unsigned)(2 * (size_t)units * nchunk)), dim3(kCompactThreads), 0, st,
+                     (unsigned char*)K, (unsigned char*)V, kept, sel, len, Hkv, Lmax, B, row_bytes, rows_moved, flags,
+                     units, nchunk, ws_words);
   return hipGetLastError();
 }
 
