@@ -26,10 +26,11 @@
 //           row max and sum of exp2 -> per-row log2-sum-exp; in a full tile
 //           the next sub-tile's products are issued among the current one's
 //           exp work, so one wave keeps the matrix core and the VALU busy;
-//   pass 2: S = Q K^T on MFMA (lane = key, 16 rows per lane), per-key max of
-//           (s - lse) over the wave's rows, then over the waves through LDS;
-//           one exp2 per key.  Pass 2 walks the tiles in reverse so that the
-//           most recently read tiles are still cached.
+//   pass 2: S = Q K^T on MFMA (lane = key, 16 rows per lane), the
+//           accumulators starting at -lse_r / scale (so the products land on
+//           s - lse_r / scale), per-key max over the wave's rows, then over
+//           the waves through LDS; one exp2 per key.  Pass 2 walks the tiles
+//           in reverse so that the most recently read tiles are still cached.
 // exp(max_r(s_r - lse_r)) = max_r exp(s_r - lse_r), so one exp per key
 // suffices.  Logits are accumulated in fp32 from exact bf16 (or fp32)
 // products.  The mean-aggregation variant (the same post, section 4.4: max
@@ -461,9 +462,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
   float* out = scores + unit * (size_t)Lmax;
   // S for key sub-tile `sub`: acc[r] is row 32 wave + acc_row(r, lane) of
   // key sub*32 + lane % 32
+  // max aggregation: each accumulator starts at -lse_r / scale2 (-inf for an
+  // absent row), so the products land on s - lse_r / scale2 and a key's score
+  // exp2(max_r (s scale2 - lse_r)) is exp2(scale2 max_r acc_r): one max per
+  // logit, no fma (scale2 > 0 keeps the maximum)
+  floatx16_t acc0 = {};
+  if constexpr (!kMean) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc0[r] = -lse_r[r] / scale2;
+  }
   auto logits = [&](int sub) {
     const unsigned char* krow = ktile + (size_t)(sub * kSub + (lane & 31)) * Lay::kRowStride;
-    floatx16_t acc = {};
+    floatx16_t acc = acc0;
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = MF::mma(qf[s], MF::load(krow, s, lane), acc);
     return acc;
@@ -476,10 +486,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
 #pragma unroll
       for (int r = 0; r < 16; ++r) t += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -lse_r[r]));
       t += __shfl_xor(t, 32, 64);
-    } else {  // maximum of the rows' log2-probabilities
-      t = ninf;
+    } else {  // maximum over the rows of s - lse_r / scale2
+      t = acc[0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t = fmaxf(t, fmaf(acc[r], scale2, -lse_r[r]));
+      for (int r = 1; r < 16; ++r) t = fmaxf(t, acc[r]);
       t = fmaxf(t, __shfl_xor(t, 32, 64));
     }
     if (lane < 32) part[wave * kTile + sub * kSub + lane] = t;
@@ -520,7 +530,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
           out[j] = t * inv_present;
         } else {
           for (int w = 1; w < nrow_waves; ++w) t = fmaxf(t, part[w * kTile + k]);
-          float v = exp2f(t);  // exp2(-inf) = 0 when no row is present
+          float v = exp2f(t * scale2);  // exp2(-inf) = 0 when no row is present
           if (capture != nullptr) v = fmaxf(v, capture[unit * (size_t)Lmax + j]);  // the recent rows' captured maxima
           out[j] = v;
         }

@@ -104,3 +104,42 @@ def test_chunked_compaction_matches_the_oracle_gather(case, kind):
     assert torch.equal(kept2, kept)
     assert np.array_equal(synth.to_numpy_storage(K2), Kn)
     assert np.array_equal(synth.to_numpy_storage(V2), Vn)
+
+
+def test_short_and_rejected_units_around_chunked_ones():
+    """A slot whose length is at most the budget moves nothing (kept[i] = i),
+    a slot with an invalid length is rejected (BKV_DEV_BAD_LEN, its rows and
+    length untouched), and the other slots are compacted as the oracle says."""
+    dtype, d, Lmax, B, W = torch.bfloat16, 128, 1500, 600, 16
+    lengths = [1500, 580, Lmax + 1, 1234]
+    N, Hkv, Hq = len(lengths), 2, 2
+    print("case: short and rejected units, lengths=%s B=%d" % (lengths, B), flush=True)
+    gen = np.random.default_rng(7)
+    shape = bkv.make_shape(N, Hkv, Hq, d, Lmax, dtype)
+    valid = [min(L, Lmax) for L in lengths]
+    scores_np = pattern_scores("random", N, Hkv, Lmax, valid, gen)
+    K = torch.randn(N, Hkv, Lmax, d, device="cuda").to(dtype)
+    V = torch.randn(N, Hkv, Lmax, d, device="cuda").to(dtype)
+    K_old, V_old = synth.to_numpy_storage(K), synth.to_numpy_storage(V)
+    length = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    kept = torch.empty(N, Hkv, B, dtype=torch.int32, device="cuda")
+    ws = bkv.alloc_workspace(shape, 4, 4)
+    bkv.bkv_select_compact(shape, torch.from_numpy(scores_np).cuda(), K, V, length, B, W, kept, ws)
+    torch.cuda.synchronize()
+    assert bkv.bkv_read_device_status(ws) == bkv.DEV_BAD_LEN
+    Kn, Vn, kg = synth.to_numpy_storage(K), synth.to_numpy_storage(V), kept.cpu().numpy()
+    out_len = length.cpu().tolist()
+    for n, L in enumerate(lengths):
+        if L > Lmax:
+            assert np.array_equal(Kn[n], K_old[n]) and np.array_equal(Vn[n], V_old[n])
+            assert out_len[n] == L
+            continue
+        assert out_len[n] == min(L, B)
+        for h in range(Hkv):
+            ko = oracle.select(scores_np[n, h].astype(np.float64), L, B, W)
+            cnt = min(L, B)
+            assert np.array_equal(kg[n, h, :cnt], ko[:cnt])
+            for new, old in ((Kn, K_old), (Vn, V_old)):
+                ref = np.ascontiguousarray(old[n, h])
+                oracle.compact(ref, ko[:cnt])
+                assert np.array_equal(new[n, h], ref), (n, h)
