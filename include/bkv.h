@@ -76,8 +76,6 @@ enum bkv_dtype { BKV_F32 = 0, BKV_BF16 = 1 };
 #define BKV_DEV_BAD_LEN 0x1   /* len[n] < 0 or len[n] > max_len */
 #define BKV_DEV_BAD_COUNT 0x2 /* qcount[n][g] < 0 or >= C on entry */
 #define BKV_DEV_BAD_INDEX 0x4 /* bkv_beacon_rows: a row index >= S */
-#define BKV_DEV_WAIT_LIMIT 0x8 /* bkv_compact: a chunk waited past its bound for an earlier chunk's reads
-                                 (seconds; not expected) and left its rows unwritten */
 
 /* Aggregation of the observation rows' probabilities into a key's score. */
 enum bkv_aggregation { BKV_AGG_MAX = 0, BKV_AGG_MEAN = 1 };
@@ -109,10 +107,7 @@ typedef struct bkv_shape {
  *   [1] valid   : int32 [N][Hkv][RP], 1 for present rows;
  *   [2] lse     : float [N][Hkv][RP], natural-log row normaliser of the
  *                 softmax (+inf for absent rows);
- *   [3] select  : int32 [N][Hkv][2] = {first evicted index, kept count},
- *                 then bkv_compact's chunk flags (uint32 [N][Hkv][2]
- *                 [ceil(max_len / chunk rows)], chunk rows = 65536 / row
- *                 bytes), cleared by every bkv_compact call;
+ *   [3] select  : int32 [N][Hkv][2] = {first evicted index, kept count};
  *   [4] rope    : float2 [N][R+1][d/2] (cos, sin) tables;
  *   [5] beacons : int32 [N][Hq][nb+1]: the pick count, then the buffer rows
  *                 of the beacons in pick order;
@@ -264,11 +259,8 @@ int bkv_select(const bkv_shape *shape, const float *scores, const int32_t *len, 
  *
  * Must follow bkv_select on the same workspace, budget and stream.  Adds the
  * number of moved rows (per tensor) to the workspace statistic rows_moved.
- * The rows move in chunks of 64 KB, one workgroup each: a chunk reads all its
- * rows, marks them read in its flag, and writes only after every earlier
- * chunk of the same (slot, KV head, tensor) that still reads its
- * destinations has marked its own (a bounded wait; past the bound the chunk
- * is left unwritten and BKV_DEV_WAIT_LIMIT is set, which is not expected).
+ * One workgroup per (slot, KV head, tensor) moves its rows in increasing
+ * index order, in steps of 128 KB; no workgroup waits for another.
  */
 int bkv_compact(const bkv_shape *shape, void *K, void *V, int32_t *len, int32_t budget,
                 const int32_t *kept, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -282,11 +274,10 @@ int bkv_select_compact(const bkv_shape *shape, const float *scores, void *K, voi
  * bkv_select_compact_noalloc -- bkv_select_compact for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): no workspace argument; the same
- * selection, and the compaction with one workgroup per (slot, KV head,
- * tensor) stepping through its rows (it needs no chunk flags), use a scratch
- * array the library holds in device memory, 1 MiB per device
- * for the life of the process (status word, statistics, and the select table
- * of at most 131,040 (slot, KV head) units).
+ * selection and compaction kernels use a scratch array the library holds in
+ * device memory, 1 MiB per device for the life of the process (status word,
+ * statistics, and the select table of at most 131,040 (slot, KV head)
+ * units).
  *
  *   scores, K, V, len, budget, window, kept  as bkv_select_compact
  *   dev_status  int32 DEVICE pointer or NULL: receives this call's device

@@ -25,7 +25,6 @@ NOALLOC_MAX_UNITS = 131040  # bkv_select_compact_noalloc: (slot, KV head) units 
 DEV_BAD_LEN = 0x1
 DEV_BAD_COUNT = 0x2
 DEV_BAD_INDEX = 0x4
-DEV_WAIT_LIMIT = 0x8
 AGG_MAX, AGG_MEAN = 0, 1
 
 WS_OBS, WS_VALID, WS_LSE, WS_SELECT, WS_ROPE, WS_BEACONS, WS_BEACON_ROWS = range(7)

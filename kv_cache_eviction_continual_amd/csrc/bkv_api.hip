@@ -26,10 +26,7 @@ hipError_t launch_beacon_rows(const void*, int, const int32_t*, int, int, int, i
 hipError_t launch_select(const float*, const int32_t*, int, int, int, int, int, int32_t*, int32_t*, int32_t*,
                          hipStream_t);
 hipError_t launch_compact(void*, void*, const int32_t*, const int32_t*, int32_t*, int, int, int, int, int,
-                          unsigned long long*, uint32_t*, int32_t*, hipStream_t);
-hipError_t launch_compact_stepped(void*, void*, const int32_t*, const int32_t*, int32_t*, int, int, int, int, int,
-                                  unsigned long long*, hipStream_t);
-size_t compact_area_words(int, int, int);
+                          unsigned long long*, hipStream_t);
 hipError_t launch_select_fill(const float*, const int32_t*, const int32_t*, int, int, int, int, int, int32_t*,
                               int32_t*, int32_t*, hipStream_t);
 hipError_t launch_compact_fill(void*, void*, int32_t*, const int32_t*, int32_t*, int32_t*, int, int, int, int, int,
@@ -108,16 +105,11 @@ struct WsLayout {
   int RP;
 };
 
-// Header, then the select table and the compaction's work counter and chunk
-// flags (these depend on the shape only, so bkv_select and bkv_compact need
-// no R or nb), then the scoring intermediates.
-size_t select_table_end(const bkv_shape* s) {
-  return align256(kHeaderBytes + (size_t)s->n_seq * s->n_kv_heads * 2 * sizeof(int32_t));
-}
+// Header, then the select table (it depends on the shape only, so
+// bkv_select and bkv_compact need no R or nb), then the scoring
+// intermediates.
 size_t select_end(const bkv_shape* s) {
-  const int row_bytes = s->head_dim * elem_bytes(s->dtype);
-  return align256(select_table_end(s) +
-                  compact_area_words(s->n_seq * s->n_kv_heads, s->max_len, row_bytes) * sizeof(uint32_t));
+  return align256(kHeaderBytes + (size_t)s->n_seq * s->n_kv_heads * 2 * sizeof(int32_t));
 }
 
 bool layout(const bkv_shape* s, int R, int nb, WsLayout* out) {
@@ -431,10 +423,8 @@ int bkv_compact(const bkv_shape* shape, void* K, void* V, int32_t* len, int32_t 
   if (N == 0) return BKV_OK;
   const int32_t* sel = (const int32_t*)((unsigned char*)ws + kHeaderBytes);
   unsigned long long* moved = (unsigned long long*)((unsigned char*)ws + 8);
-  uint32_t* area = (uint32_t*)((unsigned char*)ws + select_table_end(shape));
   const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
-  return hip_status(launch_compact(K, V, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, area,
-                                   (int32_t*)ws, stream));
+  return hip_status(launch_compact(K, V, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, stream));
 }
 
 int bkv_select_compact(const bkv_shape* shape, const float* scores, void* K, void* V, int32_t* len, int32_t budget,
@@ -466,7 +456,7 @@ int bkv_select_compact_noalloc(const bkv_shape* shape, const float* scores, void
   if (e == hipSuccess) e = launch_select(scores, len, N, Hkv, shape->max_len, budget, window, kept, sel, words, stream);
   if (e == hipSuccess) {
     const int row_bytes = shape->head_dim * elem_bytes(shape->dtype);
-    e = launch_compact_stepped(K, V, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, stream);
+    e = launch_compact(K, V, kept, sel, len, N, Hkv, shape->max_len, budget, row_bytes, moved, stream);
   }
   if (e == hipSuccess && dev_status) {
     hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, stream, (const int32_t*)words, dev_status);

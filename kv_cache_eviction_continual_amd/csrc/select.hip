@@ -17,18 +17,18 @@
 // pass gives every thread a contiguous run of entries, so one block scan
 // ranks all kept (or evicted) entries in index order.
 //
-// compact_chunk_kernel: row i <- row kept[i] for i from the first evicted
-// index up to the kept count, in chunks of 64 KB of rows, one workgroup each
-// (see its description).  Because kept is ascending, kept[i] >= i: a
-// row is only ever read by a destination at or before its own index.
-// compact_kernel: the same move with one workgroup per (slot, KV head,
-// tensor), in steps of increasing index; a block-wide barrier after each
-// step's loads have returned orders every read of a row before its
-// overwrite.  It needs no workspace beyond the select table.
+// compact_unit_kernel: row i <- row kept[i] for i from the first evicted
+// index up to the kept count, one 1024-thread workgroup per (slot, KV head,
+// tensor) walking its rows in 128 KB steps (see its description).  Because
+// kept is ascending, kept[i] >= i: a row is only ever read by a destination
+// at or before its own index.  compact_kernel: the same walk with 256
+// threads and plain global loads, for units whose rows span 2 GB or more
+// (beyond the 32-bit offsets of the buffer instructions).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <climits>
 
 #include "bkv_device.hpp"
 
@@ -268,8 +268,9 @@ __device__ inline void nt_store16(unsigned char* p, nt_u32x4 v) {
 }
 constexpr int kCompactUnroll = 2;  // row groups per thread per step (more in flight measured slower)
 
-// One workgroup per (slot, KV head, tensor).  A step moves kCompactUnroll
-// groups of (256 / lanes per row) rows: every thread first waits for its own
+// One workgroup per (slot, KV head, tensor), for units whose rows span 2 GB
+// or more (compact_unit_kernel below covers the others).  A step moves
+// kCompactUnroll groups of (256 / lanes per row) rows: every thread first waits for its own
 // loads and stores, the block synchronises, then the loads of the next step
 // are issued (they read rows at or beyond the next step's first index, which
 // this step's stores never touch) followed by this step's stores (whose rows
@@ -329,124 +330,115 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(unsigned char*
 }
 
 // ---------------------------------------------------------------------------
-// Chunked order-preserving compaction
+// Order-preserving compaction, one workgroup per (unit, tensor)
 // ---------------------------------------------------------------------------
 //
-// The rows of a (unit, tensor) are cut into chunks of CR = kChunkBytes /
-// row_bytes rows, one workgroup each; chunk j moves the destinations [s_j,
-// e_j) = [j CR, (j + 1) CR) within [f, cnt) (f the first hole, cnt the kept
-// count).  It reads kept[i] >= i for i in [s_j, e_j): a later chunk reads
-// only rows at or beyond its own first destination, above every row chunk j
-// writes, and chunk j's own reads all return before its first store.  The
-// one hazard left is a row chunk j overwrites that an earlier chunk j' still
-// reads: a source of j' at or beyond s_j, which exists only while the last
-// source of j', kept[e_j' - 1], is >= s_j (at most (L - cnt) / CR + 1
-// earlier chunks).  So each chunk loads all its rows into registers,
-// publishes "read" in its flag, waits for the flags of the earlier chunks that
-// reach into its rows, then stores.  Blocks are numbered chunk-major, so an
-// earlier chunk of the same (unit, tensor) has a lower block index: each XCD
-// dispatches its blocks in index order, so while a block waits every
-// lower-indexed block is running or done, and it publishes its flag before
-// waiting on anything; the wait is also bounded (BKV_DEV_WAIT_LIMIT).  A
-// block has no stores outstanding when it waits for its loads, so its flag
-// follows its reads alone.  compact_prepare_kernel clears the flags before
-// every call (a kernel, not a memset node, so that the call can be captured
-// into a graph).
+// A step moves the destinations [i0, i0 + SR): every lane loads kUnitLoads
+// 16-byte pieces (rows i0 + r0 + b * RPP, b < kUnitLoads), so a step is
+// kUnitThreads * kUnitLoads * 16 bytes.  Its loads read rows kept[i] >= i,
+// at or beyond i0, which no earlier step writes; its stores go out after the
+// loads of every lane for this and all earlier steps have returned (each
+// lane waits for its own loads, then one barrier), and the rows it
+// overwrites are read only by destinations at or before them, loaded
+// already.  So the next step's loads are issued before this step's stores.
+// A store keeps its data registers until it completes, so three register
+// sets rotate and a set is loaded again two steps after its stores went out
+// (with two sets every step's loads waited for the previous step's stores).
+// Rows outside [f, cnt) take an offset past the end of the buffer
+// descriptor: such a load returns zero and such a store is dropped, without
+// a memory access, so all lanes issue the same instructions.  The kept
+// indices are staged in LDS, kUnitWindow at a time.  The window's LDS (just
+// over 80 KB) also limits a CU to one such workgroup, as do its registers
+// (over 64 per lane at 1024 lanes): 256 (unit, tensor) regions are
+// streamed at once, each contiguous, which measured faster than two
+// workgroups per CU and than 64 KB chunks of many units in flight together
+// (HBM pages are only hit densely when the rows in flight are).
 
-constexpr int kChunkBytes = 65536;                                    // bytes of rows per chunk
-constexpr int kChunkPieces = kChunkBytes / 16 / kCompactThreads;     // 16-byte loads per thread
-constexpr int kChunkWaitPolls = 1 << 22;                              // bound of one flag wait (seconds)
+constexpr int kUnitThreads = 1024;
+constexpr int kUnitLoads = 8;         // 16-byte loads per lane and step (128 KB steps)
+constexpr int kUnitWindow = 20480;    // kept indices staged in LDS at a time
+constexpr int kUnitLdsWords = kUnitWindow + 64;  // just over half of a CU's 160 KB of LDS
+constexpr int kUnitRsrcWord3 = 0x00020000;  // raw buffer descriptor, word 3 (32-bit data format)
+constexpr int kNtAux = 2;             // non-temporal cache policy of the buffer instructions
 
-__host__ __device__ inline int compact_chunk_rows(int row_bytes) { return kChunkBytes / row_bytes; }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Zeroes the chunk flags.
-__global__ void compact_prepare_kernel(uint32_t* flags, size_t words) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
-    flags[i] = 0u;
-}
-
-__global__ __launch_bounds__(kCompactThreads) void compact_chunk_kernel(
+template <int LPR>  // lanes per row: row bytes / 16
+__global__ __launch_bounds__(kUnitThreads) void compact_unit_kernel(
     unsigned char* __restrict__ K, unsigned char* __restrict__ V, const int32_t* __restrict__ kept,
-    const int32_t* __restrict__ sel, int32_t* __restrict__ len, int Hkv, int Lmax, int B, int row_bytes,
-    unsigned long long* __restrict__ rows_moved, uint32_t* __restrict__ flags, int units, int nchunk,
-    int32_t* __restrict__ ws_words) {
-  __shared__ int s_go;
+    const int32_t* __restrict__ sel, int32_t* __restrict__ len, int Hkv, int Lmax, int B,
+    unsigned long long* __restrict__ rows_moved) {
+  constexpr int RB = LPR * 16;                 // row bytes
+  constexpr int RPP = kUnitThreads / LPR;      // rows between a lane's pieces
+  constexpr int SR = RPP * kUnitLoads;         // rows per step
+  static_assert(kUnitWindow % SR == 0, "a window holds whole steps");
+  __shared__ int s_idx[kUnitLdsWords];
+  const size_t unit = blockIdx.x >> 1;
+  const int tensor = blockIdx.x & 1;
   const int tid = threadIdx.x;
-  const uint32_t items_per_chunk = 2u * (uint32_t)units;
-  const int j = (int)(blockIdx.x / items_per_chunk);
-  const uint32_t ut = blockIdx.x % items_per_chunk;  // (unit, tensor)
-  const size_t unit = ut >> 1;
-  const int tensor = (int)(ut & 1u);
-  const int lpr = row_bytes / 16;
-  const int CR = compact_chunk_rows(row_bytes);
-  const int c0 = j * CR;  // chunk j: destinations [c0, c0 + CR) within [f, cnt)
-  const int32_t* kept_u = kept + unit * (size_t)B;
-  // the kept indices of the chunk's rows go out with the select table entry
-  // (kept[i] = i below the first hole, so reading them needs no f)
-  const int rows_here = max(0, min(CR, B - c0));
-  int src[kChunkPieces];
-#pragma unroll
-  for (int b = 0; b < kChunkPieces; ++b) {
-    const int r = (b * kCompactThreads + tid) / lpr;
-    src[b] = r < rows_here ? kept_u[c0 + r] : 0;
-  }
   const int f = sel[2 * unit];
   const int cnt = sel[2 * unit + 1];
   if (cnt < 0) return;  // unit rejected by the selection
-  if (j == 0 && tid == 0) {
+  if (tid == 0) {
     if (tensor == 0 && unit % Hkv == 0) len[unit / Hkv] = cnt;  // no compaction block reads len
     if (cnt > f) atomicAdd(rows_moved, (unsigned long long)(cnt - f));
   }
-  const int start = max(f, c0);
-  const int end = min(cnt, c0 + CR);
-  if (start >= end) return;  // nothing of this chunk moves
-  uint32_t* uflags = flags + ut * (size_t)nchunk;
-  // the nearest earlier chunk, if it moves rows and its reads reach into this
-  // chunk's rows (its flag is read alongside the rows; usually set long since)
-  const bool dep = j > 0 && c0 - 1 >= f && kept_u[c0 - 1] >= start;
-  uint32_t early = 1u;
-  if (tid == 0 && dep) early = __hip_atomic_load(&uflags[j - 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  unsigned char* base = (tensor ? V : K) + unit * (size_t)Lmax * row_bytes;
-  nt_u32x4 v[kChunkPieces];
+  if (cnt <= f) return;
+  const int32_t* kept_u = kept + unit * (size_t)B;
+  const int nrec = Lmax * RB;  // < 2^31 (checked on the host)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (tensor ? V : K) + unit * (size_t)Lmax * RB, (short)0, nrec, kUnitRsrcWord3);
+  const int r0 = tid / LPR;
+  const int col = (tid % LPR) * 16;
+  for (int w0 = f; w0 < cnt; w0 += kUnitWindow) {
+    const int w1 = min(cnt, w0 + kUnitWindow);
+    for (int i = w0 + tid; i < w1; i += kUnitThreads) s_idx[i - w0] = kept_u[i];
+    __syncthreads();
+    auto issue = [&](u32x4* dst, int i0) {
 #pragma unroll
-  for (int b = 0; b < kChunkPieces; ++b) {
-    const int p = b * kCompactThreads + tid;
-    const int r = p / lpr;
-    if (c0 + r >= start && c0 + r < end) v[b] = nt_load16(base + (size_t)src[b] * row_bytes + (size_t)(p - r * lpr) * 16);
-  }
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // every row of the chunk has been read
-  if (tid == 0) {
-    __hip_atomic_store(&uflags[j], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int go = 1;
-    if (dep) {
-      // the earlier chunks that move rows and whose last source lies at or
-      // beyond this chunk's first moved row: the nearest one (read above),
-      // then further back
-      for (int jp = j - 1; jp >= 0 && go; --jp) {
-        const int last = (jp + 1) * CR - 1;  // last destination of chunk jp (jp < j: a whole chunk)
-        if (last < f || kept_u[last] < start) break;
-        uint32_t fl = jp == j - 1 ? early : 0u;
-        for (int polls = 0; fl == 0u; ++polls) {
-          if (polls >= kChunkWaitPolls) {
-            go = 0;
-            set_status(ws_words, BKV_DEV_WAIT_LIMIT);
-            break;
-          }
-          if (polls > 0) __builtin_amdgcn_s_sleep(2);
-          fl = __hip_atomic_load(&uflags[jp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+      for (int b = 0; b < kUnitLoads; ++b) {
+        const int i = i0 + r0 + b * RPP;
+        dst[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, i < w1 ? s_idx[i - w0] * RB + col : nrec, 0, kNtAux);
       }
-    }
-    s_go = go;
-  }
-  __syncthreads();
-  if (!s_go) return;  // a wait passed its bound: this chunk's rows are left unwritten
+    };
+    auto put = [&](const u32x4* src, int i0) {
 #pragma unroll
-  for (int b = 0; b < kChunkPieces; ++b) {
-    const int p = b * kCompactThreads + tid;
-    const int r = p / lpr;
-    if (c0 + r >= start && c0 + r < end) nt_store16(base + (size_t)(c0 + r) * row_bytes + (size_t)(p - r * lpr) * 16, v[b]);
+      for (int b = 0; b < kUnitLoads; ++b) {
+        const int i = i0 + r0 + b * RPP;
+        __builtin_amdgcn_raw_buffer_store_b128(src[b], rs, i < w1 ? i * RB + col : nrec, 0, kNtAux);
+      }
+    };
+    // waits for this lane's loads into x (the compiler counts the stores
+    // issued after them, which stay in flight)
+    auto landed = [&](const u32x4* x) {
+#pragma unroll
+      for (int b = 0; b < kUnitLoads; ++b) __asm__ volatile("" ::"v"(x[b]));
+    };
+    u32x4 a[kUnitLoads], c[kUnitLoads], e[kUnitLoads];
+    issue(a, w0);
+    landed(a);
+    int i0 = w0;
+    while (true) {
+      __syncthreads();  // every lane's loads of the step at i0 have returned
+      if (i0 + SR < w1) issue(c, i0 + SR);
+      put(a, i0);
+      i0 += SR;
+      if (i0 >= w1) break;
+      landed(c);
+      __syncthreads();
+      if (i0 + SR < w1) issue(e, i0 + SR);
+      put(c, i0);
+      i0 += SR;
+      if (i0 >= w1) break;
+      landed(e);
+      __syncthreads();
+      if (i0 + SR < w1) issue(a, i0 + SR);
+      put(e, i0);
+      i0 += SR;
+      if (i0 >= w1) break;
+      landed(a);
+    }
+    __syncthreads();  // the next window's staging overwrites s_idx
   }
 }
 
@@ -752,40 +744,37 @@ hipError_t launch_select(const float* scores, const int32_t* len, int N, int Hkv
   return hipGetLastError();
 }
 
-// One block per (unit, tensor), stepping through its rows (no workspace
-// beyond the select table).
-hipError_t launch_compact_stepped(void* K, void* V, const int32_t* kept, const int32_t* sel, int32_t* len, int N,
-                                  int Hkv, int Lmax, int B, int row_bytes, unsigned long long* rows_moved,
-                                  hipStream_t st) {
-  hipLaunchKernelGGL(compact_kernel, dim3(N * Hkv * 2), dim3(kCompactThreads), 0, st, (unsigned char*)K, (unsigned char*)V, kept,
-                     sel, len, Hkv, Lmax, B, row_bytes, rows_moved);
-  return hipGetLastError();
-}
-
-// Words of the chunked compaction's flags.
-size_t compact_area_words(int units, int Lmax, int row_bytes) {
-  const int cr = compact_chunk_rows(row_bytes);
-  const size_t nchunk = Lmax > 0 ? ((size_t)Lmax + cr - 1) / cr : 1;
-  return 2 * (size_t)units * nchunk;
-}
-
-// The chunked compaction: the flags cleared, then one block per (chunk, unit,
-// tensor), chunk-major.
+// The order-preserving compaction: one block per (unit, tensor); the
+// 1024-thread kernel where a unit's rows span less than 2 GB, else the
+// 256-thread one with 64-bit addresses.  Needs no workspace beyond the select
+// table.
 hipError_t launch_compact(void* K, void* V, const int32_t* kept, const int32_t* sel, int32_t* len, int N, int Hkv,
-                          int Lmax, int B, int row_bytes, unsigned long long* rows_moved, uint32_t* flags,
-                          int32_t* ws_words, hipStream_t st) {
-  const int units = N * Hkv;
+                          int Lmax, int B, int row_bytes, unsigned long long* rows_moved, hipStream_t st) {
+  const size_t units = (size_t)N * Hkv;
   if (units == 0) return hipSuccess;
-  const int cr = compact_chunk_rows(row_bytes);
-  const int nchunk = Lmax > 0 ? (Lmax + cr - 1) / cr : 1;
-  const size_t words = compact_area_words(units, Lmax, row_bytes);
-  hipLaunchKernelGGL(compact_prepare_kernel, dim3((unsigned)std::min<size_t>((words + 255) / 256, 1024)), dim3(256), 0,
-                     st, flags, words);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_chunk_kernel, dim3((unsigned)(2 * (size_t)units * nchunk)), dim3(kCompactThreads), 0, st,
-                     (unsigned char*)K, (unsigned char*)V, kept, sel, len, Hkv, Lmax, B, row_bytes, rows_moved, flags,
-                     units, nchunk, ws_words);
+  const dim3 grid((unsigned)(2 * units));
+  unsigned char* k = (unsigned char*)K;
+  unsigned char* v = (unsigned char*)V;
+  if ((size_t)Lmax * row_bytes <= (size_t)INT32_MAX) {
+    switch (row_bytes) {
+      case 128:
+        hipLaunchKernelGGL(compact_unit_kernel<8>, grid, dim3(kUnitThreads), 0, st, k, v, kept, sel, len, Hkv, Lmax,
+                           B, rows_moved);
+        return hipGetLastError();
+      case 256:
+        hipLaunchKernelGGL(compact_unit_kernel<16>, grid, dim3(kUnitThreads), 0, st, k, v, kept, sel, len, Hkv, Lmax,
+                           B, rows_moved);
+        return hipGetLastError();
+      case 512:
+        hipLaunchKernelGGL(compact_unit_kernel<32>, grid, dim3(kUnitThreads), 0, st, k, v, kept, sel, len, Hkv, Lmax,
+                           B, rows_moved);
+        return hipGetLastError();
+      default:
+        break;
+    }
+  }
+  hipLaunchKernelGGL(compact_kernel, grid, dim3(kCompactThreads), 0, st, k, v, kept, sel, len, Hkv, Lmax, B, row_bytes,
+                     rows_moved);
   return hipGetLastError();
 }
 

@@ -1,15 +1,15 @@
-"""The chunked order-preserving compaction (64 KB of rows per workgroup) on
-eviction patterns that make chunks depend on one another: a chunk may write
-only after every earlier chunk that still reads its destinations has read
-them.  Each case compares K and V bit for bit with the oracle's gather
-(orc_compact) of the oracle's kept set (orc_select, which equals the GPU's
-on these tie-free scores), checks the rows at or beyond the kept count
-untouched, the lengths, the rows_moved statistic and a clear status word,
-and checks the result equal to the block-stepped compaction of
-bkv_select_compact_noalloc on the same inputs.
-
-Chunk rows: 65536 / row bytes (256 for bf16 d = 128, 128 for binary32
-d = 128, 512 for bf16 d = 64)."""
+"""The order-preserving compaction on eviction patterns that move rows far
+and across many steps: one workgroup per (slot, KV head, tensor) walks its
+rows in 128 KB steps (512 rows for bf16 d = 128, 256 for binary32 d = 128,
+1024 for bf16 d = 64), loading each step before the previous step's stores,
+with the kept indices staged in LDS 20,480 at a time.  Each case compares K
+and V bit for bit with the oracle's gather (orc_compact) of the oracle's kept
+set (orc_select, which equals the GPU's on these tie-free scores), checks the
+rows at or beyond the kept count untouched, the lengths, the rows_moved
+statistic and a clear status word, and checks the result equal to
+bkv_select_compact_noalloc's on the same inputs.  Budgets above 20,480 rows
+take several index windows; units whose rows span 2 GB or more take the
+256-thread kernel with 64-bit addresses."""
 import numpy as np
 import pytest
 import torch
@@ -35,7 +35,7 @@ def pattern_scores(kind, N, Hkv, Lmax, lengths, gen):
                 base = L - idx
             elif kind == "every4":   # every fourth row wins
                 base = np.where(idx % 4 == 0, 2.0 * L, 0.0) + idx
-            elif kind == "runs":     # evicted runs of 300 rows, longer than a chunk, at chunk edges
+            elif kind == "runs":     # evicted runs of 300 rows
                 base = np.where(((idx + 100) // 300) % 2 == 0, 2.0 * L, 0.0) + idx
             else:                    # random
                 base = gen.permutation(L).astype(np.float64)
@@ -47,7 +47,7 @@ CASES = [
     # (dtype, d, Lmax, lengths, budget, window)
     (torch.bfloat16, 128, 3000, (3000, 2923), 700, 16),
     (torch.bfloat16, 128, 1300, (1300, 1300), 1024, 32),
-    (torch.bfloat16, 128, 3000, (3000, 2811), 2000, 16),  # 1,000 holes: up to four earlier chunks in a wait
+    (torch.bfloat16, 128, 3000, (3000, 2811), 2000, 16),  # 1,000 holes: sources up to two steps ahead
     (torch.float32, 128, 1000, (1000, 911), 300, 8),
     (torch.bfloat16, 64, 2500, (2500, 2047), 900, 0),
 ]
@@ -55,7 +55,7 @@ CASES = [
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 @pytest.mark.parametrize("kind", ["front", "back", "every4", "runs", "random"])
-def test_chunked_compaction_matches_the_oracle_gather(case, kind):
+def test_compaction_matches_the_oracle_gather(case, kind):
     dtype, d, Lmax, lengths, B, W = CASES[case]
     N, Hkv, Hq = 2, 2, 4
     print("case: dtype=%s d=%d Lmax=%d lengths=%s B=%d W=%d pattern=%s" % (dtype, d, Lmax, lengths, B, W, kind),
@@ -94,7 +94,7 @@ def test_chunked_compaction_matches_the_oracle_gather(case, kind):
     assert bkv.ws_rows_moved(ws) == moved
     assert length.cpu().tolist() == [min(L, B) for L in lengths]
 
-    # the block-stepped compaction on the same inputs gives the same rows
+    # the allocation-free entry point on the same inputs gives the same rows
     length2 = torch.tensor(lengths, dtype=torch.int32, device="cuda")
     kept2 = torch.empty_like(kept)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -106,7 +106,7 @@ def test_chunked_compaction_matches_the_oracle_gather(case, kind):
     assert np.array_equal(synth.to_numpy_storage(V2), Vn)
 
 
-def test_short_and_rejected_units_around_chunked_ones():
+def test_short_and_rejected_units_around_moved_ones():
     """A slot whose length is at most the budget moves nothing (kept[i] = i),
     a slot with an invalid length is rejected (BKV_DEV_BAD_LEN, its rows and
     length untouched), and the other slots are compacted as the oracle says."""
@@ -143,3 +143,70 @@ def test_short_and_rejected_units_around_chunked_ones():
                 ref = np.ascontiguousarray(old[n, h])
                 oracle.compact(ref, ko[:cnt])
                 assert np.array_equal(new[n, h], ref), (n, h)
+
+
+@pytest.mark.parametrize("dtype,d,Lmax,lengths,B,W", [
+    (torch.bfloat16, 64, 50000, (50000, 41000), 45000, 32),   # three index windows, 1024-row steps
+    (torch.float32, 128, 30000, (30000, 29000), 25000, 16),   # two windows, 256-row steps
+])
+def test_budgets_above_one_index_window(dtype, d, Lmax, lengths, B, W):
+    """Kept counts above 20,480 rows stage their indices in several windows;
+    the rows still equal the oracle's gather."""
+    N, Hkv, Hq = len(lengths), 1, 1
+    print("case: windows dtype=%s d=%d Lmax=%d lengths=%s B=%d" % (dtype, d, Lmax, lengths, B), flush=True)
+    gen = np.random.default_rng(Lmax)
+    shape = bkv.make_shape(N, Hkv, Hq, d, Lmax, dtype)
+    scores_np = pattern_scores("random", N, Hkv, Lmax, lengths, gen)
+    torch.manual_seed(3)
+    K = torch.randn(N, Hkv, Lmax, d, device="cuda").to(dtype)
+    V = torch.randn(N, Hkv, Lmax, d, device="cuda").to(dtype)
+    K_old, V_old = synth.to_numpy_storage(K), synth.to_numpy_storage(V)
+    length = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    kept = torch.empty(N, Hkv, B, dtype=torch.int32, device="cuda")
+    ws = bkv.alloc_workspace(shape, 4, 4)
+    bkv.bkv_select_compact(shape, torch.from_numpy(scores_np).cuda(), K, V, length, B, W, kept, ws)
+    torch.cuda.synchronize()
+    assert bkv.bkv_read_device_status(ws) == 0
+    Kn, Vn = synth.to_numpy_storage(K), synth.to_numpy_storage(V)
+    for n, L in enumerate(lengths):
+        ko = oracle.select(scores_np[n, 0].astype(np.float64), L, B, W)
+        cnt = min(L, B)
+        for new, old in ((Kn, K_old), (Vn, V_old)):
+            ref = np.ascontiguousarray(old[n, 0])
+            oracle.compact(ref, ko[:cnt])
+            assert np.array_equal(new[n, 0], ref), n
+    assert length.cpu().tolist() == [min(L, B) for L in lengths]
+
+
+def test_rows_spanning_more_than_2gb_take_the_64bit_kernel():
+    """A binary32 d = 128 unit of 4,200,000 rows spans 2.15 GB, past the
+    32-bit offsets of the buffer instructions: the 256-thread kernel moves
+    it.  The 1,000 evicted rows lie near the end, so about 1,000 rows move;
+    every row is checked against the oracle's kept set on the device."""
+    dtype, d, L, W = torch.float32, 128, 4_200_000, 64
+    B = L - 1000
+    print("case: 2 GB unit, L=%d B=%d" % (L, B), flush=True)
+    shape = bkv.make_shape(1, 1, 1, d, L, dtype)
+    gen = np.random.default_rng(11)
+    s = (2.0 + gen.permutation(L).astype(np.float64) / L).astype(np.float32)   # distinct, in [2, 3)
+    lo = L - 2000
+    s[lo:lo + 1000] = (gen.permutation(1000).astype(np.float64) / 1000.0).astype(np.float32)  # the evicted rows
+    ko = oracle.select(s.astype(np.float64), L, B, W)
+    assert int(ko[lo - 1]) == lo - 1 and int(ko[lo]) == lo + 1000  # the holes are exactly [lo, lo + 1000)
+    K = torch.empty(1, 1, L, d, device="cuda", dtype=dtype)
+    K.view(-1).copy_(torch.arange(L * d, device="cuda", dtype=torch.int32).view(torch.float32))  # distinct rows
+    V = K.flip(-1).contiguous()
+    K0, V0 = K.clone(), V.clone()
+    length = torch.tensor([L], dtype=torch.int32, device="cuda")
+    kept = torch.empty(1, 1, B, dtype=torch.int32, device="cuda")
+    ws = bkv.alloc_workspace(shape, 4, 4)
+    bkv.bkv_select_compact(shape, torch.from_numpy(s[None, None]).cuda(), K, V, length, B, W, kept, ws)
+    torch.cuda.synchronize()
+    assert bkv.bkv_read_device_status(ws) == 0
+    assert np.array_equal(kept[0, 0].cpu().numpy(), ko)
+    idx = torch.from_numpy(ko.astype(np.int64)).cuda()
+    for new, old in ((K, K0), (V, V0)):
+        assert torch.equal(new[0, 0, :B].view(torch.int32), old[0, 0].index_select(0, idx).view(torch.int32))
+        assert torch.equal(new[0, 0, B:].view(torch.int32), old[0, 0, B:].view(torch.int32))
+    assert bkv.ws_rows_moved(ws) == 2 * (B - lo)
+    assert int(length.item()) == B
