@@ -234,8 +234,9 @@ class Group:
         self.sl = slice(a, b)
         self.shape = bkv.make_shape(b - a, w.n_kv_heads, w.n_q_heads, w.head_dim, w.max_len, st.K.dtype)
         self.ws, self.main, self.side = ws, main, side
-        self.ready = None   # beacon FPS of the group's next pass, enqueued on its side stream
-        self.scored = None  # the group's last scoring
+        self.ready = None     # beacon FPS of the group's next pass, enqueued on its side stream
+        self.scored = None    # the group's last scoring
+        self.released = None  # what the group's next beacon FPS waits for (its scoring, or its compaction)
 
 
 HEAD_STAGES = ("grow", "fps_update", "beacon_picks", "score")
@@ -254,7 +255,13 @@ class Schedule:
     compacts pass i.  The ingest only follows pass i's beacon FPS (same
     stream; scoring reads copies of the picked rows, not the buffers); the
     beacon FPS of pass i + 1 waits for pass i's scoring (the reader of the
-    picks), and pass i + 1's scoring waits for it.  With several groups
+    picks), or with picks_after_tail for its compaction, and pass i + 1's
+    scoring waits for it.  A compaction workgroup fills a CU's registers, so
+    an FPS wave on a CU keeps compaction blocks off it: started after the
+    compaction, the beacon FPS runs beside the next pass's new-token append
+    instead (measured faster for the order-preserving layout, whose
+    compaction is long; the hole-filling layout's short one-call tail keeps
+    the earlier start).  With several groups
     (pipelined), each group has its own main stream and workspace (the side
     stream is shared), and the groups' scorings take turns (each waits for
     the previous one), so one group's selection and compaction run beside the
@@ -263,9 +270,10 @@ class Schedule:
     bkv_score_picked, which together are bkv_score).  `ev` is a dict of
     (start, end) event pairs per stage, recorded for group 0, or None."""
 
-    def __init__(self, st, grow, tail, overlap, tail_stages=("select", "compact"), groups=1):
+    def __init__(self, st, grow, tail, overlap, tail_stages=("select", "compact"), groups=1, picks_after_tail=False):
         self.st, self.grow, self.tail, self.overlap = st, grow, tail, overlap
         self.tail_stages = tail_stages
+        self.picks_after_tail = picks_after_tail
         assert overlap or groups == 1
         # serial: the current stream.  Overlapped: every group on a stream of its own and one side stream for
         # all groups, all taken from torch's pool in a row, none of them the current (default) stream: a process
@@ -297,8 +305,8 @@ class Schedule:
         self.st.ingest(i, g, side)
         if ev is not None:
             ev["fps_update"][1].record(side)
-        if g.scored is not None:
-            side.wait_event(g.scored)
+        if g.released is not None:
+            side.wait_event(g.released)
         if ev is not None:
             ev["beacon_picks"][0].record(side)
         self.st.picks(g, side)
@@ -315,6 +323,7 @@ class Schedule:
             if g.ready is None:
                 g.scored = torch.cuda.Event()
                 g.scored.record(g.main)
+                g.released = g.scored
                 self._side_work(i, g, None)
 
     def run(self, i, ev=None):
@@ -346,8 +355,16 @@ class Schedule:
                     g.scored = torch.cuda.Event()
                     g.scored.record(m)
                     self.last_scored = g.scored
-                    self._side_work(i + 1, g, e)  # measured as this pass's ingest and beacon FPS stages
+                    if not self.picks_after_tail:
+                        g.released = g.scored
+                        self._side_work(i + 1, g, e)  # measured as this pass's ingest and beacon FPS stages
                 self.tail(i, rec, g)
+                if self.overlap and self.picks_after_tail:
+                    # the next beacon FPS waits for the compaction (whose workgroups fill whole CUs) and runs
+                    # beside the next pass's new-token append; the ingest still overlaps the scoring
+                    g.released = torch.cuda.Event()
+                    g.released.record(m)
+                    self._side_work(i + 1, g, e)
 
 
 def new_events(sched):
@@ -1003,6 +1020,9 @@ def main():
     ap.add_argument("--no-hole-fill", action="store_true", help="skip the hole-filling layout phase")
     ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped and pipelined schedules")
     ap.add_argument("--groups", type=int, default=3, help="slot groups of the pipelined schedule")
+    ap.add_argument("--picks-after-scoring", action="store_true",
+                    help="order-preserving overlapped and pipelined schedules: start the beacon FPS of pass i+1 when "
+                         "pass i's scoring ends (default: when its compaction ends)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time for the CPU baseline")
     ap.add_argument("--no-all-cores", action="store_true", help="skip the all-host-threads oracle timing")
     ap.add_argument("--workload", type=int, default=CFG, choices=(3, 4, 5),
@@ -1064,21 +1084,24 @@ def main():
     overlapped = pipelined = None
     if not args.no_overlap:
         log("timing the overlapped schedule")
-        el, sm, sp, _ = timed_passes(Schedule(st, grow, tail, True), args.warmup, K)
+        el, sm, sp, _ = timed_passes(Schedule(st, grow, tail, True, picks_after_tail=not args.picks_after_scoring),
+                                     args.warmup, K)
         overlapped = {
-            "schedule": "the ingest and beacon FPS of pass i+1 run on a second stream (default priority) while pass i "
-                        "scores, selects and compacts; same work per pass",
+            "schedule": "the ingest of pass i+1 runs on a second stream (default priority) while pass i scores, and "
+                        "its beacon FPS once pass i has compacted (beside pass i+1's new-token append; with "
+                        "--picks-after-scoring once pass i has scored); same work per pass",
             "passes_per_s": K / el,
             "ms_per_step": el * 1e3 / K,
             "stage_ms": sm,
             "stage_ms_p10_p50_p90": sp,
         }
         log("timing the pipelined schedule (%d slot groups)" % args.groups)
-        el, sm, sp, _ = timed_passes(Schedule(st, grow, tail, True, groups=args.groups), args.warmup, K)
+        el, sm, sp, _ = timed_passes(Schedule(st, grow, tail, True, groups=args.groups,
+                                              picks_after_tail=not args.picks_after_scoring), args.warmup, K)
         pipelined = {
             "schedule": "the slots split into %d groups, each with its own streams and workspace; the groups' scorings "
                         "take turns, so one group selects and compacts while the next one scores; ingest and beacon "
-                        "FPS of pass i+1 overlapped as above; same work per pass; stage times of group 0"
+                        "FPS of pass i+1 on the side stream as above; same work per pass; stage times of group 0"
                         % args.groups,
             "groups": args.groups,
             "passes_per_s": K / el,

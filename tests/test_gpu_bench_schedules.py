@@ -2,9 +2,9 @@
 Qwen3-4B, cache 2176 -> 2048), in the launch configurations bench.py
 times: two eviction passes run serially (one stream) and pipelined (three slot
 groups with their own workspaces and streams, ingest and beacon FPS of the
-next pass on a side stream), each appending the period's new tokens first,
-leave bit-identical caches, scores and kept
-indices.  Together with the full-size oracle checks of the single-call path,
+next pass on a side stream, the beacon FPS started after the compaction as
+the bench does, or after the scoring), each appending the period's new
+tokens first, leave bit-identical caches, scores and kept indices.  Together with the full-size oracle checks of the single-call path,
 this ties the reported throughput to results the oracle vouches for."""
 import pytest
 import torch
@@ -15,7 +15,7 @@ from kv_cache_eviction_continual_amd import bkv, configs
 pytestmark = pytest.mark.gpu
 
 
-def _run(bench, st, groups, passes):
+def _run(bench, st, groups, passes, picks_after_tail=False):
     w = st.w
 
     def grow(i, g):
@@ -30,7 +30,7 @@ def _run(bench, st, groups, passes):
         bkv.bkv_compact(g.shape, st.K[g.sl], st.V[g.sl], st.length[g.sl], w.budget, st.kept[g.sl], g.ws)
         rec("compact", 1)
 
-    sched = bench.Schedule(st, grow, tail, groups > 0, groups=max(groups, 1))
+    sched = bench.Schedule(st, grow, tail, groups > 0, groups=max(groups, 1), picks_after_tail=picks_after_tail)
     for i in range(passes):
         sched.run(i)
     torch.cuda.synchronize()
@@ -51,17 +51,19 @@ def test_serial_and_pipelined_passes_agree_at_full_size():
     snap = {k: getattr(st, k).clone() for k in ("K", "V", "qbuf", "qcount")}
     _run(bench, st, 0, 2)  # serial
     ref = {k: getattr(st, k).clone() for k in ("K", "V", "scores", "kept", "length")}
-    for k, v in snap.items():
-        getattr(st, k).copy_(v)
-    st.scores.zero_()
-    st.kept.fill_(-7)
-    torch.cuda.synchronize()  # the restored state is in place before other streams start on it
-    _run(bench, st, 3, 2)  # pipelined, three slot groups (the bench default)
-    for k in ("K", "V", "scores", "kept", "length"):
-        a, b = getattr(st, k), ref[k]
-        if k == "scores":
-            a, b = a[:, :, :w.length], b[:, :, :w.length]
-        assert torch.equal(_bits(a) if a.is_floating_point() else a, _bits(b) if b.is_floating_point() else b), k
+    for after_tail in (True, False):  # the bench default first
+        for k, v in snap.items():
+            getattr(st, k).copy_(v)
+        st.scores.zero_()
+        st.kept.fill_(-7)
+        torch.cuda.synchronize()  # the restored state is in place before other streams start on it
+        _run(bench, st, 3, 2, picks_after_tail=after_tail)  # pipelined, three slot groups (the bench default)
+        for k in ("K", "V", "scores", "kept", "length"):
+            a, b = getattr(st, k), ref[k]
+            if k == "scores":
+                a, b = a[:, :, :w.length], b[:, :, :w.length]
+            assert torch.equal(_bits(a) if a.is_floating_point() else a, _bits(b) if b.is_floating_point() else b), \
+                (k, after_tail)
     log("  serial and pipelined passes agree on %d units" % (st.N * w.n_kv_heads))
 
 
