@@ -23,7 +23,8 @@
  *     including the workspace; the library never allocates, frees or
  *     synchronises (bkv_read_device_status excepted) and keeps no state
  *     between calls, except for the one scratch array per device of
- *     bkv_select_compact_noalloc, which takes no workspace.
+ *     bkv_select_compact_noalloc, which takes no workspace, and the
+ *     process-wide debug-copy switch (bkv_set_debug_copies).
  *   - Work is enqueued on `stream` (0 = the null stream), in call order.
  *   - Tensors are dense and row-major in the index order written next to
  *     them.  N = shape->n_seq, Hkv = shape->n_kv_heads, Hq =
@@ -103,7 +104,9 @@ typedef struct bkv_shape {
  *   [0] obs     : rotated observation rows [N][Hkv][RP][d], storage type,
  *                 RP = G*(R+nb) rounded up to 32; row g*(R+nb)+r holds recent
  *                 query r of query head h*G+g, row g*(R+nb)+R+b its beacon b;
- *                 absent rows are zero;
+ *                 absent rows are zero.  Written by the scoring calls only
+ *                 while debug copies are on (bkv_set_debug_copies), else left
+ *                 as it was;
  *   [1] valid   : int32 [N][Hkv][RP], 1 for present rows;
  *   [2] lse     : float [N][Hkv][RP], natural-log row normaliser of the
  *                 softmax (+inf for absent rows);
@@ -433,6 +436,17 @@ int bkv_read_device_status(const void *ws, int32_t *status_out, hipStream_t stre
 
 /* Zeroes the status word and statistics (first 256 bytes of ws) on `stream`. */
 int bkv_reset_device_status(void *ws, hipStream_t stream);
+
+/*
+ * Debug copies: while on (on != 0), the scoring calls (bkv_score,
+ * bkv_score_picked, bkv_score_picked_agg, bkv_score_picked_capture) also
+ * write the rotated observation rows they score with to the workspace
+ * region [0] obs, for checking the rotation; off by default, since the
+ * scores do not need them (at 4,608 units of 128 rows, d = 128 bf16, they
+ * are 151 MB of writes per call).  Process-wide, for calls enqueued after it
+ * returns; returns the previous setting (0 or 1).  Enqueues nothing.
+ */
+int32_t bkv_set_debug_copies(int32_t on);
 
 #ifdef __cplusplus
 }

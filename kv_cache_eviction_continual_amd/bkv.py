@@ -54,6 +54,7 @@ EXPORTS = (
     "bkv_status_string",
     "bkv_read_device_status",
     "bkv_reset_device_status",
+    "bkv_set_debug_copies",
 )
 
 
@@ -132,6 +133,8 @@ def load() -> ctypes.CDLL:
     L.bkv_fps_full.restype = ctypes.c_int
     L.bkv_status_string.argtypes = [ctypes.c_int]
     L.bkv_status_string.restype = ctypes.c_char_p
+    L.bkv_set_debug_copies.argtypes = [I32]
+    L.bkv_set_debug_copies.restype = I32
     L.bkv_read_device_status.argtypes = [P, ctypes.POINTER(I32), P]
     L.bkv_read_device_status.restype = ctypes.c_int
     L.bkv_reset_device_status.argtypes = [P, P]
@@ -408,6 +411,12 @@ def bkv_fps_full(shape: Shape, hist, n: int, k: int, picks, ws, stream=None) -> 
     hp, pk, w = _on_gpu(_dev(hist, "hist", _storage_dtype(shape), _count(N, Hq, n, d), optional=n <= 0),
                         _dev(picks, "picks", torch.int32, _count(N, Hq, k), optional=k <= 0), _ws(ws))
     _check(load().bkv_fps_full(ctypes.byref(shape), hp, n, k, pk, w, _nbytes(ws), _stream(stream)))
+
+
+def bkv_set_debug_copies(on: bool) -> bool:
+    """Turns the scoring calls' copy of the rotated observation rows (workspace
+    region obs) on or off, process-wide; returns the previous setting."""
+    return bool(load().bkv_set_debug_copies(1 if on else 0))
 
 
 def bkv_status_string(status: int) -> str:

@@ -1,6 +1,8 @@
 // bkv_api.hip -- host side of the libbkv C ABI (argument checks, workspace
 // layout, kernel dispatch).  Declarations and contracts: include/bkv.h.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include <mutex>
@@ -170,6 +172,11 @@ int check_score_args(const bkv_shape* shape, const void* K, const int32_t* len, 
 
 }  // namespace
 
+// Whether the scoring calls also write the rotated observation rows to the
+// workspace (process-wide; off unless bkv_set_debug_copies turned it on).
+static std::atomic<int> g_debug_copies{0};
+static bool debug_copies_on() { return g_debug_copies.load(std::memory_order_relaxed) != 0; }
+
 // The RoPE tables and the score kernel, with the beacon picks already in ws.
 int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, const void* recent,
                   const int32_t* recent_pos, int32_t R, int32_t nb, const int32_t* pos_now, double rope_theta,
@@ -180,7 +187,7 @@ int enqueue_score(const bkv_shape* shape, const void* K, const int32_t* len, con
   unsigned char* base = (unsigned char*)ws;
   int32_t* words = (int32_t*)ws;
   float2* tab = (float2*)(base + w.rope);
-  void* obs = base + w.obs;
+  void* obs = debug_copies_on() ? base + w.obs : nullptr;  // null: the kernel skips the copy
   int32_t* valid = (int32_t*)(base + w.valid);
   float* lse = (float*)(base + w.lse);
   const int32_t* beacons = (const int32_t*)(base + w.beacons);
@@ -537,6 +544,8 @@ int bkv_read_device_status(const void* ws, int32_t* status_out, hipStream_t stre
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   return hip_status(e);
 }
+
+int32_t bkv_set_debug_copies(int32_t on) { return g_debug_copies.exchange(on != 0 ? 1 : 0) != 0 ? 1 : 0; }
 
 int bkv_reset_device_status(void* ws, hipStream_t stream) {
   if (!ws) return BKV_E_NULL;

@@ -339,12 +339,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(score_w
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) x[s2] = MF::load_raw(src, s2, lane);
     RopeFrag<DT, D>::rotate(x, tab + ((size_t)n * (R + 1) + (k < R ? k : R)) * H, lane >> 5);
-    unsigned char* orow = reinterpret_cast<unsigned char*>(obs + (unit * RP + myrow) * (size_t)D);
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
       if (!row_valid) x[s2] = MF::zero_raw();
-      MF::store_raw(orow, s2, lane, x[s2]);
       qf[s2] = MF::frag(x[s2]);
+    }
+    if (obs != nullptr) {  // the debug copy of the rotated rows
+      unsigned char* orow = reinterpret_cast<unsigned char*>(obs + (unit * RP + myrow) * (size_t)D);
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) MF::store_raw(orow, s2, lane, x[s2]);
     }
     if (lane < 32) obs_valid[unit * RP + myrow] = row_valid ? 1 : 0;
   }

@@ -35,3 +35,18 @@ def bkv():
     import kv_cache_eviction_continual_amd as pkg
 
     return pkg.lib()
+
+
+@pytest.fixture(autouse=True)
+def _debug_copies(request):
+    """GPU tests compare the rotated observation rows that the scoring calls
+    copy to the workspace when debug copies are on: turn the copies on for
+    each GPU test and restore the previous setting after it."""
+    if request.node.get_closest_marker("gpu") is None:
+        yield
+        return
+    from kv_cache_eviction_continual_amd import bkv as b
+
+    prev = b.bkv_set_debug_copies(True)
+    yield
+    b.bkv_set_debug_copies(prev)

@@ -437,3 +437,36 @@ def test_score_in_two_calls_equals_score():
             assert np.array_equal(bk[n, hq, 1:1 + len(picks)], picks)
             rows = np_storage(v2["beacon_rows"][n, hq, :len(picks)])
             assert np.array_equal(rows, qb[n, hq][picks]), "beacon row copies differ from the buffer rows"
+
+
+def test_debug_copies_off_leave_obs_untouched_and_scores_unchanged():
+    """With debug copies off (the library's default) the scoring calls leave
+    the workspace's obs region as it was and give the same scores, lse and
+    validity flags, bit for bit, as with them on (which the other tests
+    use to check the rotated rows)."""
+    w = configs.get(2)
+    inp = make_inputs(w, N=2, steps=700)
+    g = GpuRun(inp)
+    for blk in inp.blocks:
+        g.ingest(blk)
+    g.score()
+    torch.cuda.synchronize()
+    v = g.views()
+    ref_scores = g.scores.clone()
+    ref = {k: v[k].clone() for k in ("valid", "lse")}
+    L = int(inp.length[0])
+    v["obs"].view(torch.int16 if v["obs"].element_size() == 2 else torch.int32).fill_(0x1357)
+    scores2 = torch.full_like(g.scores, float("nan"))
+    prev = bkv.bkv_set_debug_copies(False)
+    assert prev is True  # the GPU tests run with the copies on
+    try:
+        bkv.bkv_score_picked(g.shape, inp.K, g.length, inp.recent, g.recent_pos, w.n_recent, w.n_beacons, g.pos_now,
+                             w.rope_theta, scores2, g.ws)
+        torch.cuda.synchronize()
+    finally:
+        bkv.bkv_set_debug_copies(prev)
+    obs_bits = v["obs"].view(torch.int16 if v["obs"].element_size() == 2 else torch.int32)
+    assert bool((obs_bits == 0x1357).all()), "obs written with debug copies off"
+    assert torch.equal(scores2[:, :, :L].view(torch.int32), ref_scores[:, :, :L].view(torch.int32))
+    for k in ("valid", "lse"):
+        assert torch.equal(v[k].view(torch.int32), ref[k].view(torch.int32)), k
