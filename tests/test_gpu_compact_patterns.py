@@ -178,14 +178,17 @@ def test_budgets_above_one_index_window(dtype, d, Lmax, lengths, B, W):
     assert length.cpu().tolist() == [min(L, B) for L in lengths]
 
 
-def test_rows_spanning_more_than_2gb_take_the_64bit_kernel():
-    """A binary32 d = 128 unit of 4,200,000 rows spans 2.15 GB, past the
-    32-bit offsets of the buffer instructions: the 256-thread kernel moves
-    it.  The 1,000 evicted rows lie near the end, so about 1,000 rows move;
-    every row is checked against the oracle's kept set on the device."""
-    dtype, d, L, W = torch.float32, 128, 4_200_000, 64
+@pytest.mark.parametrize("L", [4_194_303, 4_200_000])
+def test_units_at_and_past_the_buffer_offset_limit(L):
+    """Binary32 d = 128 units of 512-byte rows: 4,194,303 rows span just under
+    2^31 bytes, the largest the 1024-thread kernel's 32-bit buffer offsets
+    reach (its last row ends 512 bytes below 2^31); 4,200,000 rows span 2.15
+    GB and take the 256-thread kernel with 64-bit addresses.  The 1,000
+    evicted rows lie near the end, so about 1,000 rows move; every row is
+    checked against the oracle's kept set on the device."""
+    dtype, d, W = torch.float32, 128, 64
     B = L - 1000
-    print("case: 2 GB unit, L=%d B=%d" % (L, B), flush=True)
+    print("case: unit of %d rows (%d bytes), B=%d" % (L, L * 512, B), flush=True)
     shape = bkv.make_shape(1, 1, 1, d, L, dtype)
     gen = np.random.default_rng(11)
     s = (2.0 + gen.permutation(L).astype(np.float64) / L).astype(np.float32)   # distinct, in [2, 3)
